@@ -129,6 +129,8 @@ void orc_quantize_group(const float *x, int64_t n, int64_t stride, int bits,
         if (v < mn) mn = v;
         if (v > mx) mx = v;
     }
+    mn = mn + 0.0f; /* a zero extreme is taken as +0, whichever signed zero came first */
+    mx = mx + 0.0f;
     float range = mx - mn;
     float step32 = range / (float)L;
     uint16_t sh = orc_f32_to_f16(step32);
