@@ -1,0 +1,240 @@
+/*
+ * kvq.h -- C ABI of libkvq: low-bit KV-cache quantize-pack and fused attention over
+ * the packed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * The method comes from four web pages, cited by title and section:
+ *  [JB] "Quantized Keys Steal Attention: Bias Correction for KV-Cache Compression in
+ *       Video Diffusion", abstract -- chunk-wise autoregressive video diffusion keeps a
+ *       KV cache of earlier chunks; INT2 keys inflate their softmax weight (the
+ *       "Jensen bias") against the unquantized current chunk; a per-score correction
+ *       from the cached keys' step sizes and the query, second-order Taylor form, no
+ *       memory beyond the cache.
+ *  [SF] "KV Cache Quantization for Self-Forcing Video Generation: A 33-Method
+ *       Empirical Study", abstract -- INT4 caches; integrations that rebuild BF16
+ *       buffers during attention lose the memory they saved.
+ *  [WQ] WindowQuant notes (zenn.dev, "論文メモ：動画VLMのKV Cacheを軽量化するWindowQuant"),
+ *       sections "何が新しいのか", "技術的に面白い点", "実装者視点で気になった点" --
+ *       32-token windows scored by cosine similarity to the text query, FP16 / INT4 /
+ *       INT2 by relevance, window 0 always FP16, windows of one bit-width stored
+ *       together.
+ *  [QW] "QuantWM Preserves Attention in 2-Bit KV Cache Quantization for Video World
+ *       Models" -- 2-bit KV caches; keys act through the attention logits.
+ *
+ * Conventions for every call:
+ *  - Device pointers are plain HIP device addresses on the current device; host
+ *    pointers are marked "host". The caller owns every buffer. The library never
+ *    allocates, frees or synchronizes; each call only enqueues kernels on `stream`
+ *    (a hipStream_t; NULL = the null stream) and returns.
+ *  - Pointers must stay valid until the stream has run the work. Device buffers must
+ *    be 16-byte aligned.
+ *  - Every argument is checked on the host before anything is enqueued. On any error
+ *    nothing is enqueued and no output, buffer or descriptor is changed.
+ *    KVQ_ERR_HIP reports a launch failure (hipGetLastError after the launch); device
+ *    faults surface at the caller's next synchronization.
+ *  - No global mutable state: calls are reentrant and may run on several streams
+ *    at once if they touch disjoint buffers. No C++ exception crosses this ABI.
+ *  - Elements of fp16 / bf16 inputs must lie within fp16's finite range
+ *    (|x| <= 65504); step and zero are stored in fp16.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_ABI_VERSION 1
+#define KVQ_MAX_SEGMENTS 8
+
+typedef enum kvq_status {
+    KVQ_OK = 0,
+    KVQ_ERR_ARG = -1,          /* null pointer, bad size, inconsistent shapes */
+    KVQ_ERR_UNSUPPORTED = -2,  /* bits, head_dim, group size or dtype outside the table */
+    KVQ_ERR_CAPACITY = -3,     /* an append would overflow a segment */
+    KVQ_ERR_WORKSPACE = -4,    /* workspace null or smaller than kvq_attention_workspace_size */
+    KVQ_ERR_HIP = -5           /* a kernel launch failed */
+} kvq_status;
+
+typedef enum kvq_dtype { KVQ_F32 = 0, KVQ_F16 = 1, KVQ_BF16 = 2 } kvq_dtype;
+
+/* Jensen-bias correction applied to logits of quantized cached keys [JB]. */
+typedef enum kvq_jensen {
+    KVQ_JENSEN_OFF = 0,
+    /* beta(i, g) = tau^2 / 24 * sum_c q_ic^2 * step_gc^2, subtracted from every logit of a
+     * token of K-group g: half the variance of the logit noise tau * q . e when each key
+     * channel's rounding error e_c is uniform on [-step/2, step/2], i.e. the second-order
+     * term of log E[exp(tau q . e)]. step is the stored fp16 step; no extra memory. */
+    KVQ_JENSEN_TAYLOR2 = 1
+} kvq_jensen;
+
+/*
+ * One segment of the cache: every token in it has the same bit-width [WQ]. A plain
+ * chunk-wise cache is one packed segment [JB]; the WindowQuant layout is three (FP16,
+ * INT4, INT2), each holding its windows contiguously [WQ].
+ *
+ * Quantization (bits 2 or 4, L = 2^bits - 1), asymmetric min/max per group:
+ *   step = fp16(fl32(fl32(max - min) / L)), zero = fp16(min),
+ *   code = clamp(rint(fl32(fl32(x - zero) / step)), 0, L)   (0 when step == 0),
+ *   codes taken against the fp16-rounded step and zero, ties to even, IEEE fp32
+ *   division. K groups: one per (K-group of tokens, channel). V groups: one per (token,
+ *   run of v_group_channels channels).
+ * Dequantized element (what attention reads): E(fl32(code * step + zero)), E = rounding
+ *   to elem_dtype (bf16 or fp16), nearest-even.
+ *
+ * Layout per (batch b, KV head h), token-major, capacity slots each:
+ *   k, v     bits 2|4: uint32 [batch][n_kv_heads][capacity][head_dim*bits/32]; word w of a
+ *            token row holds channels [w*32/bits, (w+1)*32/bits), channel c at bit
+ *            bits*(c mod 32/bits), least significant first.
+ *            bits 16: elem_dtype [batch][n_kv_heads][capacity][head_dim], raw elements.
+ *   k_meta   bits 2|4: {fp16 step, fp16 zero} [batch][n_kv_heads][kgroup_capacity][head_dim]
+ *   v_meta   bits 2|4: {fp16 step, fp16 zero} [batch][n_kv_heads][capacity][head_dim/v_group_channels]
+ *   kgroup_start  bits 2|4: int32 [kgroup_capacity + 1]; K-group g holds tokens
+ *            [kgroup_start[g], kgroup_start[g+1]), the same for every (b, h).
+ *   For bits 16 k_meta, v_meta and kgroup_start are unused and may be NULL.
+ * The descriptor lives in host memory; n_tokens and n_kgroups mirror the device state
+ * and are advanced by kvq_quantize_append.
+ */
+typedef struct kvq_segment {
+    int32_t bits;              /* 2, 4 (packed codes) or 16 (raw elements) */
+    int32_t elem_dtype;        /* KVQ_BF16 or KVQ_F16: raw dtype / dequantization rounding */
+    int32_t batch, n_kv_heads, head_dim;   /* head_dim: 64 or 128 */
+    int32_t capacity;          /* token slots per (b, h) */
+    int32_t n_tokens;          /* valid tokens, [0, capacity] */
+    int32_t k_group_tokens;    /* K-group length of contiguous appends; max length of a gathered group; 1..1024 */
+    int32_t v_group_channels;  /* V-group width: 32 */
+    int32_t kgroup_capacity;   /* entries of k_meta per (b, h) */
+    int32_t n_kgroups;         /* valid K-groups */
+    void *k, *v;               /* device */
+    void *k_meta, *v_meta;     /* device */
+    int32_t *kgroup_start;     /* device */
+} kvq_segment;
+
+/*
+ * kvq_quantize_append -- quantize a finished chunk and append it to a segment [JB: the
+ * cache holds previously generated chunks; WQ: each window is stored at its bit-width].
+ *   dst         host descriptor; on KVQ_OK its n_tokens grows by n_new and n_kgroups by
+ *               the number of new K-groups.
+ *   k_src, v_src  device [batch][n_kv_heads][src_tokens][head_dim] of src_dtype (F32, F16
+ *               or BF16), the dst segment's batch / heads / head_dim.
+ *   src_tokens  token stride of the source per (b, h).
+ *   n_new       tokens to append. Contiguous mode (src_groups == NULL): source tokens
+ *               [0, n_new), cut into K-groups of k_group_tokens from the first appended
+ *               token, the last one possibly shorter. Gather mode: src_groups is a
+ *               DEVICE int32 array [n_src_groups][2] of {first source token, length};
+ *               each entry becomes one K-group, appended in list order. The caller
+ *               guarantees every entry lies in [0, src_tokens), lengths are in
+ *               [1, k_group_tokens] and sum to n_new; entries outside are clamped on the
+ *               device (no out-of-bounds access) and leave the segment's contents
+ *               unspecified.
+ *   Destination: tokens [n_tokens, n_tokens + n_new) of every (b, h).
+ *   bits 16 segments copy the tokens, rounding to elem_dtype (nearest-even).
+ * Errors: KVQ_ERR_ARG (null pointers, n_new < 0, shape mismatch), KVQ_ERR_UNSUPPORTED
+ * (bits, head_dim, group sizes, dtypes), KVQ_ERR_CAPACITY (n_tokens + n_new > capacity
+ * or the new K-groups exceed kgroup_capacity). n_new == 0 is a no-op returning KVQ_OK.
+ */
+typedef struct kvq_append_args {
+    kvq_segment *dst;          /* host */
+    const void *k_src, *v_src; /* device */
+    int32_t src_dtype;
+    int64_t src_tokens;
+    int32_t n_new;
+    const int32_t *src_groups; /* device, optional */
+    int32_t n_src_groups;
+} kvq_append_args;
+
+kvq_status kvq_quantize_append(const kvq_append_args *args, void *stream);
+
+/*
+ * kvq_assign_windows -- WindowQuant bit-widths for one sequence [WQ].
+ *   k            device [n_kv_heads][n_tokens][head_dim] of k_dtype (F16, BF16 or F32).
+ *   Windows are [window*w, min(window*w + window, n_tokens)), w < n_windows =
+ *   ceil(n_tokens / window).
+ *   Score: per KV head, the window's mean key (tokens summed in index order, in
+ *   double, divided by the token count); cosine with text_query (device, float32
+ *   [head_dim]) as dot / (sqrt(|mean|^2) * sqrt(|t|^2)), sums over channels in index
+ *   order, 0 if either norm is zero; score = mean over KV heads (summed in order).
+ *   Assignment: window 0 is FP16 whatever its score; windows 1.. are ranked by score,
+ *   highest first, ties to the lower index; the first n_fp16 - 1 get FP16, the next
+ *   n_int4 INT4, the rest INT2.
+ *   bits_out     device int8 [n_windows]: 16, 4 or 2.
+ *   order_out    device int32 [n_windows]: the FP16 windows ascending, then INT4
+ *                ascending, then INT2 ascending (the grouped storage order).
+ *   score_out    device double [n_windows] (required: also the scratch of the ranking).
+ * Errors: KVQ_ERR_ARG (nulls, n_tokens < 1, window < 1, n_fp16 < 1, n_int4 < 0,
+ * n_fp16 + n_int4 > n_windows), KVQ_ERR_UNSUPPORTED (head_dim not in {64, 128},
+ * n_windows > 65536).
+ */
+typedef struct kvq_window_args {
+    const void *k;
+    int32_t k_dtype;
+    int32_t n_kv_heads, head_dim, n_tokens, window;
+    const float *text_query;
+    int32_t n_fp16, n_int4;
+    int8_t *bits_out;
+    int32_t *order_out;
+    double *score_out;
+} kvq_window_args;
+
+kvq_status kvq_assign_windows(const kvq_window_args *args, void *stream);
+
+/*
+ * kvq_chunk_attention -- one chunk of queries over the quantized history plus the
+ * unquantized current chunk [JB], reading the packed cache directly (no dequantized
+ * copy of the cache is ever written to memory [SF]).
+ *   q        device [batch][n_q_heads][n_q][head_dim] of dtype (BF16 or F16).
+ *   segs     host array of n_segs (0..KVQ_MAX_SEGMENTS) segment descriptors: the
+ *            history, in any order (softmax does not depend on token order). All share
+ *            batch, n_kv_heads and head_dim with q, and elem_dtype == dtype.
+ *   k_cur, v_cur  device [batch][n_kv_heads][n_cur][head_dim] of dtype, may be NULL
+ *            when n_cur == 0.
+ *   Query head hq reads KV head hq * n_kv_heads / n_q_heads. No mask: every query sees
+ *   all history and the whole current chunk.
+ *   Logits: s = tau * q . k - beta, tau = softmax_scale (0 means 1/sqrt(head_dim));
+ *   beta as kvq_jensen for tokens of packed segments, 0 for bits-16 segments and for
+ *   the current chunk.
+ *   out      device [batch][n_q_heads][n_q][head_dim] of out_dtype (F32, F16 or BF16):
+ *            softmax(s) . V.
+ *   lse      device float32 [batch][n_q_heads][n_q], optional: log sum_j exp(s_j).
+ *   workspace  device scratch of at least kvq_attention_workspace_size bytes (may be
+ *            NULL when that size is 0). Contents on entry do not matter.
+ * Errors: KVQ_ERR_ARG (nulls, shape mismatch, no tokens at all, n_q_heads not a
+ * multiple of n_kv_heads), KVQ_ERR_UNSUPPORTED (dtypes, head_dim, bits, too many
+ * segments), KVQ_ERR_WORKSPACE.
+ */
+typedef struct kvq_attn_args {
+    const void *q;
+    int32_t dtype;
+    int32_t batch, n_q_heads, n_kv_heads, head_dim, n_q;
+    const kvq_segment *segs;   /* host */
+    int32_t n_segs;
+    const void *k_cur, *v_cur;
+    int32_t n_cur;
+    float softmax_scale;
+    int32_t jensen;
+    void *out;
+    int32_t out_dtype;
+    float *lse;
+    void *workspace;
+    size_t workspace_bytes;
+} kvq_attn_args;
+
+/* Bytes of workspace kvq_chunk_attention needs for these arguments (pointers are not
+ * read). Host only; returns KVQ_ERR_ARG / KVQ_ERR_UNSUPPORTED for arguments that
+ * kvq_chunk_attention would reject on shape grounds. */
+kvq_status kvq_attention_workspace_size(const kvq_attn_args *args, size_t *bytes);
+
+kvq_status kvq_chunk_attention(const kvq_attn_args *args, void *stream);
+
+/* Static, never-NULL description of a status code. */
+const char *kvq_status_string(kvq_status status);
+
+/* KVQ_ABI_VERSION of the loaded library. */
+int32_t kvq_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

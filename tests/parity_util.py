@@ -1,0 +1,93 @@
+"""Helpers of the GPU parity tests: build the same cache on both sides (HIP library via
+the binding, CPU oracle), copy device buffers back in the oracle's layout, compare."""
+import numpy as np
+import torch
+
+import bit_kv_cache_pack_amd as kvq
+import oracle
+
+TORCH_DT = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+def f32(t: torch.Tensor) -> np.ndarray:
+    """Exact float32 values of a CPU tensor of any float dtype."""
+    return t.float().numpy()
+
+
+def make_pair(bits, elem, B, H, d, capacity, Gk, kgroup_capacity):
+    g = kvq.Segment(bits, TORCH_DT[elem], B, H, d, capacity, k_group_tokens=Gk, kgroup_capacity=kgroup_capacity)
+    o = oracle.new_segment(bits, elem, B, H, d, capacity=capacity, k_group_tokens=Gk,
+                           kgroup_capacity=kgroup_capacity)
+    return g, o
+
+
+def append_both(gseg, oseg, k_src: torch.Tensor, v_src: torch.Tensor, groups=None):
+    """k_src/v_src CPU tensors [B][H][n][d]; groups: list of (start, len) or None."""
+    kd, vd = k_src.cuda(), v_src.cuda()
+    if groups is None:
+        kvq.quantize_append(gseg, kd, vd)
+        oracle.append(oseg, f32(k_src), f32(v_src))
+    else:
+        garr = np.asarray(groups, np.int32).reshape(-1, 2)
+        n_new = int(garr[:, 1].sum())
+        kvq.quantize_append(gseg, kd, vd, n_new=n_new, src_groups=torch.from_numpy(garr).cuda())
+        oracle.append(oseg, f32(k_src), f32(v_src), groups=garr)
+
+
+def host_view(gseg):
+    """The GPU segment's buffers as numpy arrays in the oracle's layout."""
+    out = dict(n_tokens=gseg.n_tokens, n_kgroups=gseg.n_kgroups)
+    if gseg.bits == 16:
+        out["k_raw"] = gseg.k.cpu().view(torch.int16).numpy().view(np.uint16)
+        out["v_raw"] = gseg.v.cpu().view(torch.int16).numpy().view(np.uint16)
+    else:
+        out["k_codes"] = gseg.k.cpu().numpy().view(np.uint32)
+        out["v_codes"] = gseg.v.cpu().numpy().view(np.uint32)
+        out["k_meta"] = gseg.k_meta.cpu().numpy().view(np.uint16)
+        out["v_meta"] = gseg.v_meta.cpu().numpy().view(np.uint16)
+        out["kgroup_start"] = gseg.kgroup_start.cpu().numpy()
+    return out
+
+
+def assert_segments_equal(gseg, oseg):
+    h = host_view(gseg)
+    assert h["n_tokens"] == oseg["n_tokens"]
+    n = oseg["n_tokens"]
+    if gseg.bits == 16:
+        assert np.array_equal(h["k_raw"][:, :, :n], oseg["k_raw"][:, :, :n])
+        assert np.array_equal(h["v_raw"][:, :, :n], oseg["v_raw"][:, :, :n])
+        return
+    G = oseg["n_kgroups"]
+    assert h["n_kgroups"] == G
+    assert np.array_equal(h["kgroup_start"][:G + 1], oseg["kgroup_start"][:G + 1])
+    for name, sl in (("k_codes", np.s_[:, :, :n]), ("v_codes", np.s_[:, :, :n]), ("k_meta", np.s_[:, :, :G]),
+                     ("v_meta", np.s_[:, :, :n])):
+        a, b = h[name][sl], oseg[name][sl]
+        bad = np.argwhere(a != b)
+        assert bad.size == 0, "%s differs at %d places, first %s: gpu %s oracle %s" % (
+            name, len(bad), bad[0].tolist(), a[tuple(bad[0])], b[tuple(bad[0])])
+
+
+def gpu_attention(q, gsegs, k_cur=None, v_cur=None, n_kv_heads=None, jensen=1, out_dtype=torch.float32,
+                  softmax_scale=0.0):
+    qd = q.cuda()
+    kc = None if k_cur is None else k_cur.cuda()
+    vc = None if v_cur is None else v_cur.cuda()
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    out = kvq.chunk_attention(qd, gsegs, kc, vc, n_kv_heads=n_kv_heads, jensen=jensen, out_dtype=out_dtype,
+                              lse=lse, softmax_scale=softmax_scale)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy(), lse.cpu().numpy()
+
+
+def oracle_attention(q, osegs, k_cur=None, v_cur=None, n_kv_heads=None, jensen=1, rows=None, scale=None):
+    kc = None if k_cur is None else f32(k_cur)
+    vc = None if v_cur is None else f32(v_cur)
+    return oracle.attention(f32(q), osegs, kc, vc, n_kv_heads=n_kv_heads, jensen=bool(jensen), rows=rows,
+                            scale=scale)
+
+
+def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
+    """Half a bf16 ulp at |x| (the rounding error of writing x as bf16)."""
+    ax = np.maximum(np.abs(x), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(ax)) - 8)

@@ -1,0 +1,185 @@
+"""C ABI checks that need no GPU: libkvq.so loads, exports every function include/kvq.h
+declares, and its host-side validation rejects bad arguments with the documented status
+codes before anything is enqueued (no HIP call is reached on these paths)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_kv_cache_pack_amd as kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:kvq_status|const char \*|int32_t)\s*(kvq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_declares_the_entry_points():
+    assert _declared() == sorted(["kvq_quantize_append", "kvq_assign_windows", "kvq_attention_workspace_size",
+                                  "kvq_chunk_attention", "kvq_status_string", "kvq_abi_version"])
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
+    exported = set(re.findall(r" T (kvq_\w+)", out))
+    assert set(_declared()) <= exported
+    assert L.kvq_abi_version() == 1
+
+
+def test_header_compiles_as_c():
+    src = '#include "kvq.h"\nint main(void){kvq_segment s; (void)s; return (int)sizeof(kvq_attn_args) > 0 ? 0 : 1;}\n'
+    r = subprocess.run(["gcc", "-std=c99", "-Wall", "-Werror", "-I", os.path.join(ROOT, "include"), "-x", "c",
+                        "-", "-o", "/dev/null"], input=src, capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_struct_layouts_match_binding():
+    """ctypes mirrors of the ABI structs have the C sizes (checked with the C compiler)."""
+    src = ('#include <stdio.h>\n#include "kvq.h"\nint main(void){printf("%zu %zu %zu %zu",'
+           'sizeof(kvq_segment),sizeof(kvq_append_args),sizeof(kvq_window_args),sizeof(kvq_attn_args));return 0;}\n')
+    exe = "/tmp/kvq_sizes_%d" % os.getpid()
+    r = subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), "-x", "c", "-", "-o", exe], input=src,
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    sizes = [int(x) for x in subprocess.run([exe], capture_output=True, text=True).stdout.split()]
+    os.unlink(exe)
+    assert sizes == [ctypes.sizeof(kvq.KvqSegment), ctypes.sizeof(kvq.KvqAppendArgs),
+                     ctypes.sizeof(kvq.KvqWindowArgs), ctypes.sizeof(kvq.KvqAttnArgs)]
+
+
+def test_status_strings():
+    for code in (kvq.OK, kvq.ERR_ARG, kvq.ERR_UNSUPPORTED, kvq.ERR_CAPACITY, kvq.ERR_WORKSPACE, kvq.ERR_HIP):
+        assert kvq.status_string(code)
+    assert kvq.status_string(-99) == "unknown status"
+
+
+FAKE = 0x100000  # a 16-byte aligned address that is never dereferenced on these paths
+
+
+def _seg(**kw):
+    d = dict(bits=2, elem_dtype=kvq.BF16, batch=1, n_kv_heads=2, head_dim=128, capacity=1000, n_tokens=0,
+             k_group_tokens=128, v_group_channels=32, kgroup_capacity=16, n_kgroups=0,
+             k=FAKE, v=FAKE, k_meta=FAKE, v_meta=FAKE, kgroup_start=FAKE)
+    d.update(kw)
+    return kvq.KvqSegment(**d)
+
+
+def _append(seg, **kw):
+    d = dict(dst=ctypes.pointer(seg), k_src=FAKE, v_src=FAKE, src_dtype=kvq.BF16, src_tokens=500, n_new=500,
+             src_groups=None, n_src_groups=0)
+    d.update(kw)
+    a = kvq.KvqAppendArgs(**d)
+    return kvq.lib().kvq_quantize_append(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(bits=3), kvq.ERR_UNSUPPORTED),
+    (dict(head_dim=96), kvq.ERR_UNSUPPORTED),
+    (dict(elem_dtype=kvq.F32), kvq.ERR_UNSUPPORTED),
+    (dict(v_group_channels=16), kvq.ERR_UNSUPPORTED),
+    (dict(k_group_tokens=0), kvq.ERR_UNSUPPORTED),
+    (dict(n_tokens=900), kvq.ERR_CAPACITY),          # 900 + 500 > 1000
+    (dict(n_kgroups=13), kvq.ERR_CAPACITY),          # 13 + 4 > 16
+    (dict(k=None), kvq.ERR_ARG),
+    (dict(k_meta=FAKE + 4), kvq.ERR_ARG),            # misaligned
+    (dict(n_tokens=-1), kvq.ERR_ARG),
+])
+def test_append_validation(kw, status):
+    seg = _seg(**kw)
+    before = (seg.n_tokens, seg.n_kgroups)
+    assert _append(seg) == status
+    assert (seg.n_tokens, seg.n_kgroups) == before
+
+
+def test_append_validation_args():
+    assert _append(_seg(), n_new=-1) == kvq.ERR_ARG
+    assert _append(_seg(), src_tokens=499) == kvq.ERR_ARG
+    assert _append(_seg(), src_dtype=7) == kvq.ERR_UNSUPPORTED
+    assert _append(_seg(), k_src=None) == kvq.ERR_ARG
+    assert _append(_seg(), src_groups=FAKE, n_src_groups=0) == kvq.ERR_ARG
+    assert _append(_seg(), src_groups=FAKE, n_src_groups=3) == kvq.ERR_ARG   # 3 x 128 < 500 tokens
+    seg = _seg()
+    assert _append(seg, n_new=0) == kvq.OK and seg.n_tokens == 0            # no-op, nothing launched
+    assert kvq.lib().kvq_quantize_append(None, None) == kvq.ERR_ARG
+
+
+def _attn(segs=None, **kw):
+    segs = [_seg(n_tokens=300, n_kgroups=3)] if segs is None else segs
+    arr = (kvq.KvqSegment * max(1, len(segs)))(*segs)
+    d = dict(q=FAKE, dtype=kvq.BF16, batch=1, n_q_heads=4, n_kv_heads=2, head_dim=128, n_q=10, segs=arr,
+             n_segs=len(segs), k_cur=FAKE, v_cur=FAKE, n_cur=10, softmax_scale=0.0, jensen=1, out=FAKE,
+             out_dtype=kvq.F32, lse=None, workspace=None, workspace_bytes=0)
+    d.update(kw)
+    return kvq.KvqAttnArgs(**d), arr
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(dtype=kvq.F32), kvq.ERR_UNSUPPORTED),
+    (dict(head_dim=256), kvq.ERR_UNSUPPORTED),
+    (dict(n_q_heads=3), kvq.ERR_ARG),
+    (dict(n_segs=9), kvq.ERR_UNSUPPORTED),
+    (dict(jensen=5), kvq.ERR_UNSUPPORTED),
+    (dict(out_dtype=9), kvq.ERR_UNSUPPORTED),
+    (dict(q=None), kvq.ERR_ARG),
+    (dict(out=None), kvq.ERR_ARG),
+    (dict(k_cur=None), kvq.ERR_ARG),
+    (dict(softmax_scale=-1.0), kvq.ERR_ARG),
+    (dict(n_q=0), kvq.ERR_ARG),
+])
+def test_attention_validation(kw, status):
+    a, arr = _attn(**kw)
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == status
+
+
+def test_attention_segment_checks():
+    a, arr = _attn(segs=[_seg(n_tokens=300, n_kgroups=3, elem_dtype=kvq.F16)])
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_UNSUPPORTED
+    a, arr = _attn(segs=[_seg(n_tokens=300, n_kgroups=3, n_kv_heads=4)])
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_ARG
+    a, arr = _attn(segs=[], n_cur=0)               # no tokens at all
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_ARG
+
+
+def test_workspace_size_and_check():
+    # decode shape: one query per head -> token splits -> a workspace is needed
+    a, arr = _attn(segs=[_seg(n_tokens=1000, n_kgroups=8)], n_q=1, n_cur=0, k_cur=None, v_cur=None)
+    n = ctypes.c_size_t()
+    assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK
+    assert n.value > 0 and n.value % (4 * 130) == 0
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_WORKSPACE
+    a.workspace, a.workspace_bytes = FAKE, n.value - 1
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_WORKSPACE
+    assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), None) == kvq.ERR_ARG
+    # a large chunk fills the GPU without splits: no workspace
+    a, arr = _attn(n_q=4680, n_q_heads=12, n_kv_heads=12, segs=[_seg(n_kv_heads=12, n_tokens=900, n_kgroups=8)])
+    assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK and n.value == 0
+
+
+def test_window_validation():
+    def call(**kw):
+        d = dict(k=FAKE, k_dtype=kvq.F16, n_kv_heads=2, head_dim=64, n_tokens=19600, window=32, text_query=FAKE,
+                 n_fp16=61, n_int4=184, bits_out=FAKE, order_out=FAKE, score_out=FAKE)
+        d.update(kw)
+        a = kvq.KvqWindowArgs(**d)
+        return kvq.lib().kvq_assign_windows(ctypes.byref(a), None)
+    assert call(n_fp16=0) == kvq.ERR_ARG
+    assert call(n_fp16=500, n_int4=200) == kvq.ERR_ARG
+    assert call(score_out=None) == kvq.ERR_ARG
+    assert call(k_dtype=9) == kvq.ERR_UNSUPPORTED
+    assert call(head_dim=512) == kvq.ERR_UNSUPPORTED
+    assert call(n_tokens=16384 * 32 + 1) == kvq.ERR_UNSUPPORTED
+    assert call(window=0) == kvq.ERR_ARG
+
+
+def test_binding_window_budget():
+    assert kvq.window_budget(613, 10, 30) == (61, 184)
+    g = kvq.window_groups([0, 2, 1, 3], [16, 4, 16, 2], n_tokens=100)
+    assert g[16] == ([(0, 32), (64, 32)], 64) and g[4] == ([(32, 32)], 32) and g[2] == ([(96, 4)], 4)
