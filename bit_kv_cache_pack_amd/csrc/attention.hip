@@ -14,17 +14,27 @@
 // WindowQuant notes ("技術的に面白い点"): windows of one bit-width are stored together;
 // each such segment is walked with its own bit-width.
 //
-// Workgroup: 4 waves, 128 query rows (32 per wave; rows of a KV head's query heads
-// are packed, so GQA decode fills the rows), one (batch, KV head), one token split.
-// Per 64-token tile (never straddling a K-group):
-//   1. all threads dequantize K into LDS as [token][channel] (element dtype) and V
-//      into LDS as [channel][token] in fp16, token order permuted inside each
-//      16-token block so a PV operand is one 16-byte read;
-//   2. each wave computes S^T = K Q^T (MFMA 32x32x16, lanes own queries), applies
-//      scale, Jensen term, ragged-tile mask and the online softmax (per-lane max/sum,
-//      one cross-lane exchange), and accumulates O^T += V^T P^T (MFMA 32x32x16 f16,
-//      P in fp16).
-// With several splits, unnormalized partials go to the workspace and a combine
+// Workgroup: 4 waves, 128 query rows (32 per wave; the rows of one KV head's query heads
+// are packed, so GQA decode fills rows), one (batch, KV head), one token split. Tokens
+// are walked in 64-token tiles that never straddle a K-group. Pipeline per tile, one
+// barrier per tile:
+//   - the packed codes / raw elements of tile i+1 are loaded into registers,
+//   - every wave computes tile i out of LDS buffer i%2: S^T = K Q^T with MFMA 32x32x16
+//     (lanes own queries, so softmax statistics and the Jensen term are per-lane
+//     scalars), online softmax in the log2 domain with rescaling only when a row
+//     maximum grows by more than 2^8, O^T += V^T P^T with P in fp16,
+//   - all threads dequantize tile i+1 into LDS buffer (i+1)%2.
+// LDS rows hold channels in a fixed order: inside each 16-channel block, position
+// 4j + k holds channel 4k + j (a 4x4 transpose). Q is loaded in that order, the output
+// is written back in channel order. Keys: [token][position] in the element dtype.
+// Values: [token][position] in fp16, read into the PV product with the LDS transpose
+// load. INT2 values are expanded through a 4-entry table per (token, V group) holding
+// the exact dequantized values, indexed with byte permutes; keys and INT4 values use the
+// fp16 step/zero directly in mixed-precision fused multiply-adds.
+// The Jensen terms of 32 consecutive K-groups are computed at once as a small matrix
+// product (step^2 x q^2, each split into bf16 high and low parts, three MFMAs per
+// k-step) and read back per group.
+// With several token splits, unnormalized partials go to the workspace and a combine
 // kernel merges them by log-sum-exp.
 #include "kvq_device.cuh"
 #include "kvq_internal.h"
@@ -35,32 +45,47 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int BM = 128;   // query rows per workgroup
 constexpr int TT = 64;    // tokens per tile
-constexpr int PAD = 8;    // LDS row padding, elements
 constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kRescale = 8.0f;  // log2 headroom before the running max is moved
+#ifndef KVQ_ATTN_BLOCKS_PER_CU
+#define KVQ_ATTN_BLOCKS_PER_CU 2  // workgroups per CU the register budget is sized for
+#endif
 
-template <int HD> struct alignas(16) Smem {
-    uint16_t k[TT][HD + PAD];      // dequantized keys, element dtype
-    uint16_t vt[HD][TT + PAD];     // dequantized values, fp16, transposed + permuted
-    float step[2][HD];             // K step of the current group (double-buffered)
-    float zero[2][HD];
+template <int HD> struct Geo {
+    static constexpr int KROW = HD + 8;    // halves per key row (16-byte padding)
+    static constexpr int VROW = HD + 16;   // halves per value row (32-byte padding)
+    static constexpr int KBUF = TT * KROW;
+    static constexpr int VBUF = TT * VROW;
+    static constexpr int BUF = KBUF + VBUF;   // halves per stage buffer
+    static constexpr int NBLK = HD / 16;      // 16-channel blocks per row
+    static constexpr int UNITS = TT * NBLK;   // (token, block) units per tile
+    static constexpr int UPT = UNITS / kThreads;
 };
 
-// Position of token t (0..63) inside a V^T row: bits 2 and 3 of t swapped.
-__device__ __forceinline__ int vpos(int t) {
-    return (t & ~12) | ((t & 4) << 1) | ((t & 8) >> 1);
+// position <-> channel inside a 16-channel block: p = 4j + k  <->  c = 4k + j (involution)
+__device__ __forceinline__ int swap_pos(int c) { return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
 }
+// a * (fp16 in the low half of m) + (fp16 in the high half of m), one rounding in fp32
+__device__ __forceinline__ float fma_mix(float a, uint32_t m) {
+    const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(m & 0xffffu));
+    const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
+    return __builtin_fmaf(a, (float)s, (float)z);
+}
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float other_half(float v) { return __shfl_xor(v, 32); }
 
 template <bool BF16> struct Elem;
 template <> struct Elem<true> {
     typedef bf16x8 vec;
     static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
-    // spec rounding of a value, returned as the fp16 pair used by the PV product
-    static __device__ __forceinline__ uint32_t pack_v(float a, float b) {
-        return bf16x2_to_f16x2(pack_bf16x2(a, b));
-    }
+    // element-dtype rounding of two values, returned as the fp16 pair the PV product uses
+    static __device__ __forceinline__ uint32_t pack_v(float a, float b) { return bf16x2_to_f16x2(pack_bf16x2(a, b)); }
     static __device__ __forceinline__ uint32_t raw_to_f16(uint32_t p) { return bf16x2_to_f16x2(p); }
     static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) { return mfma32_bf16(a, b, c); }
-    static __device__ __forceinline__ float to_f32(uint32_t bits) { return bf16_bits_to_f32(bits); }
+    static __device__ __forceinline__ float val(uint32_t bits16) { return bf16_bits_to_f32(bits16); }
 };
 template <> struct Elem<false> {
     typedef f16x8 vec;
@@ -68,194 +93,412 @@ template <> struct Elem<false> {
     static __device__ __forceinline__ uint32_t pack_v(float a, float b) { return pack_f16x2(a, b); }
     static __device__ __forceinline__ uint32_t raw_to_f16(uint32_t p) { return p; }
     static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) { return mfma32_f16(a, b, c); }
-    static __device__ __forceinline__ float to_f32(uint32_t bits) { return f16_bits_to_f32(bits); }
+    static __device__ __forceinline__ float val(uint32_t bits16) { return f16_bits_to_f32(bits16); }
 };
 
+// ---------------------------------------------------------------- tile walk
+enum : int { TILE_END = 0, TILE_PACKED = 1, TILE_RAW = 2, TILE_CUR = 3 };
+
+struct Tile {
+    int kind, seg, g, t, len;
+    int new_group;   // first tile of K-group g in this walk
+    int batch;       // a new block of 32 Jensen terms starts at group g
+};
+
+// Walks the segments, then the current chunk, over the token split [tb, te), in tiles
+// that never cross a K-group. Uniform across the workgroup.
+struct Walker {
+    int si, t, e, g, gfirst, last_g, inited;
+    __device__ __forceinline__ void init() { si = 0; inited = 0; last_g = -1; t = e = g = gfirst = 0; }
+    __device__ Tile next(const AttnParams &p, int tb, int te) {
+        while (true) {
+            if (si > p.n_segs) return Tile{TILE_END, 0, 0, 0, 0, 0, 0};
+            if (!inited) {
+                int a;
+                if (si == p.n_segs) {
+                    const int cb = p.n_total - p.n_cur;
+                    a = max(tb, cb) - cb;
+                    e = min(te, p.n_total) - cb;
+                } else {
+                    const SegmentView &sg = p.segs[si];
+                    a = max(tb, sg.token_begin) - sg.token_begin;
+                    e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
+                }
+                if (a >= e) { ++si; continue; }
+                t = a;
+                inited = 1;
+                if (si < p.n_segs && p.segs[si].bits != 16) {
+                    const SegmentView &sg = p.segs[si];
+                    int lo = 0, hi = sg.n_kgroups - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (sg.kgroup_start[mid + 1] <= a) lo = mid + 1; else hi = mid;
+                    }
+                    g = lo;
+                    gfirst = lo;
+                    last_g = -1;
+                }
+            }
+            if (t >= e) { ++si; inited = 0; continue; }
+            if (si == p.n_segs) {
+                const int len = min(TT, e - t);
+                Tile r{TILE_CUR, si, 0, t, len, 0, 0};
+                t += len;
+                return r;
+            }
+            const SegmentView &sg = p.segs[si];
+            if (sg.bits == 16) {
+                const int len = min(TT, e - t);
+                Tile r{TILE_RAW, si, 0, t, len, 0, 0};
+                t += len;
+                return r;
+            }
+            if (g >= sg.n_kgroups) { t = e; continue; }
+            // clamped: a corrupt table must not send reads outside the segment
+            const int ge = min(max(sg.kgroup_start[g + 1], 0), sg.n_tokens);
+            if (ge <= t) { ++g; continue; }
+            const int len = min(TT, min(ge, e) - t);
+            const int ng = g != last_g;
+            Tile r{TILE_PACKED, si, g, t, len, ng, ng && ((g - gfirst) % 32 == 0)};
+            last_g = g;
+            t += len;
+            if (t >= ge) ++g;
+            return r;
+        }
+    }
+};
+
+// ---------------------------------------------------------------- prefetch (global -> registers)
+// A thread owns UPT units (token r = u / NBLK, 16-channel block b = u % NBLK), u = tid + 256 i;
+// its block b is the same for all its units.
+// Raw tiles: w[4 i .. 4 i + 3] = K (2 x 16 B) and V (2 x 16 B) of unit i. Packed tiles:
+// w[0..3] = {step, zero} of the block's 16 key channels, w[4 + i] = codes of unit i
+// (x, z: key words; y, w: value words), w[6 + i].x = the unit's value {step, zero}.
+template <int HD> struct Prefetch {
+    u32x4 w[4 * Geo<HD>::UPT > 8 ? 4 * Geo<HD>::UPT : 8];
+};
+
+template <int HD>
+__device__ __forceinline__ void prefetch_tile(Prefetch<HD> &pf, const AttnParams &p, const Tile &tl, size_t bh) {
+    typedef Geo<HD> G;
+    const int tid = threadIdx.x;
+    if (tl.kind == TILE_PACKED) {
+        const SegmentView &sg = p.segs[tl.seg];
+        const int wpr = HD * sg.bits / 32;   // words per token row
+        const size_t row0 = bh * (size_t)sg.capacity + tl.t;
+        const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k) + row0 * wpr;
+        const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v) + row0 * wpr;
+        const uint32_t *vm = sg.v_meta + row0 * (HD / 32);
+#pragma unroll
+        for (int i = 0; i < G::UPT; ++i) {
+            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
+            u32x4 c = {0u, 0u, 0u, 0u};
+            uint32_t m = 0u;
+            if (r < tl.len) {
+                if (sg.bits == 2) {
+                    c.x = kc[(size_t)r * wpr + b];
+                    c.y = vc[(size_t)r * wpr + b];
+                } else {
+                    const u32x2 k2 = *reinterpret_cast<const u32x2 *>(kc + (size_t)r * wpr + 2 * b);
+                    const u32x2 v2 = *reinterpret_cast<const u32x2 *>(vc + (size_t)r * wpr + 2 * b);
+                    c.x = k2.x; c.z = k2.y;
+                    c.y = v2.x; c.w = v2.y;
+                }
+                m = vm[(size_t)r * (HD / 32) + b / 2];
+            }
+            pf.w[4 + i] = c;
+            pf.w[6 + i].x = m;
+        }
+        const int b = tid % G::NBLK;
+        const u32x4 *km = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD + 16 * b);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pf.w[i] = km[i];
+    } else if (tl.kind != TILE_END) {
+        const uint16_t *kb, *vb;
+        if (tl.kind == TILE_RAW) {
+            const SegmentView &sg = p.segs[tl.seg];
+            const size_t row0 = bh * (size_t)sg.capacity + tl.t;
+            kb = reinterpret_cast<const uint16_t *>(sg.k) + row0 * HD;
+            vb = reinterpret_cast<const uint16_t *>(sg.v) + row0 * HD;
+        } else {
+            const size_t row0 = bh * (size_t)p.n_cur + tl.t;
+            kb = reinterpret_cast<const uint16_t *>(p.k_cur) + row0 * HD;
+            vb = reinterpret_cast<const uint16_t *>(p.v_cur) + row0 * HD;
+        }
+#pragma unroll
+        for (int i = 0; i < G::UPT; ++i) {
+            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
+            const u32x4 z = {0u, 0u, 0u, 0u};
+            if (r < tl.len) {
+                const u32x4 *ks = reinterpret_cast<const u32x4 *>(kb + (size_t)r * HD + 16 * b);
+                const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb + (size_t)r * HD + 16 * b);
+                pf.w[4 * i] = ks[0]; pf.w[4 * i + 1] = ks[1];
+                pf.w[4 * i + 2] = vs[0]; pf.w[4 * i + 3] = vs[1];
+            } else {
+                pf.w[4 * i] = z; pf.w[4 * i + 1] = z; pf.w[4 * i + 2] = z; pf.w[4 * i + 3] = z;
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------- staging (registers -> LDS)
+// 16 values of one block in channel order (dword m = channels 2m, 2m+1) to position order.
+__device__ __forceinline__ void to_positions(const uint32_t (&d)[8], uint32_t (&o)[8]) {
+    // positions (4j, 4j+1) = channels (j, 4+j); (4j+2, 4j+3) = channels (8+j, 12+j)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        o[2 * j] = perm(d[2 + j / 2], d[j / 2], sel);
+        o[2 * j + 1] = perm(d[6 + j / 2], d[4 + j / 2], sel);
+    }
+}
+
+template <int HD, bool BF16>
+__device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch<HD> &pf, const Tile &tl, int bits) {
+    typedef Geo<HD> G;
+    typedef Elem<BF16> E;
+    uint16_t *kl = buf;
+    uint16_t *vl = buf + G::KBUF;
+    const int tid = threadIdx.x;
+    if (tl.kind == TILE_PACKED) {
+        uint32_t km[16];  // {step, zero} of the block's channels, channel order
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            km[4 * i] = pf.w[i].x; km[4 * i + 1] = pf.w[i].y; km[4 * i + 2] = pf.w[i].z; km[4 * i + 3] = pf.w[i].w;
+        }
+#pragma unroll
+        for (int i = 0; i < G::UPT; ++i) {
+            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
+            const u32x4 c = pf.w[4 + i];
+            const uint32_t vmeta = pf.w[6 + i].x;
+            uint32_t ko[8], vo[8];
+            if (bits == 2) {
+                // keys: byte k of x is the code of channel 4k + j
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t x = (c.x >> (2 * j)) & 0x03030303u;
+                    const float y0 = fma_mix((float)(x & 0xffu), km[j]);
+                    const float y1 = fma_mix((float)((x >> 8) & 0xffu), km[4 + j]);
+                    const float y2 = fma_mix((float)((x >> 16) & 0xffu), km[8 + j]);
+                    const float y3 = fma_mix((float)(x >> 24), km[12 + j]);
+                    ko[2 * j] = E::pack(y0, y1);
+                    ko[2 * j + 1] = E::pack(y2, y3);
+                }
+                // values: the 4 exact dequantized values of this (token, V group) as fp16,
+                // looked up with byte permutes (code c -> bytes 2c, 2c+1)
+                const uint32_t lut_lo = E::pack_v(fma_mix(0.0f, vmeta), fma_mix(1.0f, vmeta));
+                const uint32_t lut_hi = E::pack_v(fma_mix(2.0f, vmeta), fma_mix(3.0f, vmeta));
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t x = (c.y >> (2 * j)) & 0x03030303u;
+                    const uint32_t y = x << 1, yp = y | 0x01010101u;
+                    vo[2 * j] = perm(lut_hi, lut_lo, perm(yp, y, 0x05010400u));
+                    vo[2 * j + 1] = perm(lut_hi, lut_lo, perm(yp, y, 0x07030602u));
+                }
+            } else {
+                // INT4: two words per block; bytes of x = channels j, 8+j, 4+j, 12+j
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const uint32_t xk = ((c.x >> (4 * j)) & 0x000f000fu) | (((c.z >> (4 * j)) & 0x000f000fu) << 8);
+                    const float y0 = fma_mix((float)(xk & 0xffu), km[j]);
+                    const float y1 = fma_mix((float)((xk >> 16) & 0xffu), km[4 + j]);
+                    const float y2 = fma_mix((float)((xk >> 8) & 0xffu), km[8 + j]);
+                    const float y3 = fma_mix((float)(xk >> 24), km[12 + j]);
+                    ko[2 * j] = E::pack(y0, y1);
+                    ko[2 * j + 1] = E::pack(y2, y3);
+                    const uint32_t xv = ((c.y >> (4 * j)) & 0x000f000fu) | (((c.w >> (4 * j)) & 0x000f000fu) << 8);
+                    const float v0 = fma_mix((float)(xv & 0xffu), vmeta);
+                    const float v1 = fma_mix((float)((xv >> 16) & 0xffu), vmeta);
+                    const float v2 = fma_mix((float)((xv >> 8) & 0xffu), vmeta);
+                    const float v3 = fma_mix((float)(xv >> 24), vmeta);
+                    vo[2 * j] = E::pack_v(v0, v1);
+                    vo[2 * j + 1] = E::pack_v(v2, v3);
+                }
+            }
+            if (r >= tl.len) {
+#pragma unroll
+                for (int q = 0; q < 8; ++q) { ko[q] = 0u; vo[q] = 0u; }
+            }
+            u32x4 *kd = reinterpret_cast<u32x4 *>(kl + r * G::KROW + 16 * b);
+            u32x4 *vd = reinterpret_cast<u32x4 *>(vl + r * G::VROW + 16 * b);
+            kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
+            kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
+            vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
+            vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < G::UPT; ++i) {
+            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
+            const u32x4 k0 = pf.w[4 * i], k1 = pf.w[4 * i + 1], v0 = pf.w[4 * i + 2], v1 = pf.w[4 * i + 3];
+            const uint32_t kd8[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+            const uint32_t vd8[8] = {E::raw_to_f16(v0.x), E::raw_to_f16(v0.y), E::raw_to_f16(v0.z),
+                                     E::raw_to_f16(v0.w), E::raw_to_f16(v1.x), E::raw_to_f16(v1.y),
+                                     E::raw_to_f16(v1.z), E::raw_to_f16(v1.w)};
+            uint32_t ko[8], vo[8];
+            to_positions(kd8, ko);
+            to_positions(vd8, vo);
+            u32x4 *kd = reinterpret_cast<u32x4 *>(kl + r * G::KROW + 16 * b);
+            u32x4 *vd = reinterpret_cast<u32x4 *>(vl + r * G::VROW + 16 * b);
+            kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
+            kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
+            vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
+            vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
+        }
+    }
+}
+
+// ---------------------------------------------------------------- per-wave state and compute
 template <int HD, bool BF16> struct Ctx {
     typedef Elem<BF16> E;
     typedef typename E::vec vec;
     static constexpr int KS = HD / 16;   // k-steps of the QK product
-    static constexpr int DB = HD / 32;   // 32-channel blocks of the output
-
-    vec q[KS];          // this lane's query row, B-operand layout
-    f32x16 o[DB];       // O^T accumulators
-    float m, l;         // running max (log2 domain) and this lane's partial sum
-    float beta;         // Jensen term of the current group, log2 domain
+    static constexpr int DB = HD / 32;   // 32-position blocks of the output
+    vec q[KS];        // this lane's query at positions 16 ks + 8 hh + i
+    f32x16 o[DB];     // O^T accumulators, rows = positions
+    f32x16 bacc;      // Jensen sums of a block of 32 K-groups (rows) for this lane's query
+    float m, l;       // running max (log2 domain) and this lane's partial row sum
+    float beta;       // Jensen term of the current group, log2 domain
 };
 
-// ---------------------------------------------------------------- tile loaders
-template <int HD, bool BF16, int BITS>
-__device__ __forceinline__ void load_packed_tile(Smem<HD> &sm, int slot, const SegmentView &sg,
-                                                 size_t row0, int t0, int len) {
-    typedef Elem<BF16> E;
-    constexpr int CPW = 32 / BITS;           // channels per word
-    constexpr int WPR = HD * BITS / 32;      // words per token row
-    constexpr uint32_t LM = (1u << BITS) - 1u;
-    const int tid = threadIdx.x;
-    const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k) + (row0 + t0) * WPR;
-    const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v) + (row0 + t0) * WPR;
-
-    // K: one word (CPW channels of one token) per unit
-    for (int u = tid; u < TT * WPR; u += kThreads) {
-        const int r = u / WPR, wc = u % WPR;
-        uint32_t w = r < len ? kc[(size_t)r * WPR + wc] : 0u;
-        uint32_t out[CPW / 2];
+// Jensen sums of K-groups g0 .. g0+31 of a segment for the wave's 32 queries:
+// sum over positions of step^2 * q^2, as three bf16 MFMAs on high/low splits.
+template <int HD, bool BF16>
+__device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0) {
+    typedef Ctx<HD, BF16> C;
+    const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
+    const int g = g0 + r32;
+    const bool ok = g < sg.n_kgroups;
+    // this lane's channels in block ks: 4k + 2hh (elements i = k) and 4k + 2hh + 1 (i = 4 + k)
+    const uint32_t *km = sg.k_meta + (bh * sg.kgroup_capacity + (ok ? g : 0)) * HD + 2 * hh;
+    f32x16 acc = {};
 #pragma unroll
-        for (int i = 0; i < CPW; i += 2) {
-            const int c = wc * CPW + i;
-            float a = fmaf((float)((w >> (BITS * i)) & LM), sm.step[slot][c], sm.zero[slot][c]);
-            float b = fmaf((float)((w >> (BITS * (i + 1))) & LM), sm.step[slot][c + 1], sm.zero[slot][c + 1]);
-            out[i / 2] = r < len ? E::pack(a, b) : 0u;
-        }
-        uint32_t *dst = reinterpret_cast<uint32_t *>(&sm.k[r][wc * CPW]);
+    for (int ks = 0; ks < C::KS; ++ks) {
+        uint32_t m[8];
 #pragma unroll
-        for (int i = 0; i < CPW / 2; i += 4) {
-            u32x4 v4 = {out[i], out[i + 1], out[i + 2], out[i + 3]};
-            *reinterpret_cast<u32x4 *>(dst + i) = v4;
+        for (int k = 0; k < 4; ++k) {
+            const u32x2 v = ok ? *reinterpret_cast<const u32x2 *>(km + 16 * ks + 4 * k) : u32x2{0u, 0u};
+            m[k] = v.x;
+            m[4 + k] = v.y;
         }
+        const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+        bf16x8 ah, al, bh8, bl8;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            // position 16 ks + 8 hh + i holds channel 4 (i % 4) + 2 hh + i / 4 of the block
+            const float st = f16_bits_to_f32(m[i] & 0xffffu);
+            const float s2 = st * st;
+            const __bf16 s2h = (__bf16)s2;
+            ah[i] = s2h;
+            al[i] = (__bf16)(s2 - (float)s2h);
+            const uint32_t qb = (qw[i / 2] >> (16 * (i % 2))) & 0xffffu;
+            const float qv = C::E::val(qb);
+            const float q2 = qv * qv;
+            const __bf16 q2h = (__bf16)q2;
+            bh8[i] = q2h;
+            bl8[i] = (__bf16)(q2 - (float)q2h);
+        }
+        acc = mfma32_bf16(ah, bh8, acc);
+        acc = mfma32_bf16(ah, bl8, acc);
+        acc = mfma32_bf16(al, bh8, acc);
     }
-    // V: a pair of tokens x one word per unit; V groups are 32 channels per token
-    const uint32_t *vm = sg.v_meta + (row0 + t0) * (HD / 32);
-    for (int u = tid; u < (TT / 2) * WPR; u += kThreads) {
-        const int pr = u % (TT / 2), wc = u / (TT / 2);
-        const int r0 = 2 * pr, r1 = r0 + 1;
-        const int gv = (wc * CPW) / 32;
-        uint32_t w0 = r0 < len ? vc[(size_t)r0 * WPR + wc] : 0u;
-        uint32_t w1 = r1 < len ? vc[(size_t)r1 * WPR + wc] : 0u;
-        uint32_t m0 = r0 < len ? vm[(size_t)r0 * (HD / 32) + gv] : 0u;
-        uint32_t m1 = r1 < len ? vm[(size_t)r1 * (HD / 32) + gv] : 0u;
-        const float s0 = f16_bits_to_f32(m0 & 0xffffu), z0 = f16_bits_to_f32(m0 >> 16);
-        const float s1 = f16_bits_to_f32(m1 & 0xffffu), z1 = f16_bits_to_f32(m1 >> 16);
-        const int pos = vpos(r0);
-#pragma unroll
-        for (int i = 0; i < CPW; ++i) {
-            float a = fmaf((float)((w0 >> (BITS * i)) & LM), s0, z0);
-            float b = fmaf((float)((w1 >> (BITS * i)) & LM), s1, z1);
-            uint32_t pk = E::pack_v(a, b);
-            if (r0 >= len) pk = 0u;
-            else if (r1 >= len) pk &= 0xffffu;
-            *reinterpret_cast<uint32_t *>(&sm.vt[wc * CPW + i][pos]) = pk;
-        }
-    }
+    cx.bacc = acc;
 }
 
-// raw tokens (bits-16 segment or the current chunk): [token][channel] element dtype
+// The Jensen sum of group row rr (0..31) of the current block for this lane's query.
 template <int HD, bool BF16>
-__device__ __forceinline__ void load_raw_tile(Smem<HD> &sm, const uint16_t *kbase, const uint16_t *vbase,
-                                              int len) {
-    typedef Elem<BF16> E;
-    constexpr int CH = HD / 8;  // 16-byte chunks per row
-    const int tid = threadIdx.x;
-    for (int u = tid; u < TT * CH; u += kThreads) {
-        const int r = u / CH, c8 = u % CH;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (r < len) v = *reinterpret_cast<const u32x4 *>(kbase + (size_t)r * HD + c8 * 8);
-        *reinterpret_cast<u32x4 *>(&sm.k[r][c8 * 8]) = v;
-    }
-    for (int u = tid; u < (TT / 2) * CH; u += kThreads) {
-        const int pr = u % (TT / 2), c8 = u / (TT / 2);
-        const int r0 = 2 * pr, r1 = r0 + 1;
-        u32x4 a = {0u, 0u, 0u, 0u}, b = {0u, 0u, 0u, 0u};
-        if (r0 < len) a = *reinterpret_cast<const u32x4 *>(vbase + (size_t)r0 * HD + c8 * 8);
-        if (r1 < len) b = *reinterpret_cast<const u32x4 *>(vbase + (size_t)r1 * HD + c8 * 8);
-        uint32_t aw[4] = {E::raw_to_f16(a.x), E::raw_to_f16(a.y), E::raw_to_f16(a.z), E::raw_to_f16(a.w)};
-        uint32_t bw[4] = {E::raw_to_f16(b.x), E::raw_to_f16(b.y), E::raw_to_f16(b.z), E::raw_to_f16(b.w)};
-        const int pos = vpos(r0);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            // channel 2i: low halves of a and b; channel 2i+1: high halves
-            *reinterpret_cast<uint32_t *>(&sm.vt[c8 * 8 + 2 * i][pos]) = (aw[i] & 0xffffu) | (bw[i] << 16);
-            *reinterpret_cast<uint32_t *>(&sm.vt[c8 * 8 + 2 * i + 1][pos]) = (aw[i] >> 16) | (bw[i] & 0xffff0000u);
-        }
-    }
+__device__ __forceinline__ float beta_of(const Ctx<HD, BF16> &cx, int rr) {
+    const int hh = (threadIdx.x % kWave) / 32;
+    rr = __builtin_amdgcn_readfirstlane(rr);  // uniform: lets the table be indexed in registers
+    const int owner = (rr >> 2) & 1;
+    const int j = 4 * (rr >> 3) + (rr & 3);
+    const float v = cx.bacc[j];
+    const float other = other_half(v);
+    return hh == owner ? v : other;
 }
 
-// ---------------------------------------------------------------- per-wave compute
 template <int HD, bool BF16>
-__device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const Smem<HD> &sm, int len, float scale_log2,
-                                             float beta_log2) {
+__device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *buf, int len, float scale_log2) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
-    const int lane = threadIdx.x % kWave;
-    const int r32 = lane % 32, hh = lane / 32;
+    typedef Geo<HD> G;
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    const uint16_t *kl = buf;
+    const uint16_t *vl = buf + G::KBUF;
+    const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
 
-    // S^T (tokens x queries): two 32-token row blocks
-    f32x16 s[2];
+    const int grp = lane / 16, l16 = lane % 16;
+    const int pos_base = 16 * (grp & 1) + 4 * (l16 % 4);
+    // the tile in two 32-token halves: QK^T, softmax, PV per half (fewer live registers)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
-        s[rb] = f32x16{};
+        f32x16 s = {};
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            vec a = *reinterpret_cast<const vec *>(&sm.k[32 * rb + r32][16 * ks + 8 * hh]);
-            s[rb] = C::E::mma(a, cx.q[ks], s[rb]);
+            const vec a = *reinterpret_cast<const vec *>(kl + (32 * rb + r32) * G::KROW + 16 * ks + 8 * hh);
+            s = C::E::mma(a, cx.q[ks], s);
         }
-    }
-    // online softmax, log2 domain; token of s[rb][j] = 32 rb + 8 (j/4) + 4 hh + j%4
-    float mt = -__builtin_inff();
-#pragma unroll
-    for (int rb = 0; rb < 2; ++rb)
+        // logits in the log2 domain; token of s[j] = 32 rb + 8 (j / 4) + 4 hh + j % 4
+        float mt = -__builtin_inff();
 #pragma unroll
         for (int j = 0; j < 16; ++j) {
             const int tok = 32 * rb + 8 * (j / 4) + 4 * hh + (j % 4);
-            float x = fmaf(s[rb][j], scale_log2, -beta_log2);
-            x = tok < len ? x : -__builtin_inff();
-            s[rb][j] = x;
+            float x = __builtin_fmaf(s[j], scale_log2, -cx.beta);
+            if (len < TT) x = tok < len ? x : -__builtin_inff();
+            s[j] = x;
             mt = fmaxf(mt, x);
         }
-    mt = fmaxf(mt, __shfl_xor(mt, 32));
-    const float mnew = fmaxf(cx.m, mt);
-    const float alpha = exp2f(cx.m - mnew);
-    cx.m = mnew;
-    float ps = 0.f;
-    f16x8 pf[4];
+        mt = fmaxf(mt, other_half(mt));
+        if (__any(mt > cx.m + kRescale)) {
+            const float mnew = fmaxf(cx.m, mt);
+            const float alpha = exp2_fast(cx.m - mnew);
+            cx.m = mnew;
+            cx.l *= alpha;
 #pragma unroll
-    for (int st = 0; st < 4; ++st) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            float p = exp2f(s[st / 2][8 * (st % 2) + i] - mnew);
-            ps += p;
-            pf[st][i] = (_Float16)p;
+            for (int db = 0; db < C::DB; ++db) cx.o[db] *= alpha;
         }
-    }
-    cx.l = cx.l * alpha + ps;
+        float ps = 0.f;
+        f16x8 pf[2];
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) cx.o[db] *= alpha;
-    // O^T += V^T P^T
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            f16x8 a = *reinterpret_cast<const f16x8 *>(&sm.vt[32 * db + r32][16 * st + 8 * hh]);
-            cx.o[db] = mfma32_f16(a, pf[st], cx.o[db]);
-        }
-}
+            for (int i = 0; i < 8; ++i) {
+                const float pv = exp2_fast(s[8 * h2 + i] - cx.m);
+                ps += pv;
+                pf[h2][i] = (_Float16)pv;
+            }
+        cx.l += ps;
 
-// Jensen term of one K-group for this lane's query (log2 domain).
-template <int HD, bool BF16>
-__device__ __forceinline__ float group_beta(const Ctx<HD, BF16> &cx, const Smem<HD> &sm, int slot,
-                                            float beta_log2) {
-    const int hh = (threadIdx.x % kWave) / 32;
-    float acc = 0.f;
+        // O^T += V^T P^T. A operand: rows = positions 32 db + r32, k-slot i of half hh =
+        // token 16 st + 4 hh + (i % 4) + 8 (i / 4), matching P's layout. Two transposed
+        // 8-byte reads per operand: in each 16-lane group, source lane 4 jj + aa addresses
+        // token T + jj at positions base + 4 aa; lane l receives tokens T..T+3 at position
+        // base + l.
 #pragma unroll
-    for (int ks = 0; ks < Ctx<HD, BF16>::KS; ++ks) {
-        const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+        for (int h2 = 0; h2 < 2; ++h2) {
+            const int st = 2 * rb + h2;
+            const int tok0 = 16 * st + 4 * hh + l16 / 4;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const uint32_t bits = (qw[i / 2] >> (16 * (i % 2))) & 0xffffu;
-            const float qv = Elem<BF16>::to_f32(bits);
-            const float t = qv * sm.step[slot][16 * ks + 8 * hh + i];
-            acc = fmaf(t, t, acc);
+            for (int db = 0; db < C::DB; ++db) {
+                const uint16_t *p0 = vl + tok0 * G::VROW + 32 * db + pos_base;
+                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(p0));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(p0 + 8 * G::VROW));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+                const f16x8 a = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+                cx.o[db] = mfma32_f16(a, pf[h2], cx.o[db]);
+            }
         }
     }
-    acc += __shfl_xor(acc, 32);
-    return acc * beta_log2;
 }
 
 template <int HD, bool BF16>
-__global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, KVQ_ATTN_BLOCKS_PER_CU) void attention_kernel(AttnParams p) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
-    __shared__ Smem<HD> sm;
+    typedef Geo<HD> G;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G::BUF];
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int r32 = lane % 32, hh = lane / 32;
     const int b = blockIdx.y / p.n_kv_heads, h = blockIdx.y % p.n_kv_heads;
@@ -267,129 +510,89 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
     const int hq = h * gqa + (row_ok ? row / p.n_q : 0);
     const int qi = row_ok ? row % p.n_q : 0;
     const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
+    const size_t bh = (size_t)b * p.n_kv_heads + h;
 
     C cx;
     {
-        const uint16_t *qp = reinterpret_cast<const uint16_t *>(p.q) + qrow * HD + 8 * hh;
+        // positions 16 ks + 8 hh + i hold channels 16 ks + 4 (i % 4) + 2 hh + i / 4:
+        // element pairs (ch 2hh, 4+2hh), (8+2hh, 12+2hh), (2hh+1, 5+2hh), (9+2hh, 13+2hh)
+        // dword m of a block holds channels 2m, 2m+1: this lane uses dwords hh + 2k, k = 0..3
+        const uint32_t *qp = reinterpret_cast<const uint32_t *>(p.q) + qrow * (HD / 2) + hh;
 #pragma unroll
         for (int ks = 0; ks < C::KS; ++ks) {
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (row_ok) v = *reinterpret_cast<const u32x4 *>(qp + 16 * ks);
-            cx.q[ks] = __builtin_bit_cast(vec, v);
+            uint32_t d0 = 0u, d2 = 0u, d4 = 0u, d6 = 0u;
+            if (row_ok) {
+                d0 = qp[8 * ks];
+                d2 = qp[8 * ks + 2];
+                d4 = qp[8 * ks + 4];
+                d6 = qp[8 * ks + 6];
+            }
+            u32x4 o;
+            o.x = perm(d2, d0, 0x05040100u);
+            o.y = perm(d6, d4, 0x05040100u);
+            o.z = perm(d2, d0, 0x07060302u);
+            o.w = perm(d6, d4, 0x07060302u);
+            cx.q[ks] = __builtin_bit_cast(vec, o);
         }
     }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) cx.o[db] = f32x16{};
+    cx.bacc = f32x16{};
     cx.m = -__builtin_inff();
     cx.l = 0.f;
+    cx.beta = 0.f;
 
     const int tb = blockIdx.z * p.split_tokens;
     const int te = min(p.n_total, tb + p.split_tokens);
-    const size_t bh = (size_t)b * p.n_kv_heads + h;
-    int gcount = 0;  // groups visited, selects the meta slot
-
-    for (int si = 0; si < p.n_segs; ++si) {
-        const SegmentView &sg = p.segs[si];
-        const int a = max(tb, sg.token_begin) - sg.token_begin;
-        const int e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
-        if (a >= e) continue;
-        const size_t row0 = bh * (size_t)sg.capacity;
-        if (sg.bits == 16) {
-            for (int t = a; t < e; t += TT) {
-                const int len = min(TT, e - t);
-                __syncthreads();
-                load_raw_tile<HD, BF16>(sm, reinterpret_cast<const uint16_t *>(sg.k) + (row0 + t) * HD,
-                                        reinterpret_cast<const uint16_t *>(sg.v) + (row0 + t) * HD, len);
-                __syncthreads();
-                if (wave_ok) compute_tile<HD, BF16>(cx, sm, len, p.scale_log2, 0.f);
-            }
-            continue;
-        }
-        // first K-group ending after token a
-        int lo = 0, hi = sg.n_kgroups - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (sg.kgroup_start[mid + 1] <= a) lo = mid + 1; else hi = mid;
-        }
-        for (int g = lo; g < sg.n_kgroups; ++g) {
-            // clamped: a corrupt table must not send reads outside the segment
-            const int gs = min(max(sg.kgroup_start[g], 0), sg.n_tokens);
-            const int ge = min(max(sg.kgroup_start[g + 1], gs), sg.n_tokens);
-            if (gs >= e) break;
-            const int t0 = max(gs, a), t1 = min(ge, e);
-            if (t0 >= t1) continue;
-            const int slot = gcount & 1;
-            ++gcount;
-            const uint32_t *km = sg.k_meta + (bh * sg.kgroup_capacity + g) * HD;
-            for (int c = tid; c < HD; c += kThreads) {
-                const uint32_t mv = km[c];
-                sm.step[slot][c] = f16_bits_to_f32(mv & 0xffffu);
-                sm.zero[slot][c] = f16_bits_to_f32(mv >> 16);
-            }
-            bool first = true;
-            for (int t = t0; t < t1; t += TT) {
-                const int len = min(TT, t1 - t);
-                __syncthreads();
-                if (sg.bits == 2) load_packed_tile<HD, BF16, 2>(sm, slot, sg, row0, t, len);
-                else load_packed_tile<HD, BF16, 4>(sm, slot, sg, row0, t, len);
-                __syncthreads();
-                if (wave_ok) {
-                    if (first) cx.beta = group_beta<HD, BF16>(cx, sm, slot, p.beta_log2);
-                    compute_tile<HD, BF16>(cx, sm, len, p.scale_log2, cx.beta);
+    Walker wk;
+    wk.init();
+    Tile cur = wk.next(p, tb, te);
+    Prefetch<HD> pf;
+    int gbase = 0;  // first group of the current Jensen block
+    if (cur.kind != TILE_END) {
+        prefetch_tile<HD>(pf, p, cur, bh);
+        stage_tile<HD, BF16>(smem, pf, cur, cur.kind == TILE_PACKED ? p.segs[cur.seg].bits : 16);
+    }
+    __syncthreads();
+    int buf = 0;
+    while (cur.kind != TILE_END) {
+        const Tile nxt = wk.next(p, tb, te);
+        if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
+        if (wave_ok) {
+            if (cur.kind == TILE_PACKED) {
+                if (cur.batch) {
+                    gbase = cur.g;
+                    beta_block<HD, BF16>(cx, p.segs[cur.seg], bh, gbase);
                 }
-                first = false;
+                if (cur.new_group) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.g - gbase);
+            } else {
+                cx.beta = 0.f;
             }
+            compute_tile<HD, BF16>(cx, smem + buf * G::BUF, cur.len, p.scale_log2);
         }
-    }
-    // current chunk
-    {
-        const int cb = p.n_total - p.n_cur;
-        const int a = max(tb, cb) - cb, e = min(te, p.n_total) - cb;
-        const size_t row0 = bh * (size_t)p.n_cur;
-        for (int t = a; t < e; t += TT) {
-            const int len = min(TT, e - t);
-            __syncthreads();
-            load_raw_tile<HD, BF16>(sm, reinterpret_cast<const uint16_t *>(p.k_cur) + (row0 + t) * HD,
-                                    reinterpret_cast<const uint16_t *>(p.v_cur) + (row0 + t) * HD, len);
-            __syncthreads();
-            if (wave_ok) compute_tile<HD, BF16>(cx, sm, len, p.scale_log2, 0.f);
-        }
+        if (nxt.kind == TILE_END) break;
+        stage_tile<HD, BF16>(smem + (buf ^ 1) * G::BUF, pf, nxt,
+                             nxt.kind == TILE_PACKED ? p.segs[nxt.seg].bits : 16);
+        __syncthreads();
+        buf ^= 1;
+        cur = nxt;
     }
 
-    // epilogue: lane (query r32, half hh) holds O^T[32 db + 8 (j/4) + 4 hh + j%4][query]
-    const float lt = cx.l + __shfl_xor(cx.l, 32);
+    // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
+    const float lt = cx.l + other_half(cx.l);
     if (!row_ok) return;
     if (p.n_split == 1) {
         const float inv = 1.0f / lt;
-        if (p.out_dtype == DT_F32) {
-            float *op = reinterpret_cast<float *>(p.out) + qrow * HD;
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+        for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    f32x4 v = {cx.o[db][4 * jj] * inv, cx.o[db][4 * jj + 1] * inv, cx.o[db][4 * jj + 2] * inv,
-                               cx.o[db][4 * jj + 3] * inv};
-                    *reinterpret_cast<f32x4 *>(op + 32 * db + 8 * jj + 4 * hh) = v;
-                }
-        } else {
-            uint16_t *op = reinterpret_cast<uint16_t *>(p.out) + qrow * HD;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int jj = 0; jj < 4; ++jj) {
-                    const float v0 = cx.o[db][4 * jj] * inv, v1 = cx.o[db][4 * jj + 1] * inv;
-                    const float v2 = cx.o[db][4 * jj + 2] * inv, v3 = cx.o[db][4 * jj + 3] * inv;
-                    u32x2 w;
-                    if (p.out_dtype == DT_BF16) {
-                        w.x = pack_bf16x2(v0, v1);
-                        w.y = pack_bf16x2(v2, v3);
-                    } else {
-                        w.x = pack_f16x2(v0, v1);
-                        w.y = pack_f16x2(v2, v3);
-                    }
-                    *reinterpret_cast<u32x2 *>(op + 32 * db + 8 * jj + 4 * hh) = w;
-                }
-        }
+            for (int j = 0; j < 16; ++j) {
+                const int ch = swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4));
+                const float v = cx.o[db][j] * inv;
+                if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + ch] = v;
+                else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_bf16_bits(v);
+                else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_f16_bits(v);
+            }
         if (p.lse != nullptr && hh == 0) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
     } else {
         const size_t n_rows_total = (size_t)p.batch * p.n_q_heads * p.n_q;
@@ -397,11 +600,8 @@ __global__ __launch_bounds__(kThreads) void attention_kernel(AttnParams p) {
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                // partial rows are HD+2 floats: not 16-byte aligned in general
-#pragma unroll
-                for (int k = 0; k < 4; ++k) pp[32 * db + 8 * jj + 4 * hh + k] = cx.o[db][4 * jj + k];
-            }
+            for (int j = 0; j < 16; ++j)
+                pp[swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4))] = cx.o[db][j];
         if (hh == 0) {
             pp[HD] = cx.m;
             pp[HD + 1] = lt;
