@@ -42,24 +42,25 @@
 namespace kvq {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int BM = 128;   // query rows per workgroup
+constexpr int kWaves = 8;
+constexpr int kThreads = kWaves * kWave;
+constexpr int BM = 32 * kWaves;   // query rows per workgroup
 constexpr int TT = 64;    // tokens per tile
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;  // log2 headroom before the running max is moved
-#ifndef KVQ_ATTN_BLOCKS_PER_CU
-#define KVQ_ATTN_BLOCKS_PER_CU 2  // workgroups per CU the register budget is sized for
-#endif
 
+// Row strides (halves) chosen for the 64 LDS banks: key rows 68 dwords apart make the
+// 32 MFMA operand reads of a wave conflict-free; value rows 76 (HD 128) or 52 (HD 64)
+// dwords apart keep both the 16-byte stage writes and the 4-row transposed reads free of
+// conflicts.
 template <int HD> struct Geo {
-    static constexpr int KROW = HD + 8;    // halves per key row (16-byte padding)
-    static constexpr int VROW = HD + 16;   // halves per value row (32-byte padding)
+    static constexpr int KROW = HD + 8;
+    static constexpr int VROW = HD == 128 ? HD + 24 : HD + 40;
     static constexpr int KBUF = TT * KROW;
     static constexpr int VBUF = TT * VROW;
     static constexpr int BUF = KBUF + VBUF;   // halves per stage buffer
     static constexpr int NBLK = HD / 16;      // 16-channel blocks per row
-    static constexpr int UNITS = TT * NBLK;   // (token, block) units per tile
-    static constexpr int UPT = UNITS / kThreads;
+    static constexpr int UNITS = TT * NBLK;   // (token, block) units per tile, <= kThreads
 };
 
 // position <-> channel inside a 16-channel block: p = 4j + k  <->  c = 4k + j (involution)
@@ -75,7 +76,12 @@ __device__ __forceinline__ float fma_mix(float a, uint32_t m) {
     return __builtin_fmaf(a, (float)s, (float)z);
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-__device__ __forceinline__ float other_half(float v) { return __shfl_xor(v, 32); }
+// value of lane L ^ 32
+__device__ __forceinline__ float other_half(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
 
 template <bool BF16> struct Elem;
 template <> struct Elem<true> {
@@ -104,6 +110,17 @@ struct Tile {
     int new_group;   // first tile of K-group g in this walk
     int batch;       // a new block of 32 Jensen terms starts at group g
 };
+
+__device__ __forceinline__ Tile uniform(Tile t) {
+    t.kind = __builtin_amdgcn_readfirstlane(t.kind);
+    t.seg = __builtin_amdgcn_readfirstlane(t.seg);
+    t.g = __builtin_amdgcn_readfirstlane(t.g);
+    t.t = __builtin_amdgcn_readfirstlane(t.t);
+    t.len = __builtin_amdgcn_readfirstlane(t.len);
+    t.new_group = __builtin_amdgcn_readfirstlane(t.new_group);
+    t.batch = __builtin_amdgcn_readfirstlane(t.batch);
+    return t;
+}
 
 // Walks the segments, then the current chunk, over the token split [tb, te), in tiles
 // that never cross a K-group. Uniform across the workgroup.
@@ -169,50 +186,49 @@ struct Walker {
 };
 
 // ---------------------------------------------------------------- prefetch (global -> registers)
-// A thread owns UPT units (token r = u / NBLK, 16-channel block b = u % NBLK), u = tid + 256 i;
-// its block b is the same for all its units.
-// Raw tiles: w[4 i .. 4 i + 3] = K (2 x 16 B) and V (2 x 16 B) of unit i. Packed tiles:
-// w[0..3] = {step, zero} of the block's 16 key channels, w[4 + i] = codes of unit i
-// (x, z: key words; y, w: value words), w[6 + i].x = the unit's value {step, zero}.
-template <int HD> struct Prefetch {
-    u32x4 w[4 * Geo<HD>::UPT > 8 ? 4 * Geo<HD>::UPT : 8];
+// Thread tid owns the unit (token r = tid / NBLK, 16-channel block b = tid % NBLK).
+// Raw tiles: w[0..1] = 16 key elements, w[2..3] = 16 value elements. Packed tiles:
+// w[0..3] = {step, zero} of the block's 16 key channels, w[4] = codes (x, z: key words;
+// y, w: value words), w[5].x = the token's value {step, zero} for the block.
+struct Prefetch {
+    u32x4 w[6];
 };
 
 template <int HD>
-__device__ __forceinline__ void prefetch_tile(Prefetch<HD> &pf, const AttnParams &p, const Tile &tl, size_t bh) {
+__device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p, const Tile &tl, size_t bh) {
     typedef Geo<HD> G;
     const int tid = threadIdx.x;
+    const int r = tid / G::NBLK, b = tid % G::NBLK;
+    const bool mine = tid < G::UNITS && r < tl.len;
     if (tl.kind == TILE_PACKED) {
         const SegmentView &sg = p.segs[tl.seg];
-        const int wpr = HD * sg.bits / 32;   // words per token row
+        const int bits = sg.bits;
+        const int wpr = HD * bits / 32;   // words per token row
         const size_t row0 = bh * (size_t)sg.capacity + tl.t;
         const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k) + row0 * wpr;
         const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v) + row0 * wpr;
         const uint32_t *vm = sg.v_meta + row0 * (HD / 32);
-#pragma unroll
-        for (int i = 0; i < G::UPT; ++i) {
-            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
-            u32x4 c = {0u, 0u, 0u, 0u};
-            uint32_t m = 0u;
-            if (r < tl.len) {
-                if (sg.bits == 2) {
-                    c.x = kc[(size_t)r * wpr + b];
-                    c.y = vc[(size_t)r * wpr + b];
-                } else {
-                    const u32x2 k2 = *reinterpret_cast<const u32x2 *>(kc + (size_t)r * wpr + 2 * b);
-                    const u32x2 v2 = *reinterpret_cast<const u32x2 *>(vc + (size_t)r * wpr + 2 * b);
-                    c.x = k2.x; c.z = k2.y;
-                    c.y = v2.x; c.w = v2.y;
-                }
-                m = vm[(size_t)r * (HD / 32) + b / 2];
+        u32x4 c = {0u, 0u, 0u, 0u};
+        uint32_t m = 0u;
+        if (mine) {
+            if (bits == 2) {
+                c.x = kc[(uint32_t)(r * wpr + b)];
+                c.y = vc[(uint32_t)(r * wpr + b)];
+            } else {
+                const u32x2 k2 = *reinterpret_cast<const u32x2 *>(kc + (uint32_t)(r * wpr + 2 * b));
+                const u32x2 v2 = *reinterpret_cast<const u32x2 *>(vc + (uint32_t)(r * wpr + 2 * b));
+                c.x = k2.x; c.z = k2.y;
+                c.y = v2.x; c.w = v2.y;
             }
-            pf.w[4 + i] = c;
-            pf.w[6 + i].x = m;
+            m = vm[(uint32_t)(r * (HD / 32) + b / 2)];
         }
-        const int b = tid % G::NBLK;
-        const u32x4 *km = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD + 16 * b);
+        pf.w[4] = c;
+        pf.w[5].x = m;
+        if (tid < G::UNITS) {
+            const u32x4 *km = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pf.w[i] = km[i];
+            for (int i = 0; i < 4; ++i) pf.w[i] = km[i];
+        }
     } else if (tl.kind != TILE_END) {
         const uint16_t *kb, *vb;
         if (tl.kind == TILE_RAW) {
@@ -225,18 +241,14 @@ __device__ __forceinline__ void prefetch_tile(Prefetch<HD> &pf, const AttnParams
             kb = reinterpret_cast<const uint16_t *>(p.k_cur) + row0 * HD;
             vb = reinterpret_cast<const uint16_t *>(p.v_cur) + row0 * HD;
         }
-#pragma unroll
-        for (int i = 0; i < G::UPT; ++i) {
-            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
-            const u32x4 z = {0u, 0u, 0u, 0u};
-            if (r < tl.len) {
-                const u32x4 *ks = reinterpret_cast<const u32x4 *>(kb + (size_t)r * HD + 16 * b);
-                const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb + (size_t)r * HD + 16 * b);
-                pf.w[4 * i] = ks[0]; pf.w[4 * i + 1] = ks[1];
-                pf.w[4 * i + 2] = vs[0]; pf.w[4 * i + 3] = vs[1];
-            } else {
-                pf.w[4 * i] = z; pf.w[4 * i + 1] = z; pf.w[4 * i + 2] = z; pf.w[4 * i + 3] = z;
-            }
+        const u32x4 z = {0u, 0u, 0u, 0u};
+        if (mine) {
+            const u32x4 *ks = reinterpret_cast<const u32x4 *>(kb) + (uint32_t)(r * (HD / 8) + 2 * b);
+            const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb) + (uint32_t)(r * (HD / 8) + 2 * b);
+            pf.w[0] = ks[0]; pf.w[1] = ks[1];
+            pf.w[2] = vs[0]; pf.w[3] = vs[1];
+        } else {
+            pf.w[0] = z; pf.w[1] = z; pf.w[2] = z; pf.w[3] = z;
         }
     }
 }
@@ -254,98 +266,82 @@ __device__ __forceinline__ void to_positions(const uint32_t (&d)[8], uint32_t (&
 }
 
 template <int HD, bool BF16>
-__device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch<HD> &pf, const Tile &tl, int bits) {
+__device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, const Tile &tl, int bits) {
     typedef Geo<HD> G;
     typedef Elem<BF16> E;
-    uint16_t *kl = buf;
-    uint16_t *vl = buf + G::KBUF;
     const int tid = threadIdx.x;
+    if (tid >= G::UNITS) return;
+    const int r = tid / G::NBLK, b = tid % G::NBLK;
+    uint32_t ko[8], vo[8];
     if (tl.kind == TILE_PACKED) {
         uint32_t km[16];  // {step, zero} of the block's channels, channel order
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             km[4 * i] = pf.w[i].x; km[4 * i + 1] = pf.w[i].y; km[4 * i + 2] = pf.w[i].z; km[4 * i + 3] = pf.w[i].w;
         }
+        const u32x4 c = pf.w[4];
+        const uint32_t vmeta = pf.w[5].x;
+        if (bits == 2) {
+            // keys: byte k of x is the code of channel 4k + j
 #pragma unroll
-        for (int i = 0; i < G::UPT; ++i) {
-            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
-            const u32x4 c = pf.w[4 + i];
-            const uint32_t vmeta = pf.w[6 + i].x;
-            uint32_t ko[8], vo[8];
-            if (bits == 2) {
-                // keys: byte k of x is the code of channel 4k + j
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t x = (c.x >> (2 * j)) & 0x03030303u;
-                    const float y0 = fma_mix((float)(x & 0xffu), km[j]);
-                    const float y1 = fma_mix((float)((x >> 8) & 0xffu), km[4 + j]);
-                    const float y2 = fma_mix((float)((x >> 16) & 0xffu), km[8 + j]);
-                    const float y3 = fma_mix((float)(x >> 24), km[12 + j]);
-                    ko[2 * j] = E::pack(y0, y1);
-                    ko[2 * j + 1] = E::pack(y2, y3);
-                }
-                // values: the 4 exact dequantized values of this (token, V group) as fp16,
-                // looked up with byte permutes (code c -> bytes 2c, 2c+1)
-                const uint32_t lut_lo = E::pack_v(fma_mix(0.0f, vmeta), fma_mix(1.0f, vmeta));
-                const uint32_t lut_hi = E::pack_v(fma_mix(2.0f, vmeta), fma_mix(3.0f, vmeta));
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t x = (c.y >> (2 * j)) & 0x03030303u;
-                    const uint32_t y = x << 1, yp = y | 0x01010101u;
-                    vo[2 * j] = perm(lut_hi, lut_lo, perm(yp, y, 0x05010400u));
-                    vo[2 * j + 1] = perm(lut_hi, lut_lo, perm(yp, y, 0x07030602u));
-                }
-            } else {
-                // INT4: two words per block; bytes of x = channels j, 8+j, 4+j, 12+j
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const uint32_t xk = ((c.x >> (4 * j)) & 0x000f000fu) | (((c.z >> (4 * j)) & 0x000f000fu) << 8);
-                    const float y0 = fma_mix((float)(xk & 0xffu), km[j]);
-                    const float y1 = fma_mix((float)((xk >> 16) & 0xffu), km[4 + j]);
-                    const float y2 = fma_mix((float)((xk >> 8) & 0xffu), km[8 + j]);
-                    const float y3 = fma_mix((float)(xk >> 24), km[12 + j]);
-                    ko[2 * j] = E::pack(y0, y1);
-                    ko[2 * j + 1] = E::pack(y2, y3);
-                    const uint32_t xv = ((c.y >> (4 * j)) & 0x000f000fu) | (((c.w >> (4 * j)) & 0x000f000fu) << 8);
-                    const float v0 = fma_mix((float)(xv & 0xffu), vmeta);
-                    const float v1 = fma_mix((float)((xv >> 16) & 0xffu), vmeta);
-                    const float v2 = fma_mix((float)((xv >> 8) & 0xffu), vmeta);
-                    const float v3 = fma_mix((float)(xv >> 24), vmeta);
-                    vo[2 * j] = E::pack_v(v0, v1);
-                    vo[2 * j + 1] = E::pack_v(v2, v3);
-                }
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t x = (c.x >> (2 * j)) & 0x03030303u;
+                const float y0 = fma_mix((float)(x & 0xffu), km[j]);
+                const float y1 = fma_mix((float)((x >> 8) & 0xffu), km[4 + j]);
+                const float y2 = fma_mix((float)((x >> 16) & 0xffu), km[8 + j]);
+                const float y3 = fma_mix((float)(x >> 24), km[12 + j]);
+                ko[2 * j] = E::pack(y0, y1);
+                ko[2 * j + 1] = E::pack(y2, y3);
             }
-            if (r >= tl.len) {
+            // values: the 4 exact dequantized values of this (token, V group) as fp16,
+            // looked up with byte permutes (code c -> bytes 2c, 2c+1)
+            const uint32_t lut_lo = E::pack_v(fma_mix(0.0f, vmeta), fma_mix(1.0f, vmeta));
+            const uint32_t lut_hi = E::pack_v(fma_mix(2.0f, vmeta), fma_mix(3.0f, vmeta));
 #pragma unroll
-                for (int q = 0; q < 8; ++q) { ko[q] = 0u; vo[q] = 0u; }
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t x = (c.y >> (2 * j)) & 0x03030303u;
+                const uint32_t y = x << 1, yp = y | 0x01010101u;
+                vo[2 * j] = perm(lut_hi, lut_lo, perm(yp, y, 0x05010400u));
+                vo[2 * j + 1] = perm(lut_hi, lut_lo, perm(yp, y, 0x07030602u));
             }
-            u32x4 *kd = reinterpret_cast<u32x4 *>(kl + r * G::KROW + 16 * b);
-            u32x4 *vd = reinterpret_cast<u32x4 *>(vl + r * G::VROW + 16 * b);
-            kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
-            kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
-            vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
-            vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
+        } else {
+            // INT4: two words per block; bytes of x = channels j, 8+j, 4+j, 12+j
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const uint32_t xk = ((c.x >> (4 * j)) & 0x000f000fu) | (((c.z >> (4 * j)) & 0x000f000fu) << 8);
+                const float y0 = fma_mix((float)(xk & 0xffu), km[j]);
+                const float y1 = fma_mix((float)((xk >> 16) & 0xffu), km[4 + j]);
+                const float y2 = fma_mix((float)((xk >> 8) & 0xffu), km[8 + j]);
+                const float y3 = fma_mix((float)(xk >> 24), km[12 + j]);
+                ko[2 * j] = E::pack(y0, y1);
+                ko[2 * j + 1] = E::pack(y2, y3);
+                const uint32_t xv = ((c.y >> (4 * j)) & 0x000f000fu) | (((c.w >> (4 * j)) & 0x000f000fu) << 8);
+                const float v0 = fma_mix((float)(xv & 0xffu), vmeta);
+                const float v1 = fma_mix((float)((xv >> 16) & 0xffu), vmeta);
+                const float v2 = fma_mix((float)((xv >> 8) & 0xffu), vmeta);
+                const float v3 = fma_mix((float)(xv >> 24), vmeta);
+                vo[2 * j] = E::pack_v(v0, v1);
+                vo[2 * j + 1] = E::pack_v(v2, v3);
+            }
+        }
+        if (r >= tl.len) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) { ko[q] = 0u; vo[q] = 0u; }
         }
     } else {
-#pragma unroll
-        for (int i = 0; i < G::UPT; ++i) {
-            const int u = tid + kThreads * i, r = u / G::NBLK, b = u % G::NBLK;
-            const u32x4 k0 = pf.w[4 * i], k1 = pf.w[4 * i + 1], v0 = pf.w[4 * i + 2], v1 = pf.w[4 * i + 3];
-            const uint32_t kd8[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-            const uint32_t vd8[8] = {E::raw_to_f16(v0.x), E::raw_to_f16(v0.y), E::raw_to_f16(v0.z),
-                                     E::raw_to_f16(v0.w), E::raw_to_f16(v1.x), E::raw_to_f16(v1.y),
-                                     E::raw_to_f16(v1.z), E::raw_to_f16(v1.w)};
-            uint32_t ko[8], vo[8];
-            to_positions(kd8, ko);
-            to_positions(vd8, vo);
-            u32x4 *kd = reinterpret_cast<u32x4 *>(kl + r * G::KROW + 16 * b);
-            u32x4 *vd = reinterpret_cast<u32x4 *>(vl + r * G::VROW + 16 * b);
-            kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
-            kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
-            vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
-            vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
-        }
+        const uint32_t kd8[8] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w, pf.w[1].x, pf.w[1].y, pf.w[1].z, pf.w[1].w};
+        const uint32_t vd8[8] = {E::raw_to_f16(pf.w[2].x), E::raw_to_f16(pf.w[2].y), E::raw_to_f16(pf.w[2].z),
+                                 E::raw_to_f16(pf.w[2].w), E::raw_to_f16(pf.w[3].x), E::raw_to_f16(pf.w[3].y),
+                                 E::raw_to_f16(pf.w[3].z), E::raw_to_f16(pf.w[3].w)};
+        to_positions(kd8, ko);
+        to_positions(vd8, vo);
     }
+    u32x4 *kd = reinterpret_cast<u32x4 *>(buf + r * G::KROW + 16 * b);
+    u32x4 *vd = reinterpret_cast<u32x4 *>(buf + G::KBUF + r * G::VROW + 16 * b);
+    kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
+    kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
+    vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
+    vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
 }
 
 // ---------------------------------------------------------------- per-wave state and compute
@@ -438,16 +434,20 @@ __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *
             const vec a = *reinterpret_cast<const vec *>(kl + (32 * rb + r32) * G::KROW + 16 * ks + 8 * hh);
             s = C::E::mma(a, cx.q[ks], s);
         }
-        // logits in the log2 domain; token of s[j] = 32 rb + 8 (j / 4) + 4 hh + j % 4
-        float mt = -__builtin_inff();
+        // token of s[j] = 32 rb + 8 (j / 4) + 4 hh + j % 4; tokens past len do not exist
+        if (len < TT) {
 #pragma unroll
-        for (int j = 0; j < 16; ++j) {
-            const int tok = 32 * rb + 8 * (j / 4) + 4 * hh + (j % 4);
-            float x = __builtin_fmaf(s[j], scale_log2, -cx.beta);
-            if (len < TT) x = tok < len ? x : -__builtin_inff();
-            s[j] = x;
-            mt = fmaxf(mt, x);
+            for (int j = 0; j < 16; ++j) {
+                const int tok = 32 * rb + 8 * (j / 4) + 4 * hh + (j % 4);
+                s[j] = tok < len ? s[j] : -__builtin_inff();
+            }
         }
+        float sm = max3(s[0], s[1], s[2]);
+#pragma unroll
+        for (int j = 3; j < 15; j += 2) sm = max3(sm, s[j], s[j + 1]);
+        sm = fmaxf(sm, s[15]);
+        // the tile's row maximum of the corrected logits, log2 domain (scale > 0)
+        float mt = __builtin_fmaf(sm, scale_log2, -cx.beta);
         mt = fmaxf(mt, other_half(mt));
         if (__any(mt > cx.m + kRescale)) {
             const float mnew = fmaxf(cx.m, mt);
@@ -457,15 +457,21 @@ __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) cx.o[db] *= alpha;
         }
-        float ps = 0.f;
+        // p = 2^(scale s - beta - m) <= 2^8, rounded to fp16; the row sum adds the same
+        // rounded values the PV product uses
+        const float off = -(cx.beta + cx.m);
         f16x8 pf[2];
+        float ps = 0.f;
 #pragma unroll
         for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const float pv = exp2_fast(s[8 * h2 + i] - cx.m);
-                ps += pv;
-                pf[h2][i] = (_Float16)pv;
+            for (int i = 0; i < 8; i += 2) {
+                f16x2 pr;
+                pr.x = (_Float16)exp2_fast(__builtin_fmaf(s[8 * h2 + i], scale_log2, off));
+                pr.y = (_Float16)exp2_fast(__builtin_fmaf(s[8 * h2 + i + 1], scale_log2, off));
+                pf[h2][i] = pr.x;
+                pf[h2][i + 1] = pr.y;
+                ps = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
             }
         cx.l += ps;
 
@@ -494,7 +500,7 @@ __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *
 }
 
 template <int HD, bool BF16>
-__global__ __launch_bounds__(kThreads, KVQ_ATTN_BLOCKS_PER_CU) void attention_kernel(AttnParams p) {
+__global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
     typedef Geo<HD> G;
@@ -546,8 +552,8 @@ __global__ __launch_bounds__(kThreads, KVQ_ATTN_BLOCKS_PER_CU) void attention_ke
     const int te = min(p.n_total, tb + p.split_tokens);
     Walker wk;
     wk.init();
-    Tile cur = wk.next(p, tb, te);
-    Prefetch<HD> pf;
+    Tile cur = uniform(wk.next(p, tb, te));
+    Prefetch pf;
     int gbase = 0;  // first group of the current Jensen block
     if (cur.kind != TILE_END) {
         prefetch_tile<HD>(pf, p, cur, bh);
@@ -556,7 +562,7 @@ __global__ __launch_bounds__(kThreads, KVQ_ATTN_BLOCKS_PER_CU) void attention_ke
     __syncthreads();
     int buf = 0;
     while (cur.kind != TILE_END) {
-        const Tile nxt = wk.next(p, tb, te);
+        const Tile nxt = uniform(wk.next(p, tb, te));
         if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
         if (wave_ok) {
             if (cur.kind == TILE_PACKED) {

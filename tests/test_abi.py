@@ -159,7 +159,7 @@ def test_workspace_size_and_check():
     assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_WORKSPACE
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), None) == kvq.ERR_ARG
     # a large chunk fills the GPU without splits: no workspace
-    a, arr = _attn(n_q=4680, n_q_heads=12, n_kv_heads=12, segs=[_seg(n_kv_heads=12, n_tokens=900, n_kgroups=8)])
+    a, arr = _attn(n_q=8192, n_q_heads=12, n_kv_heads=12, segs=[_seg(n_kv_heads=12, n_tokens=900, n_kgroups=8)])
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK and n.value == 0
 
 
