@@ -14,7 +14,7 @@
 // WindowQuant notes ("技術的に面白い点"): windows of one bit-width are stored together;
 // each such segment is walked with its own bit-width.
 //
-// Workgroup: 4 waves, 128 query rows (32 per wave; the rows of one KV head's query heads
+// Workgroup: 8 waves, 256 query rows (32 per wave; the rows of one KV head's query heads
 // are packed, so GQA decode fills rows), one (batch, KV head), one token split. Tokens
 // are walked in 64-token tiles that never straddle a K-group. Pipeline per tile, one
 // barrier per tile:
