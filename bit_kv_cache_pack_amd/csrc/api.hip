@@ -65,6 +65,15 @@ kvq_status check_attention_shape(const kvq_attn_args *a, long long *n_total) {
     return KVQ_OK;
 }
 
+// Which attention kernel a call runs (the workspace size depends on it).
+bool use_decode(const kvq_attn_args *a) {
+    int bits[KVQ_MAX_SEGMENTS];
+    int n = 0;
+    for (int i = 0; i < a->n_segs; ++i)
+        if (a->segs[i].n_tokens > 0) bits[n++] = a->segs[i].bits;
+    return kvq::decode_eligible(a->dtype, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, bits, n);
+}
+
 }  // namespace
 
 extern "C" {
@@ -164,8 +173,8 @@ kvq_status kvq_attention_workspace_size(const kvq_attn_args *a, size_t *bytes) {
     kvq_status st = check_attention_shape(a, &n_total);
     if (st != KVQ_OK) return st;
     int ns, stoks;
-    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, &ns, &stoks,
-                        bytes);
+    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, use_decode(a), &ns,
+                        &stoks, bytes);
     return KVQ_OK;
 }
 
@@ -180,8 +189,9 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
         if (a->segs[i].n_tokens > 0 && (st = check_segment_ptrs(a->segs[i])) != KVQ_OK) return st;
     int ns = 1, stoks = 0;
     size_t need = 0;
-    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, &ns, &stoks,
-                        &need);
+    const bool decode = use_decode(a);
+    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, decode, &ns,
+                        &stoks, &need);
     if (need > 0 && (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace)))
         return KVQ_ERR_WORKSPACE;
 
@@ -229,6 +239,7 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
     p.n_split = ns;
     p.split_tokens = stoks;
     p.partial = reinterpret_cast<float *>(a->workspace);
+    p.decode = decode ? 1 : 0;
     return kvq::launch_attention(p, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 

@@ -36,8 +36,8 @@
 // k-step) and read back per group.
 // With several token splits, unnormalized partials go to the workspace and a combine
 // kernel merges them by log-sum-exp.
-#include "kvq_device.cuh"
 #include "kvq_internal.h"
+#include "kvq_tile.cuh"
 
 namespace kvq {
 namespace {
@@ -61,45 +61,6 @@ template <int HD> struct Geo {
     static constexpr int BUF = KBUF + VBUF;   // halves per stage buffer
     static constexpr int NBLK = HD / 16;      // 16-channel blocks per row
     static constexpr int UNITS = TT * NBLK;   // (token, block) units per tile, <= kThreads
-};
-
-// position <-> channel inside a 16-channel block: p = 4j + k  <->  c = 4k + j (involution)
-__device__ __forceinline__ int swap_pos(int c) { return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3); }
-
-__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
-    return __builtin_amdgcn_perm(hi, lo, sel);
-}
-// a * (fp16 in the low half of m) + (fp16 in the high half of m), one rounding in fp32
-__device__ __forceinline__ float fma_mix(float a, uint32_t m) {
-    const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(m & 0xffffu));
-    const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
-    return __builtin_fmaf(a, (float)s, (float)z);
-}
-__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
-// value of lane L ^ 32
-__device__ __forceinline__ float other_half(float v) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-}
-__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
-
-template <bool BF16> struct Elem;
-template <> struct Elem<true> {
-    typedef bf16x8 vec;
-    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
-    // element-dtype rounding of two values, returned as the fp16 pair the PV product uses
-    static __device__ __forceinline__ uint32_t pack_v(float a, float b) { return bf16x2_to_f16x2(pack_bf16x2(a, b)); }
-    static __device__ __forceinline__ uint32_t raw_to_f16(uint32_t p) { return bf16x2_to_f16x2(p); }
-    static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) { return mfma32_bf16(a, b, c); }
-    static __device__ __forceinline__ float val(uint32_t bits16) { return bf16_bits_to_f32(bits16); }
-};
-template <> struct Elem<false> {
-    typedef f16x8 vec;
-    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
-    static __device__ __forceinline__ uint32_t pack_v(float a, float b) { return pack_f16x2(a, b); }
-    static __device__ __forceinline__ uint32_t raw_to_f16(uint32_t p) { return p; }
-    static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) { return mfma32_f16(a, b, c); }
-    static __device__ __forceinline__ float val(uint32_t bits16) { return f16_bits_to_f32(bits16); }
 };
 
 // ---------------------------------------------------------------- tile walk
@@ -254,17 +215,6 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
 }
 
 // ---------------------------------------------------------------- staging (registers -> LDS)
-// 16 values of one block in channel order (dword m = channels 2m, 2m+1) to position order.
-__device__ __forceinline__ void to_positions(const uint32_t (&d)[8], uint32_t (&o)[8]) {
-    // positions (4j, 4j+1) = channels (j, 4+j); (4j+2, 4j+3) = channels (8+j, 12+j)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
-        o[2 * j] = perm(d[2 + j / 2], d[j / 2], sel);
-        o[2 * j + 1] = perm(d[6 + j / 2], d[4 + j / 2], sel);
-    }
-}
-
 template <int HD, bool BF16>
 __device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, const Tile &tl, int bits) {
     typedef Geo<HD> G;
@@ -644,15 +594,28 @@ hipError_t launch_t(const AttnParams &p, hipStream_t s) {
     hipLaunchKernelGGL((attention_kernel<HD, BF16>), grid, dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
-    const unsigned n_rows_total = (unsigned)p.batch * p.n_q_heads * p.n_q;
-    hipLaunchKernelGGL((combine_kernel<HD>), dim3(n_rows_total), dim3(HD), 0, s, p);
-    return hipGetLastError();
+    return launch_combine(p, s);
 }
 
 }  // namespace
 
-void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total,
+hipError_t launch_combine(const AttnParams &p, hipStream_t s) {
+    const unsigned n_rows_total = (unsigned)p.batch * p.n_q_heads * p.n_q;
+    if (p.head_dim == 64) hipLaunchKernelGGL((combine_kernel<64>), dim3(n_rows_total), dim3(64), 0, s, p);
+    else hipLaunchKernelGGL((combine_kernel<128>), dim3(n_rows_total), dim3(128), 0, s, p);
+    return hipGetLastError();
+}
+
+void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total, bool decode,
                     int *n_split, int *split_tokens, size_t *workspace_bytes) {
+    if (decode) {
+        int nw, wt;
+        decode_plan(batch, n_kv_heads, n_total, &nw, &wt);
+        *n_split = nw;
+        *split_tokens = wt;
+        *workspace_bytes = nw > 1 ? (size_t)nw * batch * n_q_heads * n_q * (head_dim + 2) * sizeof(float) : 0;
+        return;
+    }
     const long rows = (long)(n_q_heads / n_kv_heads) * n_q;
     const long base = (rows + BM - 1) / BM * (long)batch * n_kv_heads;
     long ns = 1;
@@ -673,6 +636,7 @@ void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int 
 }
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
+    if (p.decode) return launch_decode(p, s);
     const bool bf = p.dtype == DT_BF16;
     if (p.head_dim == 64) return bf ? launch_t<64, true>(p, s) : launch_t<64, false>(p, s);
     return bf ? launch_t<128, true>(p, s) : launch_t<128, false>(p, s);

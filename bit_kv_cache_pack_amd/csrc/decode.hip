@@ -1,0 +1,725 @@
+// Decode-shaped attention over a packed low-bit KV cache: at most 16 query rows per
+// (batch, KV head) -- in GQA decode, one token of each query head that shares the KV
+// head -- against a long quantized history (plus, optionally, raw segments and an
+// unquantized current chunk).
+//
+// Method: as the chunk kernel ("Quantized Keys Steal Attention: Bias Correction for
+// KV-Cache Compression in Video Diffusion", abstract): logits over packed tokens are
+// corrected by beta = tau^2/24 * sum_c q_c^2 step_c^2 of their K-group; no mask; the
+// dequantized keys and values exist only in registers and LDS ("KV Cache Quantization
+// for Self-Forcing Video Generation", abstract). The WindowQuant segments ("技術的に面白い
+// 点") are walked one after another.
+//
+// With so few rows the work is streaming the packed cache and expanding it, so the
+// layout is built for memory-level parallelism and for few vector instructions per
+// code rather than for MFMA reuse:
+//   - every wave walks its own contiguous token range (no barriers until the end) in
+//     steps of 64 INT2 / 32 INT4 tokens (16 for raw tokens); the codes of the next step
+//     are loaded into one 20-register set as soon as this step's copy has been expanded
+//     (keys after the QK product, values after their LDS write), so each load has about
+//     a whole step to land;
+//   - keys are dequantized straight into 16x16x32 MFMA operands in registers: lane
+//     (token t = L % 16, quarter j = L / 16) expands the codes of its token's quarter
+//     row, S^T (tokens x rows) = K^ Q^T; codes become floats two at a time through the
+//     fp8 conversion (bytes 0..15 read as OCP e4m3 are c * 2^-9, scaled back by 2^9);
+//     the lane keeps the {step, zero} of its quarter's channels for the current K-group;
+//   - values are expanded into a wave-private LDS tile (INT2 through a 4-entry table per
+//     (token, V group)) and read back transposed into the A operand of
+//     O^T += V^T P^T (P in fp16);
+//   - online softmax in the log2 domain with a lazily moved running maximum;
+//   - the four waves of a workgroup merge their (m, l, O) in LDS at the end; with more
+//     than one workgroup per (batch, KV head), the merged partials go to the workspace
+//     and the split-combine kernel finishes them.
+// Channel order inside 16-channel blocks is the position order of kvq_tile.cuh for K
+// operands, Q and V rows; O is written back in channel order.
+#include "kvq_internal.h"
+#include "kvq_tile.cuh"
+
+namespace kvq {
+namespace {
+
+constexpr int kDWaves = 4;
+constexpr int kDThreads = kDWaves * kWave;
+constexpr int TP = 64;   // tokens per step of an INT2 segment (32 for INT4)
+constexpr int TR = 16;   // tokens per step of a raw segment or of the current chunk
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr float kDRescale = 8.0f;  // log2 headroom before the running max is moved
+
+template <int HD> struct DGeo {
+    static constexpr int NBL = HD / 64;   // 16-channel blocks per quarter row
+    static constexpr int KS = HD / 32;    // k-steps of the QK product
+    static constexpr int DB = HD / 16;    // 16-position blocks of O^T
+    static constexpr int QV = HD / 32;    // 16-byte vectors per quarter row of 16-bit elements
+    // Value row stride (halves): 8 (HD 128) or 40 (HD 64) dwords mod 64 banks, so the
+    // eight 8-byte rows that half a wave reads per transposed load hit distinct banks.
+    static constexpr int VROW = HD + 16;
+    static constexpr int VTILE = TP * VROW;  // halves per wave
+    static constexpr int OROW = HD + 4;      // epilogue scratch row (floats)
+};
+
+enum : int { ST_END = 0, ST_PACKED = 1, ST_RAW = 2, ST_CUR = 3 };
+
+struct Step {
+    int kind, seg, g, t, len;
+    int new_group;  // first step of K-group g in this walk
+};
+
+__device__ __forceinline__ Step uniform(Step s) {
+    s.kind = __builtin_amdgcn_readfirstlane(s.kind);
+    s.seg = __builtin_amdgcn_readfirstlane(s.seg);
+    s.g = __builtin_amdgcn_readfirstlane(s.g);
+    s.t = __builtin_amdgcn_readfirstlane(s.t);
+    s.len = __builtin_amdgcn_readfirstlane(s.len);
+    s.new_group = __builtin_amdgcn_readfirstlane(s.new_group);
+    return s;
+}
+
+// Walks the segments, then the current chunk, over the token range [tb, te), in steps
+// that never cross a K-group. Uniform across the wave.
+struct Walker {
+    int si, t, e, g, last_g, inited;
+    __device__ __forceinline__ void init() { si = 0; inited = 0; last_g = -1; t = e = g = 0; }
+    __device__ Step next(const AttnParams &p, int tb, int te) {
+        while (true) {
+            if (si > p.n_segs) return Step{ST_END, 0, 0, 0, 0, 0};
+            if (!inited) {
+                int a;
+                if (si == p.n_segs) {
+                    const int cb = p.n_total - p.n_cur;
+                    a = max(tb, cb) - cb;
+                    e = min(te, p.n_total) - cb;
+                } else {
+                    const SegmentView &sg = p.segs[si];
+                    a = max(tb, sg.token_begin) - sg.token_begin;
+                    e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
+                }
+                if (a >= e) { ++si; continue; }
+                t = a;
+                inited = 1;
+                if (si < p.n_segs && p.segs[si].bits != 16) {
+                    const SegmentView &sg = p.segs[si];
+                    int lo = 0, hi = sg.n_kgroups - 1;
+                    while (lo < hi) {
+                        const int mid = (lo + hi) >> 1;
+                        if (sg.kgroup_start[mid + 1] <= a) lo = mid + 1; else hi = mid;
+                    }
+                    g = lo;
+                    last_g = -1;
+                }
+            }
+            if (t >= e) { ++si; inited = 0; continue; }
+            if (si == p.n_segs) {
+                const int len = min(TR, e - t);
+                Step r{ST_CUR, si, 0, t, len, 0};
+                t += len;
+                return r;
+            }
+            const SegmentView &sg = p.segs[si];
+            if (sg.bits == 16) {
+                const int len = min(TR, e - t);
+                Step r{ST_RAW, si, 0, t, len, 0};
+                t += len;
+                return r;
+            }
+            if (g >= sg.n_kgroups) { t = e; continue; }
+            // clamped: a corrupt table must not send reads outside the segment
+            const int ge = min(max(sg.kgroup_start[g + 1], 0), sg.n_tokens);
+            if (ge <= t) { ++g; continue; }
+            const int len = min(sg.bits == 4 ? TP / 2 : TP, min(ge, e) - t);
+            Step r{ST_PACKED, si, g, t, len, g != last_g};
+            last_g = g;
+            t += len;
+            if (t >= ge) ++g;
+            return r;
+        }
+    }
+};
+
+// Registers of one packed step, loaded a step ahead (8 + 8 + 4 words per lane):
+//   INT2: k words 2 b .. (b = 0..3) = token 16 b + L%16, quarter L/16 (HD/64 words each);
+//         v = the whole code row of token L; vm = its V {step, zero}s.
+//   INT4: k words 4 b .. (b = 0..1) = token 16 b + L%16, quarter L/16 (HD/32 words each);
+//         v = half L%2 of the code row of token L/2; vm = the {step, zero}s of that half.
+struct DSet {
+    u32x4 k[2];
+    u32x4 v[2];
+    u32x4 vm;
+};
+
+template <int N>
+__device__ __forceinline__ uint32_t word_of(const u32x4 (&a)[N], int w) {
+    const u32x4 x = a[w >> 2];
+    return (w & 3) == 0 ? x.x : (w & 3) == 1 ? x.y : (w & 3) == 2 ? x.z : x.w;
+}
+template <int N>
+__device__ __forceinline__ void set_word(u32x4 (&a)[N], int w, uint32_t v) {
+    if ((w & 3) == 0) a[w >> 2].x = v;
+    else if ((w & 3) == 1) a[w >> 2].y = v;
+    else if ((w & 3) == 2) a[w >> 2].z = v;
+    else a[w >> 2].w = v;
+}
+
+template <int HD>
+__device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step &st, size_t bh) {
+    const int r16 = threadIdx.x % 16, j = (threadIdx.x % kWave) / 16;
+    const SegmentView &sg = p.segs[st.seg];
+    const size_t row0 = bh * (size_t)sg.capacity + st.t;
+    const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k);
+    if (sg.bits == 2) {
+        constexpr int WPR = HD / 16, WL = WPR / 4;   // words per row, per quarter
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (16 * b + r16 < st.len) {
+                const uint32_t *src = kc + (row0 + 16 * b + r16) * WPR + j * WL;
+                if (WL == 2) {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
+                    set_word(d.k, 2 * b, w.x);
+                    set_word(d.k, 2 * b + 1, w.y);
+                } else {
+                    set_word(d.k, b, *src);
+                }
+            }
+        }
+    } else {
+        constexpr int WPR = HD / 8, WL = WPR / 4;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (16 * b + r16 < st.len) {
+                const uint32_t *src = kc + (row0 + 16 * b + r16) * WPR + j * WL;
+                if (WL == 4) {
+                    d.k[b] = *reinterpret_cast<const u32x4 *>(src);
+                } else {
+                    const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
+                    set_word(d.k, 2 * b, w.x);
+                    set_word(d.k, 2 * b + 1, w.y);
+                }
+            }
+        }
+    }
+}
+
+template <int HD>
+__device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step &st, size_t bh) {
+    const int lane = threadIdx.x % kWave;
+    const SegmentView &sg = p.segs[st.seg];
+    const size_t row0 = bh * (size_t)sg.capacity + st.t;
+    const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
+    if (sg.bits == 2) {
+        constexpr int WPR = HD / 16;
+        if (lane < st.len) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + lane) * WPR);
+#pragma unroll
+            for (int i = 0; i < WPR / 4; ++i) d.v[i] = src[i];
+            const uint32_t *vm = sg.v_meta + (row0 + lane) * (HD / 32);
+            if (HD == 128) {
+                d.vm = *reinterpret_cast<const u32x4 *>(vm);
+            } else {
+                const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
+                d.vm.x = m.x;
+                d.vm.y = m.y;
+            }
+        }
+    } else {
+        constexpr int WPR = HD / 8, HW = WPR / 2;  // words per row, per half row
+        const int tok = lane / 2, half = lane % 2;
+        if (tok < st.len) {
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR + half * HW);
+#pragma unroll
+            for (int i = 0; i < HW / 4; ++i) d.v[i] = src[i];
+            const uint32_t *vm = sg.v_meta + (row0 + tok) * (HD / 32) + half * (HD / 64);
+            if (HD == 128) {
+                const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
+                d.vm.x = m.x;
+                d.vm.y = m.y;
+            } else {
+                d.vm.x = *vm;
+            }
+        }
+    }
+}
+
+// Two codes (bytes 0,1 or, with HI, 2,3 of x, each 0..15) as exact floats.
+template <bool HI>
+__device__ __forceinline__ float2 codes2(uint32_t x) {
+    const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 512.0f, HI);
+    return float2{r[0], r[1]};
+}
+
+// Keys, INT2, one 16-channel block from its word, through the fp8 conversion.
+template <bool BF16>
+__device__ __forceinline__ void k2_block(uint32_t w, const uint32_t *km, uint32_t (&ko)[8]) {
+    typedef Elem<BF16> E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t x = (w >> (2 * j)) & 0x03030303u;   // bytes: channels j, 4+j, 8+j, 12+j
+        const float2 a = codes2<false>(x), b = codes2<true>(x);
+        ko[2 * j] = E::pack(fma_mix(a.x, km[j]), fma_mix(a.y, km[4 + j]));
+        ko[2 * j + 1] = E::pack(fma_mix(b.x, km[8 + j]), fma_mix(b.y, km[12 + j]));
+    }
+}
+// Keys, INT4: w0 = channels 0..7, w1 = channels 8..15 of the block.
+template <bool BF16>
+__device__ __forceinline__ void k4_block(uint32_t w0, uint32_t w1, const uint32_t *km, uint32_t (&ko)[8]) {
+    typedef Elem<BF16> E;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        // bytes of x0: channels jj, 2+jj, 4+jj, 6+jj; of x1: the same plus 8
+        const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
+        const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
+        const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
+        ko[2 * jj] = E::pack(fma_mix(a0.x, km[jj]), fma_mix(b0.x, km[4 + jj]));
+        ko[2 * jj + 1] = E::pack(fma_mix(a1.x, km[8 + jj]), fma_mix(b1.x, km[12 + jj]));
+        ko[2 * jj + 4] = E::pack(fma_mix(a0.y, km[2 + jj]), fma_mix(b0.y, km[6 + jj]));
+        ko[2 * jj + 5] = E::pack(fma_mix(a1.y, km[10 + jj]), fma_mix(b1.y, km[14 + jj]));
+    }
+}
+// Values, INT4, one block with one {step, zero}: fp16 pairs in position order.
+template <bool BF16>
+__device__ __forceinline__ void v4_block(uint32_t w0, uint32_t w1, uint32_t vm, uint32_t (&vo)[8]) {
+    typedef Elem<BF16> E;
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
+        const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
+        const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
+        vo[2 * jj] = E::pack_v(fma_mix(a0.x, vm), fma_mix(b0.x, vm));
+        vo[2 * jj + 1] = E::pack_v(fma_mix(a1.x, vm), fma_mix(b1.x, vm));
+        vo[2 * jj + 4] = E::pack_v(fma_mix(a0.y, vm), fma_mix(b0.y, vm));
+        vo[2 * jj + 5] = E::pack_v(fma_mix(a1.y, vm), fma_mix(b1.y, vm));
+    }
+}
+
+template <int HD, bool BF16> struct DCtx {
+    typedef typename Elem<BF16>::vec vec;
+    vec qb[DGeo<HD>::KS];              // B operand: Q^T, quarter L/16 of row L%16, position order
+    f32x4 o[DGeo<HD>::DB];             // O^T: positions 16 db + 4 (L/16) + i, row L%16
+    uint32_t km[16 * DGeo<HD>::NBL];   // {step, zero} of the quarter's channels, channel order
+    float m, l, beta;
+};
+
+template <int HD>
+__device__ __forceinline__ void load_kmeta(uint32_t (&km)[16 * DGeo<HD>::NBL], const AttnParams &p, const Step &st,
+                                           size_t bh) {
+    const int j = (threadIdx.x % kWave) / 16;
+    const SegmentView &sg = p.segs[st.seg];
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + st.g) * HD +
+                                                       j * (HD / 4));
+#pragma unroll
+    for (int i = 0; i < 4 * DGeo<HD>::NBL; ++i) {
+        const u32x4 w = src[i];
+        km[4 * i] = w.x;
+        km[4 * i + 1] = w.y;
+        km[4 * i + 2] = w.z;
+        km[4 * i + 3] = w.w;
+    }
+}
+
+// sum over the row's channels of (q_c step_c)^2, for the lane's row
+template <int HD, bool BF16>
+__device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx) {
+    typedef DGeo<HD> G;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, cx.qb[ks]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int pos = 8 * (ks & 1) + i;                // position inside block ks / 2
+            const int ch = 16 * (ks >> 1) + swap_pos(pos);   // channel inside the quarter
+            const uint32_t qbits = (qw[i / 2] >> (16 * (i % 2))) & 0xffffu;
+            const float t = mul_step(Elem<BF16>::val(qbits), cx.km[ch]);
+            acc = __builtin_fmaf(t, t, acc);
+        }
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += other_half(acc);
+    return acc;
+}
+
+template <int HD, bool BF16>
+__device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const Step &st, const Step &nx,
+                                             uint16_t *vt, const AttnParams &p, size_t bh) {
+    typedef DGeo<HD> G;
+    typedef Elem<BF16> E;
+    typedef typename DCtx<HD, BF16>::vec vec;
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    const int lane = threadIdx.x % kWave, r16 = lane % 16, j = lane / 16;
+    const bool packed = st.kind == ST_PACKED;
+    const int bits = packed ? p.segs[st.seg].bits : 16;
+    const bool nx_packed = nx.kind == ST_PACKED;
+
+    if (packed && st.new_group) cx.beta = p.jensen ? p.beta_log2 * jensen_sum<HD, BF16>(cx) : 0.f;
+    if (!packed) cx.beta = 0.f;
+
+    // ---- S^T = K^ Q^T: s[b][i] = logit of token 16 b + 4 j + i for row r16
+    f32x4 s[4];
+    const int nblk = (st.len + 15) / 16;
+#pragma unroll
+    for (int b = 0; b < 4; ++b) s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (bits == 2) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (b < nblk) {
+#pragma unroll
+                for (int bl = 0; bl < G::NBL; ++bl) {
+                    uint32_t ko[8];
+                    k2_block<BF16>(word_of(d.k, G::NBL * b + bl), &cx.km[16 * bl], ko);
+                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
+                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
+                }
+            }
+        }
+    } else if (bits == 4) {
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+            if (b < nblk) {
+#pragma unroll
+                for (int bl = 0; bl < G::NBL; ++bl) {
+                    uint32_t ko[8];
+                    k4_block<BF16>(word_of(d.k, 2 * G::NBL * b + 2 * bl), word_of(d.k, 2 * G::NBL * b + 2 * bl + 1),
+                                   &cx.km[16 * bl], ko);
+                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
+                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
+                }
+            }
+        }
+    } else {
+        // raw keys, read now (raw steps are rare in decode): quarter j of token r16
+        u32x4 kq[G::QV];
+        const uint16_t *kb;
+        size_t row0;
+        if (st.kind == ST_RAW) {
+            const SegmentView &sg = p.segs[st.seg];
+            row0 = bh * (size_t)sg.capacity + st.t;
+            kb = reinterpret_cast<const uint16_t *>(sg.k);
+        } else {
+            row0 = bh * (size_t)p.n_cur + st.t;
+            kb = reinterpret_cast<const uint16_t *>(p.k_cur);
+        }
+        const bool ok = r16 < st.len;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(kb + (row0 + (ok ? r16 : 0)) * HD + j * (HD / 4));
+#pragma unroll
+        for (int i = 0; i < G::QV; ++i) kq[i] = src[i];
+#pragma unroll
+        for (int bl = 0; bl < G::NBL; ++bl) {
+            uint32_t dd[8], ko[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) dd[q] = word_of(kq, 8 * bl + q);
+            to_positions(dd, ko);
+            s[0] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[0]);
+            s[0] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[0]);
+        }
+    }
+    // this step's keys are expanded: fetch the next step's keys and K-group {step, zero}
+    if (nx_packed) {
+        if (nx.new_group) load_kmeta<HD>(cx.km, p, nx, bh);
+        load_k<HD>(d, p, nx, bh);
+    }
+
+    // ---- values -> LDS (row = token, position order), zero past the step
+    __builtin_amdgcn_wave_barrier();
+    if (bits == 2) {
+        const bool mask = st.len < TP;
+        uint16_t *row = vt + lane * G::VROW;
+#pragma unroll
+        for (int gv = 0; gv < HD / 32; ++gv) {
+            uint32_t tlo, thi;
+            v_int2_table<BF16>(d.vm[gv], tlo, thi);
+#pragma unroll
+            for (int bb = 0; bb < 2; ++bb) {
+                const int blk = 2 * gv + bb;
+                uint32_t vo[8];
+                v_int2_block(word_of(d.v, blk), tlo, thi, vo);
+                if (mask) {
+#pragma unroll
+                    for (int q = 0; q < 8; ++q) vo[q] = lane < st.len ? vo[q] : 0u;
+                }
+                *reinterpret_cast<u32x4 *>(row + 16 * blk) = u32x4{vo[0], vo[1], vo[2], vo[3]};
+                *reinterpret_cast<u32x4 *>(row + 16 * blk + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
+            }
+        }
+    } else if (bits == 4) {
+        const int tok = lane / 2, half = lane % 2;
+        const bool ok = tok < st.len;
+        uint16_t *row = vt + tok * G::VROW + half * (HD / 2);
+#pragma unroll
+        for (int hb = 0; hb < HD / 32; ++hb) {
+            uint32_t vo[8];
+            v4_block<BF16>(word_of(d.v, 2 * hb), word_of(d.v, 2 * hb + 1), d.vm[hb / 2], vo);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vo[q] = ok ? vo[q] : 0u;
+            *reinterpret_cast<u32x4 *>(row + 16 * hb) = u32x4{vo[0], vo[1], vo[2], vo[3]};
+            *reinterpret_cast<u32x4 *>(row + 16 * hb + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
+        }
+    } else {
+        // raw values, read now: quarter lane % 4 of token lane / 4
+        const int tr = lane / 4, qq = lane % 4;
+        const bool ok = tr < st.len;
+        const uint16_t *vb;
+        size_t row0;
+        if (st.kind == ST_RAW) {
+            const SegmentView &sg = p.segs[st.seg];
+            row0 = bh * (size_t)sg.capacity + st.t;
+            vb = reinterpret_cast<const uint16_t *>(sg.v);
+        } else {
+            row0 = bh * (size_t)p.n_cur + st.t;
+            vb = reinterpret_cast<const uint16_t *>(p.v_cur);
+        }
+        u32x4 vq[G::QV];
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vb + (row0 + (ok ? tr : 0)) * HD + qq * (HD / 4));
+#pragma unroll
+        for (int i = 0; i < G::QV; ++i) vq[i] = src[i];
+        uint16_t *row = vt + tr * G::VROW + 16 * G::NBL * qq;
+#pragma unroll
+        for (int bl = 0; bl < G::NBL; ++bl) {
+            uint32_t dd[8], vo[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) dd[q] = word_of(vq, 8 * bl + q);
+            to_positions(dd, vo);
+#pragma unroll
+            for (int q = 0; q < 8; ++q) vo[q] = ok ? E::raw_to_f16(vo[q]) : 0u;
+            *reinterpret_cast<u32x4 *>(row + 16 * bl) = u32x4{vo[0], vo[1], vo[2], vo[3]};
+            *reinterpret_cast<u32x4 *>(row + 16 * bl + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
+        }
+    }
+    // this step's values are in LDS: fetch the next step's
+    if (nx_packed) load_v<HD>(d, p, nx, bh);
+
+    // ---- online softmax (log2 domain); tokens past the step do not exist
+    if (st.len < TP) {
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) s[b][i] = 16 * b + 4 * j + i < st.len ? s[b][i] : -__builtin_inff();
+    }
+    float sm = max3(s[0][0], s[0][1], s[0][2]);
+    sm = max3(sm, s[0][3], s[1][0]);
+    sm = max3(sm, s[1][1], s[1][2]);
+    sm = max3(sm, s[1][3], s[2][0]);
+    sm = max3(sm, s[2][1], s[2][2]);
+    sm = max3(sm, s[2][3], s[3][0]);
+    sm = max3(sm, s[3][1], s[3][2]);
+    sm = fmaxf(sm, s[3][3]);
+    float mt = __builtin_fmaf(sm, p.scale_log2, -cx.beta);
+    mt = fmaxf(mt, __shfl_xor(mt, 16));
+    mt = fmaxf(mt, other_half(mt));
+    if (__any(mt > cx.m + kDRescale)) {
+        const float mnew = fmaxf(cx.m, mt);
+        const float alpha = exp2_fast(cx.m - mnew);
+        cx.m = mnew;
+        cx.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < G::DB; ++db) cx.o[db] *= alpha;
+    }
+    const float off = -(cx.beta + cx.m);
+    const int nh = (st.len + 31) / 32;
+    f16x8 pf[2];
+    float ps = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h < nh) {
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                f16x2 pr;
+                pr.x = (_Float16)exp2_fast(__builtin_fmaf(s[2 * h + i / 4][i % 4], p.scale_log2, off));
+                pr.y = (_Float16)exp2_fast(__builtin_fmaf(s[2 * h + i / 4][i % 4 + 1], p.scale_log2, off));
+                pf[h][i] = pr.x;
+                pf[h][i + 1] = pr.y;
+                ps = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
+            }
+        }
+    }
+    cx.l += ps;
+
+    // ---- O^T += V^T P^T over 32-token slices. A operand, lane group j: positions
+    // 16 db + L%16 at tokens 32 h + 4 j + 0..3 (k-slots 0..3) and 32 h + 16 + 4 j + 0..3
+    // (k-slots 4..7), the same tokens P's k-slots hold. In each 16-lane group, source lane
+    // 4 jj + aa addresses token T + jj at positions 16 db + 4 aa.
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int l16 = lane % 16;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        if (h < nh) {
+            const int tok0 = 32 * h + 4 * j + l16 / 4;
+#pragma unroll
+            for (int db = 0; db < G::DB; ++db) {
+                const uint16_t *p0 = vt + tok0 * G::VROW + 16 * db + 4 * (l16 % 4);
+                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(p0));
+                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (__attribute__((address_space(3))) s16x4 *)(p0 + 16 * G::VROW));
+                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+                const f16x8 a = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+                cx.o[db] = mfma16_f16(a, pf[h], cx.o[db]);
+            }
+        }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+template <int HD, bool BF16>
+__global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
+    typedef DGeo<HD> G;
+    typedef typename DCtx<HD, BF16>::vec vec;
+    __shared__ __attribute__((aligned(16))) uint16_t smem[kDWaves * G::VTILE];
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: the walk runs on scalars
+    const int r16 = lane % 16, j = lane / 16;
+    const int b = blockIdx.y / p.n_kv_heads, h = blockIdx.y % p.n_kv_heads;
+    const int gqa = p.n_q_heads / p.n_kv_heads;
+    const int rows = gqa * p.n_q;   // <= 16
+    const size_t bh = (size_t)b * p.n_kv_heads + h;
+    uint16_t *vt = smem + wave * G::VTILE;
+
+    DCtx<HD, BF16> cx;
+    {
+        // Q^T operand: quarter j of row r16 in position order
+        u32x4 qv[G::QV];
+        if (r16 < rows) {
+            const int hq = h * gqa + r16 / p.n_q, qi = r16 % p.n_q;
+            const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
+            const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(p.q) + qrow * HD +
+                                                               j * (HD / 4));
+#pragma unroll
+            for (int i = 0; i < G::QV; ++i) qv[i] = src[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < G::QV; ++i) qv[i] = u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int bl = 0; bl < G::NBL; ++bl) {
+            uint32_t dd[8], o8[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) dd[q] = word_of(qv, 8 * bl + q);
+            to_positions(dd, o8);
+            cx.qb[2 * bl] = __builtin_bit_cast(vec, u32x4{o8[0], o8[1], o8[2], o8[3]});
+            cx.qb[2 * bl + 1] = __builtin_bit_cast(vec, u32x4{o8[4], o8[5], o8[6], o8[7]});
+        }
+    }
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db) cx.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < 16 * G::NBL; ++i) cx.km[i] = 0u;
+    cx.m = -__builtin_inff();
+    cx.l = 0.f;
+    cx.beta = 0.f;
+    // the value tile starts finite: rows past a short step are multiplied by p = 0
+    for (int i = lane; i < G::VTILE / 8; i += kWave) reinterpret_cast<u32x4 *>(vt)[i] = u32x4{0u, 0u, 0u, 0u};
+
+    const int part = blockIdx.x * kDWaves + wave;
+    const int tb = part * p.split_tokens;
+    const int te = min(p.n_total, tb + p.split_tokens);
+    Walker wk;
+    wk.init();
+    DSet d;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) d.k[i] = d.v[i] = u32x4{0u, 0u, 0u, 0u};
+    d.vm = u32x4{0u, 0u, 0u, 0u};
+    Step s0 = uniform(wk.next(p, tb, te));
+    Step s1 = uniform(wk.next(p, tb, te));
+    if (s0.kind == ST_PACKED) {
+        load_kmeta<HD>(cx.km, p, s0, bh);
+        load_k<HD>(d, p, s0, bh);
+        load_v<HD>(d, p, s0, bh);
+    }
+    while (s0.kind != ST_END) {
+        process_step<HD, BF16>(cx, d, s0, s1, vt, p, bh);
+        s0 = s1;
+        s1 = uniform(wk.next(p, tb, te));
+    }
+
+    // ---- merge the four waves: (m, l, O) per row through LDS
+    float lt = cx.l + __shfl_xor(cx.l, 16);
+    lt += other_half(lt);
+    float *sc = reinterpret_cast<float *>(vt);   // the wave's own value tile, no longer read
+#pragma unroll
+    for (int db = 0; db < G::DB; ++db)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) sc[r16 * G::OROW + swap_pos(16 * db + 4 * j + i)] = cx.o[db][i];
+    if (j == 0) {
+        sc[16 * G::OROW + r16] = cx.m;
+        sc[16 * G::OROW + 16 + r16] = lt;
+    }
+    __syncthreads();
+    const size_t n_rows_total = (size_t)p.batch * p.n_q_heads * p.n_q;
+    for (int idx = tid; idx < rows * HD; idx += kDThreads) {
+        const int r = idx / HD, c = idx % HD;
+        float M = -__builtin_inff();
+#pragma unroll
+        for (int w = 0; w < kDWaves; ++w)
+            M = fmaxf(M, reinterpret_cast<const float *>(smem + w * G::VTILE)[16 * G::OROW + r]);
+        float L = 0.f, acc = 0.f;
+        if (M != -__builtin_inff()) {
+#pragma unroll
+            for (int w = 0; w < kDWaves; ++w) {
+                const float *sw = reinterpret_cast<const float *>(smem + w * G::VTILE);
+                const float wt = exp2_fast(sw[16 * G::OROW + r] - M);
+                L = __builtin_fmaf(wt, sw[16 * G::OROW + 16 + r], L);
+                acc = __builtin_fmaf(wt, sw[r * G::OROW + c], acc);
+            }
+        }
+        const int hq = h * gqa + r / p.n_q, qi = r % p.n_q;
+        const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
+        if (gridDim.x == 1) {
+            const float v = acc / L;
+            if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + c] = v;
+            else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_bf16_bits(v);
+            else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_f16_bits(v);
+            if (c == 0 && p.lse != nullptr) p.lse[qrow] = (M + __log2f(L)) * kLn2;
+        } else {
+            float *pp = p.partial + ((size_t)blockIdx.x * n_rows_total + qrow) * (HD + 2);
+            pp[c] = acc;
+            if (c == 0) {
+                pp[HD] = M;
+                pp[HD + 1] = L;
+            }
+        }
+    }
+}
+
+template <int HD, bool BF16>
+hipError_t launch_d(const AttnParams &p, hipStream_t s) {
+    dim3 grid(p.n_split, p.batch * p.n_kv_heads);
+    hipLaunchKernelGGL((decode_kernel<HD, BF16>), grid, dim3(kDThreads), 0, s, p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || p.n_split == 1) return e;
+    return launch_combine(p, s);
+}
+
+}  // namespace
+
+bool decode_eligible(int dtype, int n_q_heads, int n_kv_heads, int head_dim, int n_q, const int *seg_bits,
+                     int n_segs) {
+    if ((long)(n_q_heads / n_kv_heads) * n_q > kDecodeRows || dtype != DT_BF16) return false;
+    for (int i = 0; i < n_segs; ++i) {
+        if (seg_bits[i] == 16) return false;
+        if (seg_bits[i] == 4 && head_dim != 128) return false;
+    }
+    return true;
+}
+
+void decode_plan(int batch, int n_kv_heads, int n_total, int *n_wg, int *wave_tokens) {
+    const long bh = (long)batch * n_kv_heads;
+    const long want = (512 + bh - 1) / bh;                       // two workgroups per CU
+    const long cap = (n_total + kDWaves * 256 - 1) / (kDWaves * 256);  // >= 256 tokens per wave
+    long nw = want < cap ? want : cap;
+    if (nw < 1) nw = 1;
+    long wt = (n_total + kDWaves * nw - 1) / (kDWaves * nw);
+    wt = (wt + TP - 1) / TP * TP;
+    nw = (n_total + kDWaves * wt - 1) / (kDWaves * wt);
+    if (nw < 1) nw = 1;
+    *n_wg = (int)nw;
+    *wave_tokens = (int)wt;
+}
+
+hipError_t launch_decode(const AttnParams &p, hipStream_t s) {
+    const bool bf = p.dtype == DT_BF16;
+    if (p.head_dim == 64) return bf ? launch_d<64, true>(p, s) : launch_d<64, false>(p, s);
+    return bf ? launch_d<128, true>(p, s) : launch_d<128, false>(p, s);
+}
+
+}  // namespace kvq

@@ -61,13 +61,28 @@ struct AttnParams {
     void *out;
     int32_t out_dtype;
     float *lse;
-    int32_t n_split;               // token splits; > 1 writes partials to the workspace
-    int32_t split_tokens;          // tokens per split (multiple of 64)
+    int32_t n_split;               // token splits (decode: workgroups per (batch, KV head));
+                                   // > 1 writes partials to the workspace
+    int32_t split_tokens;          // tokens per split (decode: per wave), multiple of 64
     float *partial;                // [n_split][rows][head_dim + 2]
+    int32_t decode;                // run the decode-shaped kernel (decided by decode_eligible)
 };
-// Number of token splits and the workspace they need.
-void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total,
+// Number of token splits and the workspace they need (either kernel; decode selects the
+// decode-shaped one).
+void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total, bool decode,
                     int *n_split, int *split_tokens, size_t *workspace_bytes);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
+// Log-sum-exp merge of n_split partials into the output.
+hipError_t launch_combine(const AttnParams &p, hipStream_t s);
+
+// Decode-shaped attention: at most kDecodeRows query rows per (batch, KV head), bf16, and
+// packed segments only (INT2; INT4 at head_dim 128). Raw segments, fp16 and INT4 at
+// head_dim 64 run on the chunk kernel.
+constexpr int kDecodeRows = 16;
+bool decode_eligible(int dtype, int n_q_heads, int n_kv_heads, int head_dim, int n_q, const int *seg_bits,
+                     int n_segs);
+// Workgroups per (batch, KV head) and tokens per wave.
+void decode_plan(int batch, int n_kv_heads, int n_total, int *n_wg, int *wave_tokens);
+hipError_t launch_decode(const AttnParams &p, hipStream_t s);
 
 }  // namespace kvq

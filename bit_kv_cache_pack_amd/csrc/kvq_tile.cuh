@@ -1,0 +1,150 @@
+// Dequantization of one (token, 16-channel block) unit of a packed cache row, and the
+// small lane helpers both attention kernels use (gfx950).
+//
+// Dequantized value of code c with the fp16 {step, zero} of its group:
+//   x = E(fl32(c * step + zero)),  E = round to the element dtype (bf16 or fp16),
+// c * step is exact in fp32 (c <= 15, step has 11 significant bits), so one fused
+// multiply-add rounds once, as the plain mul-then-add would.
+//
+// Inside a 16-channel block, values are emitted in "position" order: position 4j + k
+// holds channel 4k + j (a 4x4 transpose, an involution). That is the order in which
+// INT2 codes fall out of a word when it is shifted by 2j and masked per byte, and the
+// order the attention kernels keep in LDS and in their MFMA operands; Q is loaded in the
+// same order and O is written back in channel order.
+#pragma once
+
+#include "kvq_device.cuh"
+
+namespace kvq {
+
+// position <-> channel inside a 16-channel block: p = 4j + k  <->  c = 4k + j
+__device__ __forceinline__ int swap_pos(int c) { return (c & ~15) | ((c & 3) << 2) | ((c >> 2) & 3); }
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi, uint32_t lo, uint32_t sel) {
+    return __builtin_amdgcn_perm(hi, lo, sel);
+}
+// a * (fp16 in the low half of m) + (fp16 in the high half of m), one rounding in fp32
+__device__ __forceinline__ float fma_mix(float a, uint32_t m) {
+    const _Float16 s = __builtin_bit_cast(_Float16, (uint16_t)(m & 0xffffu));
+    const _Float16 z = __builtin_bit_cast(_Float16, (uint16_t)(m >> 16));
+    return __builtin_fmaf(a, (float)s, (float)z);
+}
+// a * (fp16 in the low half of m)
+__device__ __forceinline__ float mul_step(float a, uint32_t m) {
+    return a * (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xffffu));
+}
+__device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// value of lane L ^ 32
+__device__ __forceinline__ float other_half(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+}
+__device__ __forceinline__ float max3(float a, float b, float c) { return fmaxf(a, fmaxf(b, c)); }
+
+template <bool BF16> struct Elem;
+template <> struct Elem<true> {
+    typedef bf16x8 vec;
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_bf16x2(a, b); }
+    // element-dtype rounding of two values, returned as the fp16 pair the PV product uses
+    static __device__ __forceinline__ uint32_t pack_v(float a, float b) { return bf16x2_to_f16x2(pack_bf16x2(a, b)); }
+    static __device__ __forceinline__ uint32_t raw_to_f16(uint32_t p) { return bf16x2_to_f16x2(p); }
+    static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) { return mfma32_bf16(a, b, c); }
+    static __device__ __forceinline__ f32x4 mma16(vec a, vec b, f32x4 c) { return mfma16_bf16(a, b, c); }
+    static __device__ __forceinline__ float val(uint32_t bits16) { return bf16_bits_to_f32(bits16); }
+};
+template <> struct Elem<false> {
+    typedef f16x8 vec;
+    static __device__ __forceinline__ uint32_t pack(float a, float b) { return pack_f16x2(a, b); }
+    static __device__ __forceinline__ uint32_t pack_v(float a, float b) { return pack_f16x2(a, b); }
+    static __device__ __forceinline__ uint32_t raw_to_f16(uint32_t p) { return p; }
+    static __device__ __forceinline__ f32x16 mma(vec a, vec b, f32x16 c) { return mfma32_f16(a, b, c); }
+    static __device__ __forceinline__ f32x4 mma16(vec a, vec b, f32x4 c) { return mfma16_f16(a, b, c); }
+    static __device__ __forceinline__ float val(uint32_t bits16) { return f16_bits_to_f32(bits16); }
+};
+
+// 16 raw 16-bit values of one block in channel order (dword m = channels 2m, 2m+1) to
+// position order.
+__device__ __forceinline__ void to_positions(const uint32_t (&d)[8], uint32_t (&o)[8]) {
+    // positions (4j, 4j+1) = channels (j, 4+j); (4j+2, 4j+3) = channels (8+j, 12+j)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+        o[2 * j] = perm(d[2 + j / 2], d[j / 2], sel);
+        o[2 * j + 1] = perm(d[6 + j / 2], d[4 + j / 2], sel);
+    }
+}
+
+// Keys, INT2: word w holds the block's 16 codes (channel c at bits 2c); km[c] is the
+// {step, zero} of channel c. Output: 8 element-dtype pairs in position order.
+template <bool BF16>
+__device__ __forceinline__ void k_int2_block(uint32_t w, const uint32_t *km, uint32_t (&ko)[8]) {
+    typedef Elem<BF16> E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // byte b of x is the code of channel 4b + j
+        const uint32_t x = (w >> (2 * j)) & 0x03030303u;
+        const float y0 = fma_mix((float)(x & 0xffu), km[j]);
+        const float y1 = fma_mix((float)((x >> 8) & 0xffu), km[4 + j]);
+        const float y2 = fma_mix((float)((x >> 16) & 0xffu), km[8 + j]);
+        const float y3 = fma_mix((float)(x >> 24), km[12 + j]);
+        ko[2 * j] = E::pack(y0, y1);
+        ko[2 * j + 1] = E::pack(y2, y3);
+    }
+}
+
+// Keys, INT4: w0 holds channels 0..7, w1 channels 8..15 (channel c at bits 4 (c mod 8)).
+template <bool BF16>
+__device__ __forceinline__ void k_int4_block(uint32_t w0, uint32_t w1, const uint32_t *km, uint32_t (&ko)[8]) {
+    typedef Elem<BF16> E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        // bytes of x: channels j, 8 + j, 4 + j, 12 + j
+        const uint32_t x = ((w0 >> (4 * j)) & 0x000f000fu) | (((w1 >> (4 * j)) & 0x000f000fu) << 8);
+        const float y0 = fma_mix((float)(x & 0xffu), km[j]);
+        const float y1 = fma_mix((float)((x >> 16) & 0xffu), km[4 + j]);
+        const float y2 = fma_mix((float)((x >> 8) & 0xffu), km[8 + j]);
+        const float y3 = fma_mix((float)(x >> 24), km[12 + j]);
+        ko[2 * j] = E::pack(y0, y1);
+        ko[2 * j + 1] = E::pack(y2, y3);
+    }
+}
+
+// Values, INT2: the 4 possible dequantized values of a (token, V group) as fp16 (after
+// rounding to the element dtype), split into a table of low bytes and one of high bytes.
+template <bool BF16>
+__device__ __forceinline__ void v_int2_table(uint32_t vmeta, uint32_t &tlo, uint32_t &thi) {
+    typedef Elem<BF16> E;
+    const uint32_t p01 = E::pack_v(fma_mix(0.0f, vmeta), fma_mix(1.0f, vmeta));
+    const uint32_t p23 = E::pack_v(fma_mix(2.0f, vmeta), fma_mix(3.0f, vmeta));
+    tlo = perm(p23, p01, 0x06040200u);
+    thi = perm(p23, p01, 0x07050301u);
+}
+// Values, INT2: one word of 16 codes through the table; code c selects byte c of the
+// low table and byte c of the high table (selector c + 4). Output: fp16 pairs in
+// position order.
+__device__ __forceinline__ void v_int2_block(uint32_t w, uint32_t tlo, uint32_t thi, uint32_t (&vo)[8]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t x = (w >> (2 * j)) & 0x03030303u;
+        const uint32_t x4 = x | 0x04040404u;
+        vo[2 * j] = perm(thi, tlo, perm(x4, x, 0x05010400u));
+        vo[2 * j + 1] = perm(thi, tlo, perm(x4, x, 0x07030602u));
+    }
+}
+// Values, INT4 (one {step, zero} for the whole block): fp16 pairs in position order.
+template <bool BF16>
+__device__ __forceinline__ void v_int4_block(uint32_t w0, uint32_t w1, uint32_t vmeta, uint32_t (&vo)[8]) {
+    typedef Elem<BF16> E;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t x = ((w0 >> (4 * j)) & 0x000f000fu) | (((w1 >> (4 * j)) & 0x000f000fu) << 8);
+        const float v0 = fma_mix((float)(x & 0xffu), vmeta);
+        const float v1 = fma_mix((float)((x >> 16) & 0xffu), vmeta);
+        const float v2 = fma_mix((float)((x >> 8) & 0xffu), vmeta);
+        const float v3 = fma_mix((float)(x >> 24), vmeta);
+        vo[2 * j] = E::pack_v(v0, v1);
+        vo[2 * j + 1] = E::pack_v(v2, v3);
+    }
+}
+
+}  // namespace kvq

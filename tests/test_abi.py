@@ -149,8 +149,10 @@ def test_attention_segment_checks():
 
 
 def test_workspace_size_and_check():
-    # decode shape: one query per head -> token splits -> a workspace is needed
-    a, arr = _attn(segs=[_seg(n_tokens=1000, n_kgroups=8)], n_q=1, n_cur=0, k_cur=None, v_cur=None)
+    # decode shape over a long history: one query per head -> several workgroups per KV head
+    # whose partials need a workspace
+    a, arr = _attn(segs=[_seg(capacity=20000, n_tokens=20000, n_kgroups=157, kgroup_capacity=157)], n_q=1,
+                   n_cur=0, k_cur=None, v_cur=None)
     n = ctypes.c_size_t()
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK
     assert n.value > 0 and n.value % (4 * 130) == 0
@@ -158,6 +160,9 @@ def test_workspace_size_and_check():
     a.workspace, a.workspace_bytes = FAKE, n.value - 1
     assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_WORKSPACE
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), None) == kvq.ERR_ARG
+    # a short decode history fits one workgroup per KV head: no workspace
+    a, arr = _attn(segs=[_seg(n_tokens=1000, n_kgroups=8)], n_q=1, n_cur=0, k_cur=None, v_cur=None)
+    assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK and n.value == 0
     # a large chunk fills the GPU without splits: no workspace
     a, arr = _attn(n_q=8192, n_q_heads=12, n_kv_heads=12, segs=[_seg(n_kv_heads=12, n_tokens=900, n_kgroups=8)])
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK and n.value == 0
