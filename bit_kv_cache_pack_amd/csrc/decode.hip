@@ -59,6 +59,14 @@ template <int HD> struct DGeo {
 
 enum : int { ST_END = 0, ST_PACKED = 1, ST_RAW = 2, ST_CUR = 3 };
 
+// Group table entry g, read through a global-address-space pointer: the kernel never
+// writes global memory before its epilogue, so the uniform read can use a scalar load,
+// which does not wait behind the vector loads of the next step in flight.
+__device__ __forceinline__ int group_start(const int32_t *tab, int g) {
+    typedef const __attribute__((address_space(1))) int32_t *gptr;
+    return ((gptr)tab)[g];
+}
+
 struct Step {
     int kind, seg, g, t, len;
     int new_group;  // first step of K-group g in this walk
@@ -101,7 +109,7 @@ struct Walker {
                     int lo = 0, hi = sg.n_kgroups - 1;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
-                        if (sg.kgroup_start[mid + 1] <= a) lo = mid + 1; else hi = mid;
+                        if (group_start(sg.kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
                     }
                     g = lo;
                     last_g = -1;
@@ -123,7 +131,7 @@ struct Walker {
             }
             if (g >= sg.n_kgroups) { t = e; continue; }
             // clamped: a corrupt table must not send reads outside the segment
-            const int ge = min(max(sg.kgroup_start[g + 1], 0), sg.n_tokens);
+            const int ge = min(max(group_start(sg.kgroup_start, g + 1), 0), sg.n_tokens);
             if (ge <= t) { ++g; continue; }
             const int len = min(sg.bits == 4 ? TP / 2 : TP, min(ge, e) - t);
             Step r{ST_PACKED, si, g, t, len, g != last_g};
@@ -346,6 +354,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     const int lane = threadIdx.x % kWave, r16 = lane % 16, j = lane / 16;
     const bool packed = st.kind == ST_PACKED;
     const int bits = packed ? p.segs[st.seg].bits : 16;
+    const int len = st.len;
     const bool nx_packed = nx.kind == ST_PACKED;
 
     if (packed && st.new_group) cx.beta = p.jensen ? p.beta_log2 * jensen_sum<HD, BF16>(cx) : 0.f;
@@ -353,7 +362,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
 
     // ---- S^T = K^ Q^T: s[b][i] = logit of token 16 b + 4 j + i for row r16
     f32x4 s[4];
-    const int nblk = (st.len + 15) / 16;
+    const int nblk = (len + 15) / 16;
 #pragma unroll
     for (int b = 0; b < 4; ++b) s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (bits == 2) {
@@ -396,7 +405,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             row0 = bh * (size_t)p.n_cur + st.t;
             kb = reinterpret_cast<const uint16_t *>(p.k_cur);
         }
-        const bool ok = r16 < st.len;
+        const bool ok = r16 < len;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(kb + (row0 + (ok ? r16 : 0)) * HD + j * (HD / 4));
 #pragma unroll
         for (int i = 0; i < G::QV; ++i) kq[i] = src[i];
@@ -417,9 +426,8 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     }
 
     // ---- values -> LDS (row = token, position order), zero past the step
-    __builtin_amdgcn_wave_barrier();
     if (bits == 2) {
-        const bool mask = st.len < TP;
+        const bool mask = len < TP;
         uint16_t *row = vt + lane * G::VROW;
 #pragma unroll
         for (int gv = 0; gv < HD / 32; ++gv) {
@@ -432,7 +440,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
                 v_int2_block(word_of(d.v, blk), tlo, thi, vo);
                 if (mask) {
 #pragma unroll
-                    for (int q = 0; q < 8; ++q) vo[q] = lane < st.len ? vo[q] : 0u;
+                    for (int q = 0; q < 8; ++q) vo[q] = lane < len ? vo[q] : 0u;
                 }
                 *reinterpret_cast<u32x4 *>(row + 16 * blk) = u32x4{vo[0], vo[1], vo[2], vo[3]};
                 *reinterpret_cast<u32x4 *>(row + 16 * blk + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
@@ -440,7 +448,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
         }
     } else if (bits == 4) {
         const int tok = lane / 2, half = lane % 2;
-        const bool ok = tok < st.len;
+        const bool ok = tok < len;
         uint16_t *row = vt + tok * G::VROW + half * (HD / 2);
 #pragma unroll
         for (int hb = 0; hb < HD / 32; ++hb) {
@@ -454,7 +462,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     } else {
         // raw values, read now: quarter lane % 4 of token lane / 4
         const int tr = lane / 4, qq = lane % 4;
-        const bool ok = tr < st.len;
+        const bool ok = tr < len;
         const uint16_t *vb;
         size_t row0;
         if (st.kind == ST_RAW) {
@@ -486,11 +494,11 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     if (nx_packed) load_v<HD>(d, p, nx, bh);
 
     // ---- online softmax (log2 domain); tokens past the step do not exist
-    if (st.len < TP) {
+    if (len < TP) {
 #pragma unroll
         for (int b = 0; b < 4; ++b)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) s[b][i] = 16 * b + 4 * j + i < st.len ? s[b][i] : -__builtin_inff();
+            for (int i = 0; i < 4; ++i) s[b][i] = 16 * b + 4 * j + i < len ? s[b][i] : -__builtin_inff();
     }
     float sm = max3(s[0][0], s[0][1], s[0][2]);
     sm = max3(sm, s[0][3], s[1][0]);
@@ -512,7 +520,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
         for (int db = 0; db < G::DB; ++db) cx.o[db] *= alpha;
     }
     const float off = -(cx.beta + cx.m);
-    const int nh = (st.len + 31) / 32;
+    const int nh = (len + 31) / 32;
     f16x8 pf[2];
     float ps = 0.f;
 #pragma unroll
@@ -535,9 +543,8 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     // 16 db + L%16 at tokens 32 h + 4 j + 0..3 (k-slots 0..3) and 32 h + 16 + 4 j + 0..3
     // (k-slots 4..7), the same tokens P's k-slots hold. In each 16-lane group, source lane
     // 4 jj + aa addresses token T + jj at positions 16 db + 4 aa.
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // the wave's own LDS writes above are read below: one wave's LDS operations complete
+    // in issue order, and the compiler keeps the reads after the stores they may alias
     const int l16 = lane % 16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
@@ -556,9 +563,6 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             }
         }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 template <int HD, bool BF16>
