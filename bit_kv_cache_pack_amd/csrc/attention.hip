@@ -84,19 +84,40 @@ __device__ __forceinline__ Tile uniform(Tile t) {
 }
 
 // Walks the segments, then the current chunk, over the token split [tb, te), in tiles
-// that never cross a K-group. Uniform across the workgroup.
+// that never cross a K-group. Uniform across the workgroup: the walk's state, and the
+// call's scalars it compares against, are re-read as uniform on every call, since the
+// compiler may route them through joins of per-lane branches (e.g. the staging code's idle
+// threads), which it would otherwise treat as per-lane values.
 struct Walker {
     int si, t, e, g, gfirst, last_g, inited;
-    __device__ __forceinline__ void init() { si = 0; inited = 0; last_g = -1; t = e = g = gfirst = 0; }
-    __device__ Tile next(const AttnParams &p, int tb, int te) {
+    int ns, cb, nt, tb, te;   // segments, first current-chunk token, all tokens, the split
+    __device__ __forceinline__ void init(const AttnParams &p, int tb_, int te_) {
+        si = 0; inited = 0; last_g = -1; t = e = g = gfirst = 0;
+        ns = p.n_segs; nt = p.n_total; cb = p.n_total - p.n_cur; tb = tb_; te = te_;
+    }
+    __device__ __forceinline__ void make_uniform() {
+        si = __builtin_amdgcn_readfirstlane(si);
+        t = __builtin_amdgcn_readfirstlane(t);
+        e = __builtin_amdgcn_readfirstlane(e);
+        g = __builtin_amdgcn_readfirstlane(g);
+        gfirst = __builtin_amdgcn_readfirstlane(gfirst);
+        last_g = __builtin_amdgcn_readfirstlane(last_g);
+        inited = __builtin_amdgcn_readfirstlane(inited);
+        ns = __builtin_amdgcn_readfirstlane(ns);
+        cb = __builtin_amdgcn_readfirstlane(cb);
+        nt = __builtin_amdgcn_readfirstlane(nt);
+        tb = __builtin_amdgcn_readfirstlane(tb);
+        te = __builtin_amdgcn_readfirstlane(te);
+    }
+    __device__ Tile next(const AttnParams &p) {
+        make_uniform();
         while (true) {
-            if (si > p.n_segs) return Tile{TILE_END, 0, 0, 0, 0, 0, 0};
+            if (si > ns) return Tile{TILE_END, 0, 0, 0, 0, 0, 0};
             if (!inited) {
                 int a;
-                if (si == p.n_segs) {
-                    const int cb = p.n_total - p.n_cur;
+                if (si == ns) {
                     a = max(tb, cb) - cb;
-                    e = min(te, p.n_total) - cb;
+                    e = min(te, nt) - cb;
                 } else {
                     const SegmentView &sg = p.segs[si];
                     a = max(tb, sg.token_begin) - sg.token_begin;
@@ -105,12 +126,12 @@ struct Walker {
                 if (a >= e) { ++si; continue; }
                 t = a;
                 inited = 1;
-                if (si < p.n_segs && p.segs[si].bits != 16) {
+                if (si < ns && p.segs[si].bits != 16) {
                     const SegmentView &sg = p.segs[si];
                     int lo = 0, hi = sg.n_kgroups - 1;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
-                        if (sg.kgroup_start[mid + 1] <= a) lo = mid + 1; else hi = mid;
+                        if (group_start(sg.kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
                     }
                     g = lo;
                     gfirst = lo;
@@ -118,7 +139,7 @@ struct Walker {
                 }
             }
             if (t >= e) { ++si; inited = 0; continue; }
-            if (si == p.n_segs) {
+            if (si == ns) {
                 const int len = min(TT, e - t);
                 Tile r{TILE_CUR, si, 0, t, len, 0, 0};
                 t += len;
@@ -133,7 +154,7 @@ struct Walker {
             }
             if (g >= sg.n_kgroups) { t = e; continue; }
             // clamped: a corrupt table must not send reads outside the segment
-            const int ge = min(max(sg.kgroup_start[g + 1], 0), sg.n_tokens);
+            const int ge = min(max(group_start(sg.kgroup_start, g + 1), 0), sg.n_tokens);
             if (ge <= t) { ++g; continue; }
             const int len = min(TT, min(ge, e) - t);
             const int ng = g != last_g;
@@ -455,7 +476,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     typedef typename C::vec vec;
     typedef Geo<HD> G;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G::BUF];
-    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid % kWave;
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: wave_ok branches on scalars
     const int r32 = lane % 32, hh = lane / 32;
     const int b = blockIdx.y / p.n_kv_heads, h = blockIdx.y % p.n_kv_heads;
     const int gqa = p.n_q_heads / p.n_kv_heads;
@@ -501,8 +523,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     const int tb = blockIdx.z * p.split_tokens;
     const int te = min(p.n_total, tb + p.split_tokens);
     Walker wk;
-    wk.init();
-    Tile cur = uniform(wk.next(p, tb, te));
+    wk.init(p, tb, te);
+    Tile cur = uniform(wk.next(p));
     Prefetch pf;
     int gbase = 0;  // first group of the current Jensen block
     if (cur.kind != TILE_END) {
@@ -512,7 +534,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     __syncthreads();
     int buf = 0;
     while (cur.kind != TILE_END) {
-        const Tile nxt = uniform(wk.next(p, tb, te));
+        const Tile nxt = uniform(wk.next(p));
         if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
         if (wave_ok) {
             if (cur.kind == TILE_PACKED) {

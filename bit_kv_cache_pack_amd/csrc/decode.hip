@@ -59,13 +59,6 @@ template <int HD> struct DGeo {
 
 enum : int { ST_END = 0, ST_PACKED = 1, ST_RAW = 2, ST_CUR = 3 };
 
-// Group table entry g, read through a global-address-space pointer: the kernel never
-// writes global memory before its epilogue, so the uniform read can use a scalar load,
-// which does not wait behind the vector loads of the next step in flight.
-__device__ __forceinline__ int group_start(const int32_t *tab, int g) {
-    typedef const __attribute__((address_space(1))) int32_t *gptr;
-    return ((gptr)tab)[g];
-}
 
 struct Step {
     int kind, seg, g, t, len;

@@ -34,6 +34,14 @@ __device__ __forceinline__ float mul_step(float a, uint32_t m) {
     return a * (float)__builtin_bit_cast(_Float16, (uint16_t)(m & 0xffffu));
 }
 __device__ __forceinline__ float exp2_fast(float x) { return __builtin_amdgcn_exp2f(x); }
+// Entry g of a K-group table, read through a global-address-space pointer. Through a
+// generic pointer the read could be private memory, which makes its value (and every
+// walker decision taken from it) per-lane; as a global read of a uniform address it is
+// uniform, and with no global store before the kernels' epilogues it can be a scalar load.
+__device__ __forceinline__ int group_start(const int32_t *tab, int g) {
+    typedef const __attribute__((address_space(1))) int32_t *gptr;
+    return ((gptr)tab)[g];
+}
 // value of lane L ^ 32
 __device__ __forceinline__ float other_half(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
