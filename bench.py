@@ -117,6 +117,37 @@ class ChunkStep:
             events[2].record()
 
 
+def kernel_source_digest() -> str:
+    """sha256 over the HIP sources of the library (any change invalidates stored counters)."""
+    import hashlib
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "bit_kv_cache_pack_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        if name.endswith((".hip", ".cuh", ".h")):
+            with open(os.path.join(csrc, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from profiles/, or None when no summary
+    exists or the kernel sources changed since its counters were taken."""
+    path = os.path.join(ROOT, "profiles", "%s_%s_traffic.md" % (kernel, workload))
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("source_sha256") != kernel_source_digest():
+        return None
+    try:
+        return int(vals["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(step: ChunkStep, target_s: float = 15.0):
     """Time the CPU oracle (as it stands) on a bounded sample of the same workload: the
     quantize-append of the current chunk in full, and the attention of every r-th query row
@@ -176,6 +207,9 @@ def main():
     ap.add_argument("--workload", default="video_chunk_int2_h12_d128", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
+    ap.add_argument("--probe-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (the reference dispatch "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -222,10 +256,12 @@ def main():
         alg = kvb + step.qo_bytes()
         ach = alg / (attn_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "attention_kernel"}
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": stored_traffic(w.name, "decode_kernel"),
+                "kernel": "decode_kernel"}
     else:
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None, "kernel": "attention_kernel"}
+                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(w.name, "attention_kernel"),
+                "kernel": "attention_kernel"}
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -242,6 +278,14 @@ def main():
         "append": {"ms": round(app_avg, 4), "bytes": step.append_bytes(),
                    "gbps": round(step.append_bytes() / (app_avg * 1e-3) / 1e9, 1) if step.append else None},
     }
+    if args.probe_copy_mib:
+        n = args.probe_copy_mib << 20
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB read, %d MiB written" % (args.probe_copy_mib, args.probe_copy_mib))
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         res["cpu_baseline"] = cpu_baseline(step)
