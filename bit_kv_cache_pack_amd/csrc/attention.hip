@@ -253,47 +253,14 @@ __device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, co
         const u32x4 c = pf.w[4];
         const uint32_t vmeta = pf.w[5].x;
         if (bits == 2) {
-            // keys: byte k of x is the code of channel 4k + j
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t x = (c.x >> (2 * j)) & 0x03030303u;
-                const float y0 = fma_mix((float)(x & 0xffu), km[j]);
-                const float y1 = fma_mix((float)((x >> 8) & 0xffu), km[4 + j]);
-                const float y2 = fma_mix((float)((x >> 16) & 0xffu), km[8 + j]);
-                const float y3 = fma_mix((float)(x >> 24), km[12 + j]);
-                ko[2 * j] = E::pack(y0, y1);
-                ko[2 * j + 1] = E::pack(y2, y3);
-            }
-            // values: the 4 exact dequantized values of this (token, V group) as fp16,
-            // looked up with byte permutes (code c -> bytes 2c, 2c+1)
-            const uint32_t lut_lo = E::pack_v(fma_mix(0.0f, vmeta), fma_mix(1.0f, vmeta));
-            const uint32_t lut_hi = E::pack_v(fma_mix(2.0f, vmeta), fma_mix(3.0f, vmeta));
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t x = (c.y >> (2 * j)) & 0x03030303u;
-                const uint32_t y = x << 1, yp = y | 0x01010101u;
-                vo[2 * j] = perm(lut_hi, lut_lo, perm(yp, y, 0x05010400u));
-                vo[2 * j + 1] = perm(lut_hi, lut_lo, perm(yp, y, 0x07030602u));
-            }
+            k2_block<BF16>(c.x, km, ko);
+            uint32_t tlo, thi;
+            v_int2_table<BF16>(vmeta, tlo, thi);
+            v_int2_block(c.y, tlo, thi, vo);
         } else {
-            // INT4: two words per block; bytes of x = channels j, 8+j, 4+j, 12+j
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const uint32_t xk = ((c.x >> (4 * j)) & 0x000f000fu) | (((c.z >> (4 * j)) & 0x000f000fu) << 8);
-                const float y0 = fma_mix((float)(xk & 0xffu), km[j]);
-                const float y1 = fma_mix((float)((xk >> 16) & 0xffu), km[4 + j]);
-                const float y2 = fma_mix((float)((xk >> 8) & 0xffu), km[8 + j]);
-                const float y3 = fma_mix((float)(xk >> 24), km[12 + j]);
-                ko[2 * j] = E::pack(y0, y1);
-                ko[2 * j + 1] = E::pack(y2, y3);
-                const uint32_t xv = ((c.y >> (4 * j)) & 0x000f000fu) | (((c.w >> (4 * j)) & 0x000f000fu) << 8);
-                const float v0 = fma_mix((float)(xv & 0xffu), vmeta);
-                const float v1 = fma_mix((float)((xv >> 16) & 0xffu), vmeta);
-                const float v2 = fma_mix((float)((xv >> 8) & 0xffu), vmeta);
-                const float v3 = fma_mix((float)(xv >> 24), vmeta);
-                vo[2 * j] = E::pack_v(v0, v1);
-                vo[2 * j + 1] = E::pack_v(v2, v3);
-            }
+            // INT4: two words per block (x, z: keys; y, w: values)
+            k4_block<BF16>(c.x, c.z, km, ko);
+            v4_block<BF16>(c.y, c.w, vmeta, vo);
         }
         if (r >= tl.len) {
 #pragma unroll
@@ -323,7 +290,7 @@ template <int HD, bool BF16> struct Ctx {
     static constexpr int DB = HD / 32;   // 32-position blocks of the output
     vec q[KS];        // this lane's query at positions 16 ks + 8 hh + i
     f32x16 o[DB];     // O^T accumulators, rows = positions
-    f32x16 bacc;      // Jensen sums of a block of 32 K-groups (rows) for this lane's query
+    float *btab;      // LDS [32 K-groups][32 queries]: Jensen sums of the current block of groups
     float m, l;       // running max (log2 domain) and this lane's partial row sum
     float beta;       // Jensen term of the current group, log2 domain
 };
@@ -369,19 +336,16 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
         acc = mfma32_bf16(ah, bl8, acc);
         acc = mfma32_bf16(al, bh8, acc);
     }
-    cx.bacc = acc;
+    // C layout: acc[j] is group 8 (j / 4) + 4 hh + j % 4 of the block, for query r32. The
+    // wave alone writes and reads its table, and one wave's LDS operations complete in order.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cx.btab[(8 * (j / 4) + 4 * hh + (j % 4)) * 32 + r32] = acc[j];
 }
 
 // The Jensen sum of group row rr (0..31) of the current block for this lane's query.
 template <int HD, bool BF16>
 __device__ __forceinline__ float beta_of(const Ctx<HD, BF16> &cx, int rr) {
-    const int hh = (threadIdx.x % kWave) / 32;
-    rr = __builtin_amdgcn_readfirstlane(rr);  // uniform: lets the table be indexed in registers
-    const int owner = (rr >> 2) & 1;
-    const int j = 4 * (rr >> 3) + (rr & 3);
-    const float v = cx.bacc[j];
-    const float other = other_half(v);
-    return hh == owner ? v : other;
+    return cx.btab[rr * 32 + (threadIdx.x % 32)];
 }
 
 template <int HD, bool BF16>
@@ -476,6 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     typedef typename C::vec vec;
     typedef Geo<HD> G;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G::BUF];
+    __shared__ float btab_all[kWaves][32 * 32];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: wave_ok branches on scalars
     const int r32 = lane % 32, hh = lane / 32;
@@ -515,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     }
 #pragma unroll
     for (int db = 0; db < C::DB; ++db) cx.o[db] = f32x16{};
-    cx.bacc = f32x16{};
+    cx.btab = btab_all[wave];
     cx.m = -__builtin_inff();
     cx.l = 0.f;
     cx.beta = 0.f;

@@ -239,57 +239,6 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
     }
 }
 
-// Two codes (bytes 0,1 or, with HI, 2,3 of x, each 0..15) as exact floats.
-template <bool HI>
-__device__ __forceinline__ float2 codes2(uint32_t x) {
-    const auto r = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(x, 512.0f, HI);
-    return float2{r[0], r[1]};
-}
-
-// Keys, INT2, one 16-channel block from its word, through the fp8 conversion.
-template <bool BF16>
-__device__ __forceinline__ void k2_block(uint32_t w, const uint32_t *km, uint32_t (&ko)[8]) {
-    typedef Elem<BF16> E;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t x = (w >> (2 * j)) & 0x03030303u;   // bytes: channels j, 4+j, 8+j, 12+j
-        const float2 a = codes2<false>(x), b = codes2<true>(x);
-        ko[2 * j] = E::pack(fma_mix(a.x, km[j]), fma_mix(a.y, km[4 + j]));
-        ko[2 * j + 1] = E::pack(fma_mix(b.x, km[8 + j]), fma_mix(b.y, km[12 + j]));
-    }
-}
-// Keys, INT4: w0 = channels 0..7, w1 = channels 8..15 of the block.
-template <bool BF16>
-__device__ __forceinline__ void k4_block(uint32_t w0, uint32_t w1, const uint32_t *km, uint32_t (&ko)[8]) {
-    typedef Elem<BF16> E;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        // bytes of x0: channels jj, 2+jj, 4+jj, 6+jj; of x1: the same plus 8
-        const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
-        const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
-        const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
-        ko[2 * jj] = E::pack(fma_mix(a0.x, km[jj]), fma_mix(b0.x, km[4 + jj]));
-        ko[2 * jj + 1] = E::pack(fma_mix(a1.x, km[8 + jj]), fma_mix(b1.x, km[12 + jj]));
-        ko[2 * jj + 4] = E::pack(fma_mix(a0.y, km[2 + jj]), fma_mix(b0.y, km[6 + jj]));
-        ko[2 * jj + 5] = E::pack(fma_mix(a1.y, km[10 + jj]), fma_mix(b1.y, km[14 + jj]));
-    }
-}
-// Values, INT4, one block with one {step, zero}: fp16 pairs in position order.
-template <bool BF16>
-__device__ __forceinline__ void v4_block(uint32_t w0, uint32_t w1, uint32_t vm, uint32_t (&vo)[8]) {
-    typedef Elem<BF16> E;
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
-        const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
-        const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
-        vo[2 * jj] = E::pack_v(fma_mix(a0.x, vm), fma_mix(b0.x, vm));
-        vo[2 * jj + 1] = E::pack_v(fma_mix(a1.x, vm), fma_mix(b1.x, vm));
-        vo[2 * jj + 4] = E::pack_v(fma_mix(a0.y, vm), fma_mix(b0.y, vm));
-        vo[2 * jj + 5] = E::pack_v(fma_mix(a1.y, vm), fma_mix(b1.y, vm));
-    }
-}
-
 template <int HD, bool BF16> struct DCtx {
     typedef typename Elem<BF16>::vec vec;
     vec qb[DGeo<HD>::KS];              // B operand: Q^T, quarter L/16 of row L%16, position order
