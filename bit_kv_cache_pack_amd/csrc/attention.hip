@@ -91,9 +91,12 @@ __device__ __forceinline__ Tile uniform(Tile t) {
 struct Walker {
     int si, t, e, g, gfirst, last_g, inited;
     int ns, cb, nt, tb, te;   // segments, first current-chunk token, all tokens, the split
+    int sbits, sn, sng;       // the current segment's bit-width, tokens, K-groups
+    int ge, gen;              // end token of group g, and of group g + 1 (fetched a group ahead)
     __device__ __forceinline__ void init(const AttnParams &p, int tb_, int te_) {
         si = 0; inited = 0; last_g = -1; t = e = g = gfirst = 0;
         ns = p.n_segs; nt = p.n_total; cb = p.n_total - p.n_cur; tb = tb_; te = te_;
+        sbits = 16; sn = sng = ge = gen = 0;
     }
     __device__ __forceinline__ void make_uniform() {
         si = __builtin_amdgcn_readfirstlane(si);
@@ -108,6 +111,16 @@ struct Walker {
         nt = __builtin_amdgcn_readfirstlane(nt);
         tb = __builtin_amdgcn_readfirstlane(tb);
         te = __builtin_amdgcn_readfirstlane(te);
+        sbits = __builtin_amdgcn_readfirstlane(sbits);
+        sn = __builtin_amdgcn_readfirstlane(sn);
+        sng = __builtin_amdgcn_readfirstlane(sng);
+        ge = __builtin_amdgcn_readfirstlane(ge);
+        gen = __builtin_amdgcn_readfirstlane(gen);
+    }
+    // end token of group gg of the current segment, clamped: a corrupt table must not send
+    // reads outside the segment
+    __device__ __forceinline__ int group_end(const AttnParams &p, int gg) const {
+        return gg < sng ? min(max(group_start(p.segs[si].kgroup_start, gg + 1), 0), sn) : sn;
     }
     __device__ Tile next(const AttnParams &p) {
         make_uniform();
@@ -118,24 +131,29 @@ struct Walker {
                 if (si == ns) {
                     a = max(tb, cb) - cb;
                     e = min(te, nt) - cb;
+                    sbits = 16;
                 } else {
                     const SegmentView &sg = p.segs[si];
                     a = max(tb, sg.token_begin) - sg.token_begin;
                     e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
+                    sbits = sg.bits;
+                    sn = sg.n_tokens;
+                    sng = sg.n_kgroups;
                 }
                 if (a >= e) { ++si; continue; }
                 t = a;
                 inited = 1;
-                if (si < ns && p.segs[si].bits != 16) {
-                    const SegmentView &sg = p.segs[si];
-                    int lo = 0, hi = sg.n_kgroups - 1;
+                if (si < ns && sbits != 16) {
+                    int lo = 0, hi = sng - 1;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
-                        if (group_start(sg.kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
+                        if (group_start(p.segs[si].kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
                     }
                     g = lo;
                     gfirst = lo;
                     last_g = -1;
+                    ge = group_end(p, g);
+                    gen = group_end(p, g + 1);
                 }
             }
             if (t >= e) { ++si; inited = 0; continue; }
@@ -145,23 +163,29 @@ struct Walker {
                 t += len;
                 return r;
             }
-            const SegmentView &sg = p.segs[si];
-            if (sg.bits == 16) {
+            if (sbits == 16) {
                 const int len = min(TT, e - t);
                 Tile r{TILE_RAW, si, 0, t, len, 0, 0};
                 t += len;
                 return r;
             }
-            if (g >= sg.n_kgroups) { t = e; continue; }
-            // clamped: a corrupt table must not send reads outside the segment
-            const int ge = min(max(group_start(sg.kgroup_start, g + 1), 0), sg.n_tokens);
-            if (ge <= t) { ++g; continue; }
+            if (g >= sng) { t = e; continue; }
+            if (ge <= t) {
+                ++g;
+                ge = gen;
+                gen = group_end(p, g + 1);
+                continue;
+            }
             const int len = min(TT, min(ge, e) - t);
             const int ng = g != last_g;
             Tile r{TILE_PACKED, si, g, t, len, ng, ng && ((g - gfirst) % 32 == 0)};
             last_g = g;
             t += len;
-            if (t >= ge) ++g;
+            if (t >= ge) {
+                ++g;
+                ge = gen;
+                gen = group_end(p, g + 1);
+            }
             return r;
         }
     }
@@ -206,7 +230,9 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
         }
         pf.w[4] = c;
         pf.w[5].x = m;
-        if (tid < G::UNITS) {
+        // the {step, zero} of the thread's 16 channels change only with the K-group (a thread
+        // keeps its channel block from tile to tile; raw tiles are followed by a new group)
+        if (tid < G::UNITS && tl.new_group) {
             const u32x4 *km = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf.w[i] = km[i];
@@ -487,9 +513,24 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 
     const int tb = blockIdx.z * p.split_tokens;
     const int te = min(p.n_total, tb + p.split_tokens);
+    // Wave 0 alone walks the tiles, two ahead, and publishes them in a 3-slot LDS ring: the
+    // walk is scalar work, and a CU's scalar unit is shared by all its waves. Tile k is
+    // written before barrier k - 2 and read after it; its slot is rewritten only after
+    // barrier k + 1, by when every wave has read it.
+    __shared__ Tile desc[3];
     Walker wk;
-    wk.init(p, tb, te);
-    Tile cur = uniform(wk.next(p));
+    if (wave == 0) {
+        wk.init(p, tb, te);
+        const Tile t0 = uniform(wk.next(p));
+        const Tile t1 = t0.kind == TILE_END ? t0 : uniform(wk.next(p));
+        if (lane == 0) {
+            desc[0] = t0;
+            desc[1] = t1;
+        }
+    }
+    __syncthreads();
+    Tile cur = uniform(desc[0]);
+    Tile nxt = uniform(desc[1]);
     Prefetch pf;
     int gbase = 0;  // first group of the current Jensen block
     if (cur.kind != TILE_END) {
@@ -497,10 +538,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         stage_tile<HD, BF16>(smem, pf, cur, cur.kind == TILE_PACKED ? p.segs[cur.seg].bits : 16);
     }
     __syncthreads();
-    int buf = 0;
+    int buf = 0, slot = 2;  // the ring slot of tile i + 2
     while (cur.kind != TILE_END) {
-        const Tile nxt = uniform(wk.next(p));
         if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
+        if (wave == 0) {
+            const Tile far = nxt.kind == TILE_END ? nxt : uniform(wk.next(p));
+            if (lane == 0) desc[slot] = far;
+        }
         if (wave_ok) {
             if (cur.kind == TILE_PACKED) {
                 if (cur.batch) {
@@ -519,6 +563,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         __syncthreads();
         buf ^= 1;
         cur = nxt;
+        nxt = uniform(desc[slot]);
+        slot = slot == 2 ? 0 : slot + 1;
     }
 
     // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
