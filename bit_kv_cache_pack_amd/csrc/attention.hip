@@ -194,18 +194,20 @@ struct Walker {
 // ---------------------------------------------------------------- prefetch (global -> registers)
 // Thread tid owns the unit (token r = tid / NBLK, 16-channel block b = tid % NBLK).
 // Raw tiles: w[0..1] = 16 key elements, w[2..3] = 16 value elements. Packed tiles:
-// w[0..3] = {step, zero} of the block's 16 key channels, w[4] = codes (x, z: key words;
-// y, w: value words), w[5].x = the token's value {step, zero} for the block.
+// w[0..3] = {step, zero} of the block's 16 key channels, w[4] = a key word pair (x, y) and
+// a value word pair (z, w), w[5].x = the token's value {step, zero} for the block.
 struct Prefetch {
     u32x4 w[6];
 };
 
+// Loads are unconditional, from rows clamped into the tile (staging zeroes rows past it):
+// a load under a per-lane condition would have to land before its registers are merged
+// with the old contents, which turns every prefetch into a wait for memory.
 template <int HD>
 __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p, const Tile &tl, size_t bh) {
     typedef Geo<HD> G;
     const int tid = threadIdx.x;
-    const int r = tid / G::NBLK, b = tid % G::NBLK;
-    const bool mine = tid < G::UNITS && r < tl.len;
+    const int r = min(tid / G::NBLK, tl.len - 1), b = tid % G::NBLK;
     if (tl.kind == TILE_PACKED) {
         const SegmentView &sg = p.segs[tl.seg];
         const int bits = sg.bits;
@@ -214,25 +216,17 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
         const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k) + row0 * wpr;
         const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v) + row0 * wpr;
         const uint32_t *vm = sg.v_meta + row0 * (HD / 32);
-        u32x4 c = {0u, 0u, 0u, 0u};
-        uint32_t m = 0u;
-        if (mine) {
-            if (bits == 2) {
-                c.x = kc[(uint32_t)(r * wpr + b)];
-                c.y = vc[(uint32_t)(r * wpr + b)];
-            } else {
-                const u32x2 k2 = *reinterpret_cast<const u32x2 *>(kc + (uint32_t)(r * wpr + 2 * b));
-                const u32x2 v2 = *reinterpret_cast<const u32x2 *>(vc + (uint32_t)(r * wpr + 2 * b));
-                c.x = k2.x; c.z = k2.y;
-                c.y = v2.x; c.w = v2.y;
-            }
-            m = vm[(uint32_t)(r * (HD / 32) + b / 2)];
-        }
-        pf.w[4] = c;
-        pf.w[5].x = m;
+        // one word pair per thread for either bit-width, so both fill the same registers: INT4
+        // needs words 2b, 2b+1 of the row; INT2 needs word b, and reads the aligned pair
+        // around it (still inside the row)
+        const uint32_t widx = (uint32_t)(r * wpr + (bits == 2 ? (b & ~1) : 2 * b));
+        const u32x2 k2 = *reinterpret_cast<const u32x2 *>(kc + widx);
+        const u32x2 v2 = *reinterpret_cast<const u32x2 *>(vc + widx);
+        pf.w[4] = u32x4{k2.x, k2.y, v2.x, v2.y};
+        pf.w[5].x = vm[(uint32_t)(r * (HD / 32) + b / 2)];
         // the {step, zero} of the thread's 16 channels change only with the K-group (a thread
         // keeps its channel block from tile to tile; raw tiles are followed by a new group)
-        if (tid < G::UNITS && tl.new_group) {
+        if (tl.new_group) {
             const u32x4 *km = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
 #pragma unroll
             for (int i = 0; i < 4; ++i) pf.w[i] = km[i];
@@ -249,15 +243,10 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
             kb = reinterpret_cast<const uint16_t *>(p.k_cur) + row0 * HD;
             vb = reinterpret_cast<const uint16_t *>(p.v_cur) + row0 * HD;
         }
-        const u32x4 z = {0u, 0u, 0u, 0u};
-        if (mine) {
-            const u32x4 *ks = reinterpret_cast<const u32x4 *>(kb) + (uint32_t)(r * (HD / 8) + 2 * b);
-            const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb) + (uint32_t)(r * (HD / 8) + 2 * b);
-            pf.w[0] = ks[0]; pf.w[1] = ks[1];
-            pf.w[2] = vs[0]; pf.w[3] = vs[1];
-        } else {
-            pf.w[0] = z; pf.w[1] = z; pf.w[2] = z; pf.w[3] = z;
-        }
+        const u32x4 *ks = reinterpret_cast<const u32x4 *>(kb) + (uint32_t)(r * (HD / 8) + 2 * b);
+        const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb) + (uint32_t)(r * (HD / 8) + 2 * b);
+        pf.w[0] = ks[0]; pf.w[1] = ks[1];
+        pf.w[2] = vs[0]; pf.w[3] = vs[1];
     }
 }
 
@@ -276,17 +265,17 @@ __device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, co
         for (int i = 0; i < 4; ++i) {
             km[4 * i] = pf.w[i].x; km[4 * i + 1] = pf.w[i].y; km[4 * i + 2] = pf.w[i].z; km[4 * i + 3] = pf.w[i].w;
         }
-        const u32x4 c = pf.w[4];
+        const u32x4 c = pf.w[4];   // key word pair, value word pair
         const uint32_t vmeta = pf.w[5].x;
         if (bits == 2) {
-            k2_block<BF16>(c.x, km, ko);
+            const bool odd = b & 1;
+            k2_block<BF16>(odd ? c.y : c.x, km, ko);
             uint32_t tlo, thi;
             v_int2_table<BF16>(vmeta, tlo, thi);
-            v_int2_block(c.y, tlo, thi, vo);
+            v_int2_block(odd ? c.w : c.z, tlo, thi, vo);
         } else {
-            // INT4: two words per block (x, z: keys; y, w: values)
-            k4_block<BF16>(c.x, c.z, km, ko);
-            v4_block<BF16>(c.y, c.w, vmeta, vo);
+            k4_block<BF16>(c.x, c.y, km, ko);
+            v4_block<BF16>(c.z, c.w, vmeta, vo);
         }
         if (r >= tl.len) {
 #pragma unroll
@@ -299,6 +288,10 @@ __device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, co
                                  E::raw_to_f16(pf.w[3].z), E::raw_to_f16(pf.w[3].w)};
         to_positions(kd8, ko);
         to_positions(vd8, vo);
+        if (r >= tl.len) {
+#pragma unroll
+            for (int q = 0; q < 8; ++q) { ko[q] = 0u; vo[q] = 0u; }
+        }
     }
     u32x4 *kd = reinterpret_cast<u32x4 *>(buf + r * G::KROW + 16 * b);
     u32x4 *vd = reinterpret_cast<u32x4 *>(buf + G::KBUF + r * G::VROW + 16 * b);
@@ -540,11 +533,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     __syncthreads();
     int buf = 0, slot = 2;  // the ring slot of tile i + 2
     while (cur.kind != TILE_END) {
-        if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
+        // the walk first: its reads must not queue behind this tile's prefetch
         if (wave == 0) {
             const Tile far = nxt.kind == TILE_END ? nxt : uniform(wk.next(p));
             if (lane == 0) desc[slot] = far;
         }
+        if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
         if (wave_ok) {
             if (cur.kind == TILE_PACKED) {
                 if (cur.batch) {
