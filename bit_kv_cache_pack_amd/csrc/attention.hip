@@ -83,6 +83,17 @@ __device__ __forceinline__ Tile uniform(Tile t) {
     return t;
 }
 
+// Entry g of a K-group table through the scalar cache, for a uniform address. The kernel
+// never writes the table, but the barriers' fences keep the compiler from proving that, so
+// it would read it with a vector load: hundreds of cycles, behind every vector load in
+// flight. The load waits for itself inside the same asm statement.
+__device__ __forceinline__ int group_start_scalar(const int32_t *tab, int g) {
+    const int32_t *ptr = tab + g;
+    int v;
+    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
+    return v;
+}
+
 // Walks the segments, then the current chunk, over the token split [tb, te), in tiles
 // that never cross a K-group. Uniform across the workgroup: the walk's state, and the
 // call's scalars it compares against, are re-read as uniform on every call, since the
@@ -120,7 +131,7 @@ struct Walker {
     // end token of group gg of the current segment, clamped: a corrupt table must not send
     // reads outside the segment
     __device__ __forceinline__ int group_end(const AttnParams &p, int gg) const {
-        return gg < sng ? min(max(group_start(p.segs[si].kgroup_start, gg + 1), 0), sn) : sn;
+        return gg < sng ? min(max(group_start_scalar(p.segs[si].kgroup_start, gg + 1), 0), sn) : sn;
     }
     __device__ Tile next(const AttnParams &p) {
         make_uniform();
@@ -147,7 +158,7 @@ struct Walker {
                     int lo = 0, hi = sng - 1;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
-                        if (group_start(p.segs[si].kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
+                        if (group_start_scalar(p.segs[si].kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
                     }
                     g = lo;
                     gfirst = lo;
