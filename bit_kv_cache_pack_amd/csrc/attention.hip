@@ -378,12 +378,33 @@ __device__ __forceinline__ float beta_of(const Ctx<HD, BF16> &cx, int rr) {
     return cx.btab[rr * 32 + (threadIdx.x % 32)];
 }
 
+// A operands of O^T += V^T P^T for the 16 tokens 16 st .. 16 st + 15 of the tile:
+// va[db] rows = positions 32 db + r32, k-slot i of half hh = token 16 st + 4 hh + (i % 4)
+// + 8 (i / 4), matching P's layout. Two transposed 8-byte reads per operand: in each
+// 16-lane group, source lane 4 jj + aa addresses token T + jj at positions base + 4 aa, and
+// lane l receives tokens T..T+3 at position base + l.
+template <int HD>
+__device__ __forceinline__ void load_v_operands(f16x8 (&va)[HD / 32], const uint16_t *vl, int st, int pos_base) {
+    typedef Geo<HD> G;
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    const int lane = threadIdx.x % kWave, hh = lane / 32, l16 = lane % 16;
+    const int tok0 = 16 * st + 4 * hh + l16 / 4;
+#pragma unroll
+    for (int db = 0; db < HD / 32; ++db) {
+        const uint16_t *p0 = vl + tok0 * G::VROW + 32 * db + pos_base;
+        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p0));
+        const s16x4 hi4 =
+            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p0 + 8 * G::VROW));
+        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+        va[db] = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+    }
+}
+
 template <int HD, bool BF16>
 __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *buf, int len, float scale_log2) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
     typedef Geo<HD> G;
-    typedef __attribute__((ext_vector_type(4))) short s16x4;
     const uint16_t *kl = buf;
     const uint16_t *vl = buf + G::KBUF;
     const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
@@ -393,12 +414,21 @@ __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *
     // the tile in two 32-token halves: QK^T, softmax, PV per half (fewer live registers)
 #pragma unroll
     for (int rb = 0; rb < 2; ++rb) {
+        // every K operand of the half is read before the first product: one LDS round trip
+        // per half instead of one per product
+        vec ka[C::KS];
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+            ka[ks] = *reinterpret_cast<const vec *>(kl + (32 * rb + r32) * G::KROW + 16 * ks + 8 * hh);
+        __builtin_amdgcn_sched_barrier(0);
         f32x16 s = {};
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            const vec a = *reinterpret_cast<const vec *>(kl + (32 * rb + r32) * G::KROW + 16 * ks + 8 * hh);
-            s = C::E::mma(a, cx.q[ks], s);
-        }
+        for (int ks = 0; ks < C::KS; ++ks) s = C::E::mma(ka[ks], cx.q[ks], s);
+        // the V operands of the half's first 16 tokens, read while the products run (the
+        // other 16 once the K operands are dead)
+        f16x8 va[2][C::DB];
+        load_v_operands<HD>(va[0], vl, 2 * rb, pos_base);
+        __builtin_amdgcn_sched_barrier(0);
         // token of s[j] = 32 rb + 8 (j / 4) + 4 hh + j % 4; tokens past len do not exist
         if (len < TT) {
 #pragma unroll
@@ -422,6 +452,8 @@ __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *
 #pragma unroll
             for (int db = 0; db < C::DB; ++db) cx.o[db] *= alpha;
         }
+        load_v_operands<HD>(va[1], vl, 2 * rb + 1, pos_base);
+        __builtin_amdgcn_sched_barrier(0);
         // p = 2^(scale s - beta - m) <= 2^8, rounded to fp16; the row sum adds the same
         // rounded values the PV product uses
         const float off = -(cx.beta + cx.m);
@@ -440,27 +472,11 @@ __device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *
             }
         cx.l += ps;
 
-        // O^T += V^T P^T. A operand: rows = positions 32 db + r32, k-slot i of half hh =
-        // token 16 st + 4 hh + (i % 4) + 8 (i / 4), matching P's layout. Two transposed
-        // 8-byte reads per operand: in each 16-lane group, source lane 4 jj + aa addresses
-        // token T + jj at positions base + 4 aa; lane l receives tokens T..T+3 at position
-        // base + l.
+        // O^T += V^T P^T
 #pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2) {
-            const int st = 2 * rb + h2;
-            const int tok0 = 16 * st + 4 * hh + l16 / 4;
+        for (int h2 = 0; h2 < 2; ++h2)
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db) {
-                const uint16_t *p0 = vl + tok0 * G::VROW + 32 * db + pos_base;
-                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(p0));
-                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(p0 + 8 * G::VROW));
-                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
-                const f16x8 a = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-                cx.o[db] = mfma32_f16(a, pf[h2], cx.o[db]);
-            }
-        }
+            for (int db = 0; db < C::DB; ++db) cx.o[db] = mfma32_f16(va[h2][db], pf[h2], cx.o[db]);
     }
 }
 
