@@ -66,20 +66,29 @@ template <int HD> struct Geo {
 // ---------------------------------------------------------------- tile walk
 enum : int { TILE_END = 0, TILE_PACKED = 1, TILE_RAW = 2, TILE_CUR = 3 };
 
+// A tile descriptor in four words: kind, segment, flags and bit-width in one.
 struct Tile {
-    int kind, seg, g, t, len;
-    int new_group;   // first tile of K-group g in this walk
-    int batch;       // a new block of 32 Jensen terms starts at group g
+    int info;        // kind | segment << 4 | new_group << 8 | batch << 9 | bits << 10
+    int g, t, len;   // K-group, first token (segment-relative), tokens
+    __device__ __forceinline__ int kind() const { return info & 15; }
+    __device__ __forceinline__ int seg() const { return (info >> 4) & 15; }
+    // first tile of K-group g in this walk
+    __device__ __forceinline__ bool new_group() const { return (info >> 8) & 1; }
+    // a new block of 32 Jensen terms starts at group g
+    __device__ __forceinline__ bool batch() const { return (info >> 9) & 1; }
+    // the segment's bit-width (16: raw elements)
+    __device__ __forceinline__ int bits() const { return info >> 10; }
+    static __device__ __forceinline__ Tile make(int kind, int seg, int g, int t, int len, int new_group, int batch,
+                                                int bits) {
+        return Tile{kind | seg << 4 | new_group << 8 | batch << 9 | bits << 10, g, t, len};
+    }
 };
 
 __device__ __forceinline__ Tile uniform(Tile t) {
-    t.kind = __builtin_amdgcn_readfirstlane(t.kind);
-    t.seg = __builtin_amdgcn_readfirstlane(t.seg);
+    t.info = __builtin_amdgcn_readfirstlane(t.info);
     t.g = __builtin_amdgcn_readfirstlane(t.g);
     t.t = __builtin_amdgcn_readfirstlane(t.t);
     t.len = __builtin_amdgcn_readfirstlane(t.len);
-    t.new_group = __builtin_amdgcn_readfirstlane(t.new_group);
-    t.batch = __builtin_amdgcn_readfirstlane(t.batch);
     return t;
 }
 
@@ -136,7 +145,7 @@ struct Walker {
     __device__ Tile next(const AttnParams &p) {
         make_uniform();
         while (true) {
-            if (si > ns) return Tile{TILE_END, 0, 0, 0, 0, 0, 0};
+            if (si > ns) return Tile::make(TILE_END, 0, 0, 0, 0, 0, 0, 16);
             if (!inited) {
                 int a;
                 if (si == ns) {
@@ -170,13 +179,13 @@ struct Walker {
             if (t >= e) { ++si; inited = 0; continue; }
             if (si == ns) {
                 const int len = min(TT, e - t);
-                Tile r{TILE_CUR, si, 0, t, len, 0, 0};
+                const Tile r = Tile::make(TILE_CUR, si, 0, t, len, 0, 0, 16);
                 t += len;
                 return r;
             }
             if (sbits == 16) {
                 const int len = min(TT, e - t);
-                Tile r{TILE_RAW, si, 0, t, len, 0, 0};
+                const Tile r = Tile::make(TILE_RAW, si, 0, t, len, 0, 0, 16);
                 t += len;
                 return r;
             }
@@ -189,7 +198,7 @@ struct Walker {
             }
             const int len = min(TT, min(ge, e) - t);
             const int ng = g != last_g;
-            Tile r{TILE_PACKED, si, g, t, len, ng, ng && ((g - gfirst) % 32 == 0)};
+            const Tile r = Tile::make(TILE_PACKED, si, g, t, len, ng, ng && ((g - gfirst) % 32 == 0), sbits);
             last_g = g;
             t += len;
             if (t >= ge) {
@@ -214,38 +223,50 @@ struct Prefetch {
 // Loads are unconditional, from rows clamped into the tile (staging zeroes rows past it):
 // a load under a per-lane condition would have to land before its registers are merged
 // with the old contents, which turns every prefetch into a wait for memory.
+// The thread index, opaque to the compiler: values derived from it are recomputed where
+// they are used instead of being held in registers across the tile loop.
+__device__ __forceinline__ int fresh_tid() {
+    int t = threadIdx.x;
+    asm volatile("" : "+v"(t));
+    return t;
+}
+
 template <int HD>
 __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p, const Tile &tl, size_t bh) {
     typedef Geo<HD> G;
-    const int tid = threadIdx.x;
+    const int tid = fresh_tid();
     const int r = min(tid / G::NBLK, tl.len - 1), b = tid % G::NBLK;
-    if (tl.kind == TILE_PACKED) {
-        const SegmentView &sg = p.segs[tl.seg];
-        const int bits = sg.bits;
+    if (tl.kind() == TILE_END) return;
+    // The same loads for every kind, into the same registers; only their addresses depend
+    // on it. w[0..3]: four 16-byte loads (raw keys and values, or the K-group's
+    // {step, zero} when it changes). w[4], w[5].x: the packed word pairs and value meta
+    // (raw tiles read a harmless copy of their own row).
+    const u32x4 *ka, *va;
+    const u32x2 *kp, *vp;
+    const uint32_t *vmp;
+    bool load4;
+    if (tl.kind() == TILE_PACKED) {
+        const SegmentView &sg = p.segs[tl.seg()];
+        const int bits = tl.bits();
         const int wpr = HD * bits / 32;   // words per token row
         const size_t row0 = bh * (size_t)sg.capacity + tl.t;
         const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k) + row0 * wpr;
         const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v) + row0 * wpr;
-        const uint32_t *vm = sg.v_meta + row0 * (HD / 32);
-        // one word pair per thread for either bit-width, so both fill the same registers: INT4
-        // needs words 2b, 2b+1 of the row; INT2 needs word b, and reads the aligned pair
-        // around it (still inside the row)
+        // one word pair per thread for either bit-width: INT4 needs words 2b, 2b+1 of the
+        // row; INT2 needs word b, and reads the aligned pair around it (still in the row)
         const uint32_t widx = (uint32_t)(r * wpr + (bits == 2 ? (b & ~1) : 2 * b));
-        const u32x2 k2 = *reinterpret_cast<const u32x2 *>(kc + widx);
-        const u32x2 v2 = *reinterpret_cast<const u32x2 *>(vc + widx);
-        pf.w[4] = u32x4{k2.x, k2.y, v2.x, v2.y};
-        pf.w[5].x = vm[(uint32_t)(r * (HD / 32) + b / 2)];
+        kp = reinterpret_cast<const u32x2 *>(kc + widx);
+        vp = reinterpret_cast<const u32x2 *>(vc + widx);
+        vmp = sg.v_meta + row0 * (HD / 32) + (uint32_t)(r * (HD / 32) + b / 2);
         // the {step, zero} of the thread's 16 channels change only with the K-group (a thread
         // keeps its channel block from tile to tile; raw tiles are followed by a new group)
-        if (tl.new_group) {
-            const u32x4 *km = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) pf.w[i] = km[i];
-        }
-    } else if (tl.kind != TILE_END) {
+        ka = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
+        va = ka + 2;
+        load4 = tl.new_group();
+    } else {
         const uint16_t *kb, *vb;
-        if (tl.kind == TILE_RAW) {
-            const SegmentView &sg = p.segs[tl.seg];
+        if (tl.kind() == TILE_RAW) {
+            const SegmentView &sg = p.segs[tl.seg()];
             const size_t row0 = bh * (size_t)sg.capacity + tl.t;
             kb = reinterpret_cast<const uint16_t *>(sg.k) + row0 * HD;
             vb = reinterpret_cast<const uint16_t *>(sg.v) + row0 * HD;
@@ -254,23 +275,47 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
             kb = reinterpret_cast<const uint16_t *>(p.k_cur) + row0 * HD;
             vb = reinterpret_cast<const uint16_t *>(p.v_cur) + row0 * HD;
         }
-        const u32x4 *ks = reinterpret_cast<const u32x4 *>(kb) + (uint32_t)(r * (HD / 8) + 2 * b);
-        const u32x4 *vs = reinterpret_cast<const u32x4 *>(vb) + (uint32_t)(r * (HD / 8) + 2 * b);
-        pf.w[0] = ks[0]; pf.w[1] = ks[1];
-        pf.w[2] = vs[0]; pf.w[3] = vs[1];
+        ka = reinterpret_cast<const u32x4 *>(kb) + (uint32_t)(r * (HD / 8) + 2 * b);
+        va = reinterpret_cast<const u32x4 *>(vb) + (uint32_t)(r * (HD / 8) + 2 * b);
+        kp = reinterpret_cast<const u32x2 *>(ka);
+        vp = reinterpret_cast<const u32x2 *>(va);
+        vmp = reinterpret_cast<const uint32_t *>(ka);
+        load4 = true;
     }
+    if (load4) {
+        pf.w[0] = ka[0];
+        pf.w[1] = ka[1];
+        pf.w[2] = va[0];
+        pf.w[3] = va[1];
+    }
+    const u32x2 k2 = *kp, v2 = *vp;
+    pf.w[4] = u32x4{k2.x, k2.y, v2.x, v2.y};
+    pf.w[5].x = *vmp;
 }
 
 // ---------------------------------------------------------------- staging (registers -> LDS)
-template <int HD, bool BF16>
-__device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, const Tile &tl, int bits) {
-    typedef Geo<HD> G;
+enum : int { STAGE_NONE = 0, STAGE_INT2 = 1, STAGE_INT4 = 2, STAGE_RAW = 3 };
+
+__device__ __forceinline__ int stage_kind(const Tile &tl) {
+    if (tl.kind() == TILE_END) return STAGE_NONE;
+    if (tl.kind() != TILE_PACKED) return STAGE_RAW;
+    return tl.bits() == 2 ? STAGE_INT2 : STAGE_INT4;
+}
+
+// The thread's unit of a prefetched tile, dequantized: 16 keys (element dtype) and 16
+// values (fp16), position order. Rows past the tile's end hold a copy of its last row
+// (the loads are clamped); their scores are masked, so they add nothing.
+template <int SK, bool BF16>
+__device__ __forceinline__ void dequant_unit(const Prefetch &pf, int b, uint32_t (&ko)[8], uint32_t (&vo)[8]) {
     typedef Elem<BF16> E;
-    const int tid = threadIdx.x;
-    if (tid >= G::UNITS) return;
-    const int r = tid / G::NBLK, b = tid % G::NBLK;
-    uint32_t ko[8], vo[8];
-    if (tl.kind == TILE_PACKED) {
+    if constexpr (SK == STAGE_RAW) {
+        const uint32_t kd8[8] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w, pf.w[1].x, pf.w[1].y, pf.w[1].z, pf.w[1].w};
+        const uint32_t vd8[8] = {E::raw_to_f16(pf.w[2].x), E::raw_to_f16(pf.w[2].y), E::raw_to_f16(pf.w[2].z),
+                                 E::raw_to_f16(pf.w[2].w), E::raw_to_f16(pf.w[3].x), E::raw_to_f16(pf.w[3].y),
+                                 E::raw_to_f16(pf.w[3].z), E::raw_to_f16(pf.w[3].w)};
+        to_positions(kd8, ko);
+        to_positions(vd8, vo);
+    } else {
         uint32_t km[16];  // {step, zero} of the block's channels, channel order
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -278,7 +323,7 @@ __device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, co
         }
         const u32x4 c = pf.w[4];   // key word pair, value word pair
         const uint32_t vmeta = pf.w[5].x;
-        if (bits == 2) {
+        if constexpr (SK == STAGE_INT2) {
             const bool odd = b & 1;
             k2_block<BF16>(odd ? c.y : c.x, km, ko);
             uint32_t tlo, thi;
@@ -288,28 +333,36 @@ __device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, co
             k4_block<BF16>(c.x, c.y, km, ko);
             v4_block<BF16>(c.z, c.w, vmeta, vo);
         }
-        if (r >= tl.len) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) { ko[q] = 0u; vo[q] = 0u; }
-        }
-    } else {
-        const uint32_t kd8[8] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w, pf.w[1].x, pf.w[1].y, pf.w[1].z, pf.w[1].w};
-        const uint32_t vd8[8] = {E::raw_to_f16(pf.w[2].x), E::raw_to_f16(pf.w[2].y), E::raw_to_f16(pf.w[2].z),
-                                 E::raw_to_f16(pf.w[2].w), E::raw_to_f16(pf.w[3].x), E::raw_to_f16(pf.w[3].y),
-                                 E::raw_to_f16(pf.w[3].z), E::raw_to_f16(pf.w[3].w)};
-        to_positions(kd8, ko);
-        to_positions(vd8, vo);
-        if (r >= tl.len) {
-#pragma unroll
-            for (int q = 0; q < 8; ++q) { ko[q] = 0u; vo[q] = 0u; }
-        }
     }
-    u32x4 *kd = reinterpret_cast<u32x4 *>(buf + r * G::KROW + 16 * b);
-    u32x4 *vd = reinterpret_cast<u32x4 *>(buf + G::KBUF + r * G::VROW + 16 * b);
-    kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
-    kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
-    vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
-    vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
+}
+
+template <int HD>
+__device__ __forceinline__ void write_unit(uint16_t *buf, const uint32_t (&ko)[8], const uint32_t (&vo)[8]) {
+    typedef Geo<HD> G;
+    const int tid = threadIdx.x;
+    const int r = tid / G::NBLK, b = tid % G::NBLK;
+    if (G::UNITS >= kThreads || tid < G::UNITS) {
+        u32x4 *kd = reinterpret_cast<u32x4 *>(buf + r * G::KROW + 16 * b);
+        u32x4 *vd = reinterpret_cast<u32x4 *>(buf + G::KBUF + r * G::VROW + 16 * b);
+        kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
+        kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
+        vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
+        vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
+    }
+}
+
+template <int HD, bool BF16, int SK>
+__device__ __forceinline__ void stage_only(uint16_t *buf, const Prefetch &pf) {
+    uint32_t ko[8], vo[8];
+    dequant_unit<SK, BF16>(pf, threadIdx.x % Geo<HD>::NBLK, ko, vo);
+    write_unit<HD>(buf, ko, vo);
+}
+
+template <int HD, bool BF16>
+__device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, int sk) {
+    if (sk == STAGE_INT2) stage_only<HD, BF16, STAGE_INT2>(buf, pf);
+    else if (sk == STAGE_INT4) stage_only<HD, BF16, STAGE_INT4>(buf, pf);
+    else if (sk == STAGE_RAW) stage_only<HD, BF16, STAGE_RAW>(buf, pf);
 }
 
 // ---------------------------------------------------------------- per-wave state and compute
@@ -375,109 +428,228 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
 // The Jensen sum of group row rr (0..31) of the current block for this lane's query.
 template <int HD, bool BF16>
 __device__ __forceinline__ float beta_of(const Ctx<HD, BF16> &cx, int rr) {
-    return cx.btab[rr * 32 + (threadIdx.x % 32)];
+    return cx.btab[rr * 32 + (fresh_tid() % 32)];
 }
 
-// A operands of O^T += V^T P^T for the 16 tokens 16 st .. 16 st + 15 of the tile:
-// va[db] rows = positions 32 db + r32, k-slot i of half hh = token 16 st + 4 hh + (i % 4)
-// + 8 (i / 4), matching P's layout. Two transposed 8-byte reads per operand: in each
-// 16-lane group, source lane 4 jj + aa addresses token T + jj at positions base + 4 aa, and
-// lane l receives tokens T..T+3 at position base + l.
-template <int HD>
-__device__ __forceinline__ void load_v_operands(f16x8 (&va)[HD / 32], const uint16_t *vl, int st, int pos_base) {
-    typedef Geo<HD> G;
-    typedef __attribute__((ext_vector_type(4))) short s16x4;
-    const int lane = threadIdx.x % kWave, hh = lane / 32, l16 = lane % 16;
-    const int tok0 = 16 * st + 4 * hh + l16 / 4;
-#pragma unroll
-    for (int db = 0; db < HD / 32; ++db) {
-        const uint16_t *p0 = vl + tok0 * G::VROW + 32 * db + pos_base;
-        const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p0));
-        const s16x4 hi4 =
-            __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p0 + 8 * G::VROW));
-        const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
-        va[db] = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+// Scheduling masks of the instruction-group barriers
+constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSchedDsWrite = 0x200;
+
+// One of 8 slices of the dequantization of the thread's unit (k = 0..7: keys in 0..3,
+// values in 4..7), so that it can be spread between matrix products. ko / vo complete after
+// slices 3 / 7; tab carries the INT2 value table from slice 4 on.
+template <int SK, bool BF16>
+__device__ __forceinline__ void dequant_slice(const Prefetch &pf, int b, int k, uint32_t (&ko)[8],
+                                              uint32_t (&vo)[8], uint32_t (&tab)[2]) {
+    typedef Elem<BF16> E;
+    if constexpr (SK == STAGE_RAW) {
+        // keys: 16-bit elements to position order; values: to fp16 as well
+        if (k == 0) {
+            const uint32_t kd8[8] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w,
+                                     pf.w[1].x, pf.w[1].y, pf.w[1].z, pf.w[1].w};
+            to_positions(kd8, ko);
+        } else if (k == 4) {
+            const uint32_t vd8[8] = {E::raw_to_f16(pf.w[2].x), E::raw_to_f16(pf.w[2].y), E::raw_to_f16(pf.w[2].z),
+                                     E::raw_to_f16(pf.w[2].w), E::raw_to_f16(pf.w[3].x), E::raw_to_f16(pf.w[3].y),
+                                     E::raw_to_f16(pf.w[3].z), E::raw_to_f16(pf.w[3].w)};
+            to_positions(vd8, vo);
+        }
+    } else if constexpr (SK == STAGE_INT2 || SK == STAGE_INT4) {
+        const uint32_t km[16] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w, pf.w[1].x, pf.w[1].y,
+                                 pf.w[1].z, pf.w[1].w, pf.w[2].x, pf.w[2].y, pf.w[2].z, pf.w[2].w,
+                                 pf.w[3].x, pf.w[3].y, pf.w[3].z, pf.w[3].w};
+        const u32x4 c = pf.w[4];   // key word pair, value word pair
+        if constexpr (SK == STAGE_INT2) {
+            const bool odd = b & 1;
+            if (k < 4) {
+                k2_step<BF16>(odd ? c.y : c.x, km, k, ko);
+            } else {
+                if (k == 4) v_int2_table<BF16>(pf.w[5].x, tab[0], tab[1]);
+                v_int2_step(odd ? c.w : c.z, tab[0], tab[1], k - 4, vo);
+            }
+        } else {
+            if (k == 0 || k == 2) k4_step<BF16>(c.x, c.y, km, k / 2, ko);
+            else if (k == 4 || k == 6) v4_step<BF16>(c.z, c.w, pf.w[5].x, (k - 4) / 2, vo);
+        }
     }
 }
 
-template <int HD, bool BF16>
-__device__ __forceinline__ void compute_tile(Ctx<HD, BF16> &cx, const uint16_t *buf, int len, float scale_log2) {
+template <int HD>
+__device__ __forceinline__ void write_keys(uint16_t *buf, const uint32_t (&ko)[8]) {
+    typedef Geo<HD> G;
+    const int tid = threadIdx.x;
+    if (G::UNITS >= kThreads || tid < G::UNITS) {
+        u32x4 *kd = reinterpret_cast<u32x4 *>(buf + (tid / G::NBLK) * G::KROW + 16 * (tid % G::NBLK));
+        kd[0] = u32x4{ko[0], ko[1], ko[2], ko[3]};
+        kd[1] = u32x4{ko[4], ko[5], ko[6], ko[7]};
+    }
+}
+template <int HD>
+__device__ __forceinline__ void write_values(uint16_t *buf, const uint32_t (&vo)[8]) {
+    typedef Geo<HD> G;
+    const int tid = threadIdx.x;
+    if (G::UNITS >= kThreads || tid < G::UNITS) {
+        u32x4 *vd = reinterpret_cast<u32x4 *>(buf + G::KBUF + (tid / G::NBLK) * G::VROW + 16 * (tid % G::NBLK));
+        vd[0] = u32x4{vo[0], vo[1], vo[2], vo[3]};
+        vd[1] = u32x4{vo[4], vo[5], vo[6], vo[7]};
+    }
+}
+
+// S^T = K Q^T for the tile in LDS buffer kl (two 32-token halves, s[rb]), while the
+// thread's unit of the next tile is dequantized into LDS buffer nbuf. A wave issues in
+// order, so the dequantization is written between the products: the matrix core works
+// through each product while the vector unit converts. Operand reads run LEAD products
+// ahead through a ring of registers.
+template <int HD, bool BF16, int SK>
+__device__ __forceinline__ void qk_stage(const Ctx<HD, BF16> &cx, const uint16_t *kl, uint16_t *nbuf,
+                                         const Prefetch &pf, f32x16 (&s)[2]) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
     typedef Geo<HD> G;
-    const uint16_t *kl = buf;
-    const uint16_t *vl = buf + G::KBUF;
+    constexpr int NP = 2 * C::KS;    // products
+    constexpr int LEAD = 2;          // operand reads ahead of their product
+    constexpr int EVERY = NP / 8;    // products per dequantization slice
     const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
+    const int b = threadIdx.x % G::NBLK;
+    const uint16_t *kr = kl + r32 * G::KROW + 8 * hh;
+    uint32_t ko[8], vo[8], tab[2];
+    vec ka[LEAD + 1];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < LEAD; ++i) ka[i] = *reinterpret_cast<const vec *>(kr + 32 * (i / C::KS) * G::KROW + 16 * (i % C::KS));
+    s[0] = f32x16{};
+    s[1] = f32x16{};
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        if (i + LEAD < NP) {
+            const int n = i + LEAD;
+            ka[n % (LEAD + 1)] = *reinterpret_cast<const vec *>(kr + 32 * (n / C::KS) * G::KROW + 16 * (n % C::KS));
+        }
+        s[i / C::KS] = C::E::mma(ka[i % (LEAD + 1)], cx.q[i % C::KS], s[i / C::KS]);
+        if (i % EVERY == 0) {
+            const int k = i / EVERY;
+            dequant_slice<SK, BF16>(pf, b, k, ko, vo, tab);
+            if (SK != STAGE_NONE && k == 3) write_keys<HD>(nbuf, ko);
+            if (SK != STAGE_NONE && k == 7) write_values<HD>(nbuf, vo);
+        }
+    }
+    // keep the written order: per product, its operand read ahead, the product, a slice
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, LEAD, 0);
+#pragma unroll
+    for (int i = 0; i < NP; ++i) {
+        if (i + LEAD < NP) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedValu, 6, 0);
+        if (i == NP / 2 - 1 || i == NP - 1) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 2, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+}
 
-    const int grp = lane / 16, l16 = lane % 16;
-    const int pos_base = 16 * (grp & 1) + 4 * (l16 % 4);
-    // the tile in two 32-token halves: QK^T, softmax, PV per half (fewer live registers)
+// Two of the 8 probabilities of the 16 tokens 16 st .. 16 st + 15 (scores
+// s[st / 2][8 (st % 2) + i], i = 2 k, 2 k + 1), rounded to fp16, and their sum (the row
+// sum adds the same rounded values the PV product uses).
+__device__ __forceinline__ void exp_pair(const f32x16 (&s)[2], int st, int k, float scale_log2, float off,
+                                         f16x8 &pv, float &ps) {
+    f16x2 pr;
+    pr.x = (_Float16)exp2_fast(__builtin_fmaf(s[st / 2][8 * (st % 2) + 2 * k], scale_log2, off));
+    pr.y = (_Float16)exp2_fast(__builtin_fmaf(s[st / 2][8 * (st % 2) + 2 * k + 1], scale_log2, off));
+    pv[2 * k] = pr.x;
+    pv[2 * k + 1] = pr.y;
+    ps = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
+}
+
+// A operand db of O^T += V^T P^T for the 16 tokens 16 st .. 16 st + 15 of the tile:
+// rows = positions 32 db + r32, k-slot i of half hh = token 16 st + 4 hh + (i % 4)
+// + 8 (i / 4), matching P's layout. Two transposed 8-byte reads: in each 16-lane group,
+// source lane 4 jj + aa addresses token T + jj at positions base + 4 aa, and lane l
+// receives tokens T..T+3 at position base + l.
+template <int HD>
+__device__ __forceinline__ f16x8 load_v_operand(const uint16_t *vr, int st, int db) {
+    typedef Geo<HD> G;
+    typedef __attribute__((ext_vector_type(4))) short s16x4;
+    const uint16_t *p0 = vr + 16 * st * G::VROW + 32 * db;
+    const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p0));
+    const s16x4 hi4 =
+        __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(p0 + 8 * G::VROW));
+    const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+    return __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+}
+
+// Online softmax of the tile's scores and O^T += V^T P^T, in four 16-token steps; the
+// probabilities of step st + 1 and its V operand reads are written between the products
+// of step st.
+template <int HD, bool BF16>
+__device__ __forceinline__ void softmax_pv(Ctx<HD, BF16> &cx, const uint16_t *vl, f32x16 (&s)[2], int len,
+                                           float scale_log2) {
+    typedef Ctx<HD, BF16> C;
+    typedef Geo<HD> G;
+    constexpr int DB = C::DB;
+    const int lane = threadIdx.x % kWave, hh = lane / 32, l16 = lane % 16;
+    // token of s[rb][j] = 32 rb + 8 (j / 4) + 4 hh + j % 4; tokens past len do not exist
+    if (len < TT) {
 #pragma unroll
-    for (int rb = 0; rb < 2; ++rb) {
-        // every K operand of the half is read before the first product: one LDS round trip
-        // per half instead of one per product
-        vec ka[C::KS];
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-            ka[ks] = *reinterpret_cast<const vec *>(kl + (32 * rb + r32) * G::KROW + 16 * ks + 8 * hh);
-        __builtin_amdgcn_sched_barrier(0);
-        f32x16 s = {};
-#pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) s = C::E::mma(ka[ks], cx.q[ks], s);
-        // the V operands of the half's first 16 tokens, read while the products run (the
-        // other 16 once the K operands are dead)
-        f16x8 va[2][C::DB];
-        load_v_operands<HD>(va[0], vl, 2 * rb, pos_base);
-        __builtin_amdgcn_sched_barrier(0);
-        // token of s[j] = 32 rb + 8 (j / 4) + 4 hh + j % 4; tokens past len do not exist
-        if (len < TT) {
+        for (int rb = 0; rb < 2; ++rb)
 #pragma unroll
             for (int j = 0; j < 16; ++j) {
                 const int tok = 32 * rb + 8 * (j / 4) + 4 * hh + (j % 4);
-                s[j] = tok < len ? s[j] : -__builtin_inff();
+                s[rb][j] = tok < len ? s[rb][j] : -__builtin_inff();
             }
-        }
-        float sm = max3(s[0], s[1], s[2]);
-#pragma unroll
-        for (int j = 3; j < 15; j += 2) sm = max3(sm, s[j], s[j + 1]);
-        sm = fmaxf(sm, s[15]);
-        // the tile's row maximum of the corrected logits, log2 domain (scale > 0)
-        float mt = __builtin_fmaf(sm, scale_log2, -cx.beta);
-        mt = fmaxf(mt, other_half(mt));
-        if (__any(mt > cx.m + kRescale)) {
-            const float mnew = fmaxf(cx.m, mt);
-            const float alpha = exp2_fast(cx.m - mnew);
-            cx.m = mnew;
-            cx.l *= alpha;
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) cx.o[db] *= alpha;
-        }
-        load_v_operands<HD>(va[1], vl, 2 * rb + 1, pos_base);
-        __builtin_amdgcn_sched_barrier(0);
-        // p = 2^(scale s - beta - m) <= 2^8, rounded to fp16; the row sum adds the same
-        // rounded values the PV product uses
-        const float off = -(cx.beta + cx.m);
-        f16x8 pf[2];
-        float ps = 0.f;
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                f16x2 pr;
-                pr.x = (_Float16)exp2_fast(__builtin_fmaf(s[8 * h2 + i], scale_log2, off));
-                pr.y = (_Float16)exp2_fast(__builtin_fmaf(s[8 * h2 + i + 1], scale_log2, off));
-                pf[h2][i] = pr.x;
-                pf[h2][i + 1] = pr.y;
-                ps = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
-            }
-        cx.l += ps;
-
-        // O^T += V^T P^T
-#pragma unroll
-        for (int h2 = 0; h2 < 2; ++h2)
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db) cx.o[db] = mfma32_f16(va[h2][db], pf[h2], cx.o[db]);
     }
+    float sm = max3(s[0][0], s[0][1], s[1][0]);
+#pragma unroll
+    for (int j = 2; j < 16; ++j) sm = max3(sm, s[0][j], s[1][j - 1]);
+    sm = fmaxf(sm, s[1][15]);
+    // the tile's row maximum of the corrected logits, log2 domain (scale > 0)
+    float mt = __builtin_fmaf(sm, scale_log2, -cx.beta);
+    mt = fmaxf(mt, other_half(mt));
+    if (__any(mt > cx.m + kRescale)) {
+        const float mnew = fmaxf(cx.m, mt);
+        const float alpha = exp2_fast(cx.m - mnew);
+        cx.m = mnew;
+        cx.l *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; ++db) cx.o[db] *= alpha;
+    }
+    // p = 2^(scale s - beta - m) <= 2^8
+    const float off = -(cx.beta + cx.m);
+    const uint16_t *vr = vl + (4 * hh + l16 / 4) * G::VROW + 16 * ((lane / 16) & 1) + 4 * (l16 % 4);
+    float ps = 0.f;
+    f16x8 va[2][DB], pv[2];
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int db = 0; db < DB; ++db) va[0][db] = load_v_operand<HD>(vr, 0, db);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) exp_pair(s, 0, k, scale_log2, off, pv[0], ps);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        const int c = st & 1, n = c ^ 1;
+        if (st < 3) {
+#pragma unroll
+            for (int db = 0; db < DB; ++db) va[n][db] = load_v_operand<HD>(vr, st + 1, db);
+        }
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            cx.o[db] = mfma32_f16(va[c][db], pv[c], cx.o[db]);
+            if (st < 3) {
+                // 4 pairs of the next step spread over the DB products
+#pragma unroll
+                for (int k = db * 4 / DB; k < (db + 1) * 4 / DB; ++k) exp_pair(s, st + 1, k, scale_log2, off, pv[n], ps);
+            }
+        }
+    }
+    // keep the written order
+    __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * DB, 0);
+    __builtin_amdgcn_sched_group_barrier(kSchedValu, 24, 0);
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        if (st < 3) __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2 * DB, 0);
+#pragma unroll
+        for (int db = 0; db < DB; ++db) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            if (st < 3) __builtin_amdgcn_sched_group_barrier(kSchedValu, 24 / DB, 0);
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    cx.l += ps;
 }
 
 template <int HD, bool BF16>
@@ -533,59 +705,84 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 
     const int tb = blockIdx.z * p.split_tokens;
     const int te = min(p.n_total, tb + p.split_tokens);
-    // Wave 0 alone walks the tiles, two ahead, and publishes them in a 3-slot LDS ring: the
-    // walk is scalar work, and a CU's scalar unit is shared by all its waves. Tile k is
-    // written before barrier k - 2 and read after it; its slot is rewritten only after
-    // barrier k + 1, by when every wave has read it.
-    __shared__ Tile desc[3];
-    Walker wk;
+    // Wave 0 alone walks the tiles, three ahead, and publishes them in a 4-slot LDS ring:
+    // the walk is scalar work, and a CU's scalar unit is shared by all its waves. Tile k is
+    // written before barrier k - 3 and read after it; its slot is rewritten only after
+    // barrier k, by when every wave has read it. The walk's state lives in LDS between
+    // walks, so it holds no registers across the loop.
+    __shared__ Tile desc[4];
+    __shared__ Walker walk_state;
     if (wave == 0) {
+        Walker wk;
         wk.init(p, tb, te);
         const Tile t0 = uniform(wk.next(p));
-        const Tile t1 = t0.kind == TILE_END ? t0 : uniform(wk.next(p));
+        const Tile t1 = t0.kind() == TILE_END ? t0 : uniform(wk.next(p));
+        const Tile t2 = t1.kind() == TILE_END ? t1 : uniform(wk.next(p));
         if (lane == 0) {
             desc[0] = t0;
             desc[1] = t1;
+            desc[2] = t2;
+            walk_state = wk;
         }
     }
     __syncthreads();
     Tile cur = uniform(desc[0]);
     Tile nxt = uniform(desc[1]);
+    Tile far = uniform(desc[2]);
+    // Pipeline per tile i (one barrier per tile): tile i is computed out of LDS buffer i%2
+    // while tile i+1, loaded into registers during tile i-1, is dequantized into buffer
+    // (i+1)%2; then tile i+2 is loaded into the registers.
     Prefetch pf;
-    int gbase = 0;  // first group of the current Jensen block
-    if (cur.kind != TILE_END) {
+    if (cur.kind() != TILE_END) {
         prefetch_tile<HD>(pf, p, cur, bh);
-        stage_tile<HD, BF16>(smem, pf, cur, cur.kind == TILE_PACKED ? p.segs[cur.seg].bits : 16);
+        stage_tile<HD, BF16>(smem, pf, stage_kind(cur));
     }
+    if (nxt.kind() != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
     __syncthreads();
-    int buf = 0, slot = 2;  // the ring slot of tile i + 2
-    while (cur.kind != TILE_END) {
-        // the walk first: its reads must not queue behind this tile's prefetch
-        if (wave == 0) {
-            const Tile far = nxt.kind == TILE_END ? nxt : uniform(wk.next(p));
+    int gbase = 0;  // first group of the current Jensen block
+    int buf = 0, slot = 3;  // the ring slot of tile i + 3
+    while (cur.kind() != TILE_END) {
+        if (wave == 0 && far.kind() != TILE_END) {
+            Walker wk = walk_state;
+            const Tile t3 = uniform(wk.next(p));
+            if (lane == 0) {
+                desc[slot] = t3;
+                walk_state = wk;
+            }
+        } else if (wave == 0) {
             if (lane == 0) desc[slot] = far;
         }
-        if (nxt.kind != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
+        const int sk = stage_kind(nxt);
+        const uint16_t *cbuf = smem + buf * G::BUF;
+        uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
         if (wave_ok) {
-            if (cur.kind == TILE_PACKED) {
-                if (cur.batch) {
+            if (cur.kind() == TILE_PACKED) {
+                if (cur.batch()) {
                     gbase = cur.g;
-                    beta_block<HD, BF16>(cx, p.segs[cur.seg], bh, gbase);
+                    beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, gbase);
                 }
-                if (cur.new_group) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.g - gbase);
+                if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.g - gbase);
             } else {
                 cx.beta = 0.f;
             }
-            compute_tile<HD, BF16>(cx, smem + buf * G::BUF, cur.len, p.scale_log2);
+            f32x16 s[2];
+            if (sk == STAGE_INT2) qk_stage<HD, BF16, STAGE_INT2>(cx, cbuf, nbuf, pf, s);
+            else if (sk == STAGE_INT4) qk_stage<HD, BF16, STAGE_INT4>(cx, cbuf, nbuf, pf, s);
+            else if (sk == STAGE_RAW) qk_stage<HD, BF16, STAGE_RAW>(cx, cbuf, nbuf, pf, s);
+            else qk_stage<HD, BF16, STAGE_NONE>(cx, cbuf, nbuf, pf, s);
+            softmax_pv<HD, BF16>(cx, cbuf + G::KBUF, s, cur.len, p.scale_log2);
+            if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
+        } else {
+            stage_tile<HD, BF16>(nbuf, pf, sk);
+            if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
         }
-        if (nxt.kind == TILE_END) break;
-        stage_tile<HD, BF16>(smem + (buf ^ 1) * G::BUF, pf, nxt,
-                             nxt.kind == TILE_PACKED ? p.segs[nxt.seg].bits : 16);
+        if (nxt.kind() == TILE_END) break;
         __syncthreads();
         buf ^= 1;
         cur = nxt;
-        nxt = uniform(desc[slot]);
-        slot = slot == 2 ? 0 : slot + 1;
+        nxt = far;
+        far = uniform(desc[slot]);
+        slot = (slot + 1) & 3;
     }
 
     // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]

@@ -92,33 +92,39 @@ __device__ __forceinline__ float2 codes2(uint32_t x) {
 }
 
 // Keys, INT2: word w holds the block's 16 codes (channel c at bits 2c); km[c] is the
-// {step, zero} of channel c. Output: 8 element-dtype pairs in position order.
+// {step, zero} of channel c. Step j (0..3) emits position pairs 2j, 2j+1 (channels j,
+// 4+j and 8+j, 12+j) of the 8 element-dtype pairs, position order.
+template <bool BF16>
+__device__ __forceinline__ void k2_step(uint32_t w, const uint32_t *km, int j, uint32_t (&ko)[8]) {
+    typedef Elem<BF16> E;
+    const uint32_t x = (w >> (2 * j)) & 0x03030303u;   // bytes: channels j, 4+j, 8+j, 12+j
+    const float2 a = codes2<false>(x), b = codes2<true>(x);
+    ko[2 * j] = E::pack(fma_mix(a.x, km[j]), fma_mix(a.y, km[4 + j]));
+    ko[2 * j + 1] = E::pack(fma_mix(b.x, km[8 + j]), fma_mix(b.y, km[12 + j]));
+}
 template <bool BF16>
 __device__ __forceinline__ void k2_block(uint32_t w, const uint32_t *km, uint32_t (&ko)[8]) {
-    typedef Elem<BF16> E;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t x = (w >> (2 * j)) & 0x03030303u;   // bytes: channels j, 4+j, 8+j, 12+j
-        const float2 a = codes2<false>(x), b = codes2<true>(x);
-        ko[2 * j] = E::pack(fma_mix(a.x, km[j]), fma_mix(a.y, km[4 + j]));
-        ko[2 * j + 1] = E::pack(fma_mix(b.x, km[8 + j]), fma_mix(b.y, km[12 + j]));
-    }
+    for (int j = 0; j < 4; ++j) k2_step<BF16>(w, km, j, ko);
 }
 // Keys, INT4: w0 holds channels 0..7, w1 channels 8..15 (channel c at bits 4 (c mod 8)).
+// Step jj (0..1) emits pairs 2jj, 2jj+1, 2jj+4, 2jj+5.
+template <bool BF16>
+__device__ __forceinline__ void k4_step(uint32_t w0, uint32_t w1, const uint32_t *km, int jj, uint32_t (&ko)[8]) {
+    typedef Elem<BF16> E;
+    // bytes of x0: channels jj, 2+jj, 4+jj, 6+jj; of x1: the same plus 8
+    const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
+    const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
+    const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
+    ko[2 * jj] = E::pack(fma_mix(a0.x, km[jj]), fma_mix(b0.x, km[4 + jj]));
+    ko[2 * jj + 1] = E::pack(fma_mix(a1.x, km[8 + jj]), fma_mix(b1.x, km[12 + jj]));
+    ko[2 * jj + 4] = E::pack(fma_mix(a0.y, km[2 + jj]), fma_mix(b0.y, km[6 + jj]));
+    ko[2 * jj + 5] = E::pack(fma_mix(a1.y, km[10 + jj]), fma_mix(b1.y, km[14 + jj]));
+}
 template <bool BF16>
 __device__ __forceinline__ void k4_block(uint32_t w0, uint32_t w1, const uint32_t *km, uint32_t (&ko)[8]) {
-    typedef Elem<BF16> E;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        // bytes of x0: channels jj, 2+jj, 4+jj, 6+jj; of x1: the same plus 8
-        const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
-        const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
-        const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
-        ko[2 * jj] = E::pack(fma_mix(a0.x, km[jj]), fma_mix(b0.x, km[4 + jj]));
-        ko[2 * jj + 1] = E::pack(fma_mix(a1.x, km[8 + jj]), fma_mix(b1.x, km[12 + jj]));
-        ko[2 * jj + 4] = E::pack(fma_mix(a0.y, km[2 + jj]), fma_mix(b0.y, km[6 + jj]));
-        ko[2 * jj + 5] = E::pack(fma_mix(a1.y, km[10 + jj]), fma_mix(b1.y, km[14 + jj]));
-    }
+    for (int jj = 0; jj < 2; ++jj) k4_step<BF16>(w0, w1, km, jj, ko);
 }
 
 // Values, INT2: the 4 possible dequantized values of a (token, V group) as fp16 (after
@@ -132,31 +138,35 @@ __device__ __forceinline__ void v_int2_table(uint32_t vmeta, uint32_t &tlo, uint
     thi = perm(p23, p01, 0x07050301u);
 }
 // Values, INT2: one word of 16 codes through the table; code c selects byte c of the
-// low table and byte c of the high table (selector c + 4). Output: fp16 pairs in
-// position order.
+// low table and byte c of the high table (selector c + 4). Step j emits fp16 pairs 2j,
+// 2j+1, position order.
+__device__ __forceinline__ void v_int2_step(uint32_t w, uint32_t tlo, uint32_t thi, int j, uint32_t (&vo)[8]) {
+    const uint32_t x = (w >> (2 * j)) & 0x03030303u;
+    const uint32_t x4 = x | 0x04040404u;
+    vo[2 * j] = perm(thi, tlo, perm(x4, x, 0x05010400u));
+    vo[2 * j + 1] = perm(thi, tlo, perm(x4, x, 0x07030602u));
+}
 __device__ __forceinline__ void v_int2_block(uint32_t w, uint32_t tlo, uint32_t thi, uint32_t (&vo)[8]) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-        const uint32_t x = (w >> (2 * j)) & 0x03030303u;
-        const uint32_t x4 = x | 0x04040404u;
-        vo[2 * j] = perm(thi, tlo, perm(x4, x, 0x05010400u));
-        vo[2 * j + 1] = perm(thi, tlo, perm(x4, x, 0x07030602u));
-    }
+    for (int j = 0; j < 4; ++j) v_int2_step(w, tlo, thi, j, vo);
 }
-// Values, INT4, one block with one {step, zero}: fp16 pairs in position order.
+// Values, INT4, one block with one {step, zero}: fp16 pairs in position order; step jj
+// emits pairs 2jj, 2jj+1, 2jj+4, 2jj+5.
+template <bool BF16>
+__device__ __forceinline__ void v4_step(uint32_t w0, uint32_t w1, uint32_t vm, int jj, uint32_t (&vo)[8]) {
+    typedef Elem<BF16> E;
+    const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
+    const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
+    const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
+    vo[2 * jj] = E::pack_v(fma_mix(a0.x, vm), fma_mix(b0.x, vm));
+    vo[2 * jj + 1] = E::pack_v(fma_mix(a1.x, vm), fma_mix(b1.x, vm));
+    vo[2 * jj + 4] = E::pack_v(fma_mix(a0.y, vm), fma_mix(b0.y, vm));
+    vo[2 * jj + 5] = E::pack_v(fma_mix(a1.y, vm), fma_mix(b1.y, vm));
+}
 template <bool BF16>
 __device__ __forceinline__ void v4_block(uint32_t w0, uint32_t w1, uint32_t vm, uint32_t (&vo)[8]) {
-    typedef Elem<BF16> E;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const uint32_t x0 = (w0 >> (4 * jj)) & 0x0f0f0f0fu, x1 = (w1 >> (4 * jj)) & 0x0f0f0f0fu;
-        const float2 a0 = codes2<false>(x0), b0 = codes2<true>(x0);
-        const float2 a1 = codes2<false>(x1), b1 = codes2<true>(x1);
-        vo[2 * jj] = E::pack_v(fma_mix(a0.x, vm), fma_mix(b0.x, vm));
-        vo[2 * jj + 1] = E::pack_v(fma_mix(a1.x, vm), fma_mix(b1.x, vm));
-        vo[2 * jj + 4] = E::pack_v(fma_mix(a0.y, vm), fma_mix(b0.y, vm));
-        vo[2 * jj + 5] = E::pack_v(fma_mix(a1.y, vm), fma_mix(b1.y, vm));
-    }
+    for (int jj = 0; jj < 2; ++jj) v4_step<BF16>(w0, w1, vm, jj, vo);
 }
 
 }  // namespace kvq
