@@ -66,9 +66,9 @@ template <int HD> struct Geo {
 // ---------------------------------------------------------------- tile walk
 enum : int { TILE_END = 0, TILE_PACKED = 1, TILE_RAW = 2, TILE_CUR = 3 };
 
-// A tile descriptor in four words: kind, segment, flags and bit-width in one.
+// A tile descriptor in four words: kind, segment, flags, Jensen row and bit-width in one.
 struct Tile {
-    int info;        // kind | segment << 4 | new_group << 8 | batch << 9 | bits << 10
+    int info;        // kind | segment << 4 | new_group << 8 | batch << 9 | jrow << 10 | bits << 16
     int g, t, len;   // K-group, first token (segment-relative), tokens
     __device__ __forceinline__ int kind() const { return info & 15; }
     __device__ __forceinline__ int seg() const { return (info >> 4) & 15; }
@@ -76,11 +76,14 @@ struct Tile {
     __device__ __forceinline__ bool new_group() const { return (info >> 8) & 1; }
     // a new block of 32 Jensen terms starts at group g
     __device__ __forceinline__ bool batch() const { return (info >> 9) & 1; }
+    // row of group g in its block of 32 Jensen terms
+    __device__ __forceinline__ int jrow() const { return (info >> 10) & 31; }
     // the segment's bit-width (16: raw elements)
-    __device__ __forceinline__ int bits() const { return info >> 10; }
-    static __device__ __forceinline__ Tile make(int kind, int seg, int g, int t, int len, int new_group, int batch,
+    __device__ __forceinline__ int bits() const { return info >> 16; }
+    static __device__ __forceinline__ Tile make(int kind, int seg, int g, int t, int len, int new_group, int jrow,
                                                 int bits) {
-        return Tile{kind | seg << 4 | new_group << 8 | batch << 9 | bits << 10, g, t, len};
+        return Tile{kind | seg << 4 | new_group << 8 | (new_group && jrow == 0) << 9 | jrow << 10 | bits << 16, g,
+                    t, len};
     }
 };
 
@@ -198,7 +201,7 @@ struct Walker {
             }
             const int len = min(TT, min(ge, e) - t);
             const int ng = g != last_g;
-            const Tile r = Tile::make(TILE_PACKED, si, g, t, len, ng, ng && ((g - gfirst) % 32 == 0), sbits);
+            const Tile r = Tile::make(TILE_PACKED, si, g, t, len, ng, (g - gfirst) % 32, sbits);
             last_g = g;
             t += len;
             if (t >= ge) {
@@ -739,7 +742,6 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     }
     if (nxt.kind() != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
     __syncthreads();
-    int gbase = 0;  // first group of the current Jensen block
     int buf = 0, slot = 3;  // the ring slot of tile i + 3
     while (cur.kind() != TILE_END) {
         if (wave == 0 && far.kind() != TILE_END) {
@@ -757,11 +759,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
         if (wave_ok) {
             if (cur.kind() == TILE_PACKED) {
-                if (cur.batch()) {
-                    gbase = cur.g;
-                    beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, gbase);
-                }
-                if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.g - gbase);
+                if (cur.batch()) beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g);
+                if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.jrow());
             } else {
                 cx.beta = 0.f;
             }
