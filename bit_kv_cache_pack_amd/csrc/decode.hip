@@ -160,6 +160,10 @@ __device__ __forceinline__ void set_word(u32x4 (&a)[N], int w, uint32_t v) {
     else a[w >> 2].w = v;
 }
 
+// The next step's loads are unconditional, from rows clamped into the step (a token past
+// it repeats the last one: its keys' scores are masked and its values are zeroed in LDS):
+// a load under a per-lane condition would have to land before its registers are merged
+// with the old contents, which turns every prefetch into a wait for memory.
 template <int HD>
 __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step &st, size_t bh) {
     const int r16 = threadIdx.x % 16, j = (threadIdx.x % kWave) / 16;
@@ -170,30 +174,26 @@ __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step 
         constexpr int WPR = HD / 16, WL = WPR / 4;   // words per row, per quarter
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            if (16 * b + r16 < st.len) {
-                const uint32_t *src = kc + (row0 + 16 * b + r16) * WPR + j * WL;
-                if (WL == 2) {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
-                    set_word(d.k, 2 * b, w.x);
-                    set_word(d.k, 2 * b + 1, w.y);
-                } else {
-                    set_word(d.k, b, *src);
-                }
+            const uint32_t *src = kc + (row0 + min(16 * b + r16, st.len - 1)) * WPR + j * WL;
+            if (WL == 2) {
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
+                set_word(d.k, 2 * b, w.x);
+                set_word(d.k, 2 * b + 1, w.y);
+            } else {
+                set_word(d.k, b, *src);
             }
         }
     } else {
         constexpr int WPR = HD / 8, WL = WPR / 4;
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            if (16 * b + r16 < st.len) {
-                const uint32_t *src = kc + (row0 + 16 * b + r16) * WPR + j * WL;
-                if (WL == 4) {
-                    d.k[b] = *reinterpret_cast<const u32x4 *>(src);
-                } else {
-                    const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
-                    set_word(d.k, 2 * b, w.x);
-                    set_word(d.k, 2 * b + 1, w.y);
-                }
+            const uint32_t *src = kc + (row0 + min(16 * b + r16, st.len - 1)) * WPR + j * WL;
+            if (WL == 4) {
+                d.k[b] = *reinterpret_cast<const u32x4 *>(src);
+            } else {
+                const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
+                set_word(d.k, 2 * b, w.x);
+                set_word(d.k, 2 * b + 1, w.y);
             }
         }
     }
@@ -207,34 +207,31 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
     const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
     if (sg.bits == 2) {
         constexpr int WPR = HD / 16;
-        if (lane < st.len) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + lane) * WPR);
+        const int tok = min(lane, st.len - 1);
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR);
 #pragma unroll
-            for (int i = 0; i < WPR / 4; ++i) d.v[i] = src[i];
-            const uint32_t *vm = sg.v_meta + (row0 + lane) * (HD / 32);
-            if (HD == 128) {
-                d.vm = *reinterpret_cast<const u32x4 *>(vm);
-            } else {
-                const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
-                d.vm.x = m.x;
-                d.vm.y = m.y;
-            }
+        for (int i = 0; i < WPR / 4; ++i) d.v[i] = src[i];
+        const uint32_t *vm = sg.v_meta + (row0 + tok) * (HD / 32);
+        if (HD == 128) {
+            d.vm = *reinterpret_cast<const u32x4 *>(vm);
+        } else {
+            const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
+            d.vm.x = m.x;
+            d.vm.y = m.y;
         }
     } else {
         constexpr int WPR = HD / 8, HW = WPR / 2;  // words per row, per half row
-        const int tok = lane / 2, half = lane % 2;
-        if (tok < st.len) {
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR + half * HW);
+        const int tok = min(lane / 2, st.len - 1), half = lane % 2;
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR + half * HW);
 #pragma unroll
-            for (int i = 0; i < HW / 4; ++i) d.v[i] = src[i];
-            const uint32_t *vm = sg.v_meta + (row0 + tok) * (HD / 32) + half * (HD / 64);
-            if (HD == 128) {
-                const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
-                d.vm.x = m.x;
-                d.vm.y = m.y;
-            } else {
-                d.vm.x = *vm;
-            }
+        for (int i = 0; i < HW / 4; ++i) d.v[i] = src[i];
+        const uint32_t *vm = sg.v_meta + (row0 + tok) * (HD / 32) + half * (HD / 64);
+        if (HD == 128) {
+            const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
+            d.vm.x = m.x;
+            d.vm.y = m.y;
+        } else {
+            d.vm.x = *vm;
         }
     }
 }
