@@ -240,24 +240,31 @@ template <int HD, bool BF16> struct DCtx {
     typedef typename Elem<BF16>::vec vec;
     vec qb[DGeo<HD>::KS];              // B operand: Q^T, quarter L/16 of row L%16, position order
     f32x4 o[DGeo<HD>::DB];             // O^T: positions 16 db + 4 (L/16) + i, row L%16
-    uint32_t km[16 * DGeo<HD>::NBL];   // {step, zero} of the quarter's channels, channel order
+    u32x4 km[4 * DGeo<HD>::NBL];       // {step, zero} of the quarter's channels, channel order
+                                       // (kept as the 16-byte words they are loaded in)
     float m, l, beta;
 };
 
 template <int HD>
-__device__ __forceinline__ void load_kmeta(uint32_t (&km)[16 * DGeo<HD>::NBL], const AttnParams &p, const Step &st,
+__device__ __forceinline__ void load_kmeta(u32x4 (&km)[4 * DGeo<HD>::NBL], const AttnParams &p, const Step &st,
                                            size_t bh) {
     const int j = (threadIdx.x % kWave) / 16;
     const SegmentView &sg = p.segs[st.seg];
     const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + st.g) * HD +
                                                        j * (HD / 4));
 #pragma unroll
-    for (int i = 0; i < 4 * DGeo<HD>::NBL; ++i) {
-        const u32x4 w = src[i];
-        km[4 * i] = w.x;
-        km[4 * i + 1] = w.y;
-        km[4 * i + 2] = w.z;
-        km[4 * i + 3] = w.w;
+    for (int i = 0; i < 4 * DGeo<HD>::NBL; ++i) km[i] = src[i];
+}
+
+// the {step, zero}s of 16-channel block bl of the quarter, channel order
+template <int HD>
+__device__ __forceinline__ void kmeta_block(const u32x4 (&km)[4 * DGeo<HD>::NBL], int bl, uint32_t (&o)[16]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        o[4 * i] = km[4 * bl + i].x;
+        o[4 * i + 1] = km[4 * bl + i].y;
+        o[4 * i + 2] = km[4 * bl + i].z;
+        o[4 * i + 3] = km[4 * bl + i].w;
     }
 }
 
@@ -274,7 +281,7 @@ __device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx) {
             const int pos = 8 * (ks & 1) + i;                // position inside block ks / 2
             const int ch = 16 * (ks >> 1) + swap_pos(pos);   // channel inside the quarter
             const uint32_t qbits = (qw[i / 2] >> (16 * (i % 2))) & 0xffffu;
-            const float t = mul_step(Elem<BF16>::val(qbits), cx.km[ch]);
+            const float t = mul_step(Elem<BF16>::val(qbits), cx.km[ch / 4][ch % 4]);
             acc = __builtin_fmaf(t, t, acc);
         }
     }
@@ -310,8 +317,9 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             if (b < nblk) {
 #pragma unroll
                 for (int bl = 0; bl < G::NBL; ++bl) {
-                    uint32_t ko[8];
-                    k2_block<BF16>(word_of(d.k, G::NBL * b + bl), &cx.km[16 * bl], ko);
+                    uint32_t ko[8], kmb[16];
+                    kmeta_block<HD>(cx.km, bl, kmb);
+                    k2_block<BF16>(word_of(d.k, G::NBL * b + bl), kmb, ko);
                     s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
                     s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
                 }
@@ -323,9 +331,10 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             if (b < nblk) {
 #pragma unroll
                 for (int bl = 0; bl < G::NBL; ++bl) {
-                    uint32_t ko[8];
+                    uint32_t ko[8], kmb[16];
+                    kmeta_block<HD>(cx.km, bl, kmb);
                     k4_block<BF16>(word_of(d.k, 2 * G::NBL * b + 2 * bl), word_of(d.k, 2 * G::NBL * b + 2 * bl + 1),
-                                   &cx.km[16 * bl], ko);
+                                   kmb, ko);
                     s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
                     s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
                 }
@@ -546,7 +555,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < G::DB; ++db) cx.o[db] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 16 * G::NBL; ++i) cx.km[i] = 0u;
+    for (int i = 0; i < 4 * G::NBL; ++i) cx.km[i] = u32x4{0u, 0u, 0u, 0u};
     cx.m = -__builtin_inff();
     cx.l = 0.f;
     cx.beta = 0.f;
