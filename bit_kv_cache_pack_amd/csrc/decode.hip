@@ -307,37 +307,35 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     if (!packed) cx.beta = 0.f;
 
     // ---- S^T = K^ Q^T: s[b][i] = logit of token 16 b + 4 j + i for row r16
+    // every block of the step, also past its end: those rows repeat the last token (the loads
+    // are clamped) and their scores are masked; straight-line code schedules better than
+    // blocks split by branches on the step length
     f32x4 s[4];
-    const int nblk = (len + 15) / 16;
 #pragma unroll
     for (int b = 0; b < 4; ++b) s[b] = f32x4{0.f, 0.f, 0.f, 0.f};
     if (bits == 2) {
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            if (b < nblk) {
 #pragma unroll
-                for (int bl = 0; bl < G::NBL; ++bl) {
-                    uint32_t ko[8], kmb[16];
-                    kmeta_block<HD>(cx.km, bl, kmb);
-                    k2_block<BF16>(word_of(d.k, G::NBL * b + bl), kmb, ko);
-                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
-                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
-                }
+            for (int bl = 0; bl < G::NBL; ++bl) {
+                uint32_t ko[8], kmb[16];
+                kmeta_block<HD>(cx.km, bl, kmb);
+                k2_block<BF16>(word_of(d.k, G::NBL * b + bl), kmb, ko);
+                s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
+                s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
             }
         }
     } else if (bits == 4) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
-            if (b < nblk) {
 #pragma unroll
-                for (int bl = 0; bl < G::NBL; ++bl) {
-                    uint32_t ko[8], kmb[16];
-                    kmeta_block<HD>(cx.km, bl, kmb);
-                    k4_block<BF16>(word_of(d.k, 2 * G::NBL * b + 2 * bl), word_of(d.k, 2 * G::NBL * b + 2 * bl + 1),
-                                   kmb, ko);
-                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
-                    s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
-                }
+            for (int bl = 0; bl < G::NBL; ++bl) {
+                uint32_t ko[8], kmb[16];
+                kmeta_block<HD>(cx.km, bl, kmb);
+                k4_block<BF16>(word_of(d.k, 2 * G::NBL * b + 2 * bl), word_of(d.k, 2 * G::NBL * b + 2 * bl + 1),
+                               kmb, ko);
+                s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[0], ko[1], ko[2], ko[3]}), cx.qb[2 * bl], s[b]);
+                s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
             }
         }
     } else {
@@ -373,9 +371,9 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
         load_k<HD>(d, p, nx, bh);
     }
 
-    // ---- values -> LDS (row = token, position order), zero past the step
+    // ---- values -> LDS (row = token, position order); rows past the step repeat its last
+    // token (finite, and multiplied by p = 0)
     if (bits == 2) {
-        const bool mask = len < TP;
         uint16_t *row = vt + lane * G::VROW;
 #pragma unroll
         for (int gv = 0; gv < HD / 32; ++gv) {
@@ -386,24 +384,17 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
                 const int blk = 2 * gv + bb;
                 uint32_t vo[8];
                 v_int2_block(word_of(d.v, blk), tlo, thi, vo);
-                if (mask) {
-#pragma unroll
-                    for (int q = 0; q < 8; ++q) vo[q] = lane < len ? vo[q] : 0u;
-                }
                 *reinterpret_cast<u32x4 *>(row + 16 * blk) = u32x4{vo[0], vo[1], vo[2], vo[3]};
                 *reinterpret_cast<u32x4 *>(row + 16 * blk + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
             }
         }
     } else if (bits == 4) {
         const int tok = lane / 2, half = lane % 2;
-        const bool ok = tok < len;
         uint16_t *row = vt + tok * G::VROW + half * (HD / 2);
 #pragma unroll
         for (int hb = 0; hb < HD / 32; ++hb) {
             uint32_t vo[8];
             v4_block<BF16>(word_of(d.v, 2 * hb), word_of(d.v, 2 * hb + 1), d.vm[hb / 2], vo);
-#pragma unroll
-            for (int q = 0; q < 8; ++q) vo[q] = ok ? vo[q] : 0u;
             *reinterpret_cast<u32x4 *>(row + 16 * hb) = u32x4{vo[0], vo[1], vo[2], vo[3]};
             *reinterpret_cast<u32x4 *>(row + 16 * hb + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
         }
@@ -468,21 +459,18 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
         for (int db = 0; db < G::DB; ++db) cx.o[db] *= alpha;
     }
     const float off = -(cx.beta + cx.m);
-    const int nh = (len + 31) / 32;
     f16x8 pf[2];
     float ps = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        if (h < nh) {
 #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                f16x2 pr;
-                pr.x = (_Float16)exp2_fast(__builtin_fmaf(s[2 * h + i / 4][i % 4], p.scale_log2, off));
-                pr.y = (_Float16)exp2_fast(__builtin_fmaf(s[2 * h + i / 4][i % 4 + 1], p.scale_log2, off));
-                pf[h][i] = pr.x;
-                pf[h][i + 1] = pr.y;
-                ps = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
-            }
+        for (int i = 0; i < 8; i += 2) {
+            f16x2 pr;
+            pr.x = (_Float16)exp2_fast(__builtin_fmaf(s[2 * h + i / 4][i % 4], p.scale_log2, off));
+            pr.y = (_Float16)exp2_fast(__builtin_fmaf(s[2 * h + i / 4][i % 4 + 1], p.scale_log2, off));
+            pf[h][i] = pr.x;
+            pf[h][i + 1] = pr.y;
+            ps = __builtin_amdgcn_fdot2(pr, f16x2{(_Float16)1.0f, (_Float16)1.0f}, ps, false);
         }
     }
     cx.l += ps;
@@ -496,19 +484,17 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     const int l16 = lane % 16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        if (h < nh) {
-            const int tok0 = 32 * h + 4 * j + l16 / 4;
+        const int tok0 = 32 * h + 4 * j + l16 / 4;
 #pragma unroll
-            for (int db = 0; db < G::DB; ++db) {
-                const uint16_t *p0 = vt + tok0 * G::VROW + 16 * db + 4 * (l16 % 4);
-                const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(p0));
-                const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                    (__attribute__((address_space(3))) s16x4 *)(p0 + 16 * G::VROW));
-                const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
-                const f16x8 a = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
-                cx.o[db] = mfma16_f16(a, pf[h], cx.o[db]);
-            }
+        for (int db = 0; db < G::DB; ++db) {
+            const uint16_t *p0 = vt + tok0 * G::VROW + 16 * db + 4 * (l16 % 4);
+            const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(p0));
+            const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (__attribute__((address_space(3))) s16x4 *)(p0 + 16 * G::VROW));
+            const u32x2 lo2 = __builtin_bit_cast(u32x2, lo4), hi2 = __builtin_bit_cast(u32x2, hi4);
+            const f16x8 a = __builtin_bit_cast(f16x8, u32x4{lo2.x, lo2.y, hi2.x, hi2.y});
+            cx.o[db] = mfma16_f16(a, pf[h], cx.o[db]);
         }
     }
 }
