@@ -63,6 +63,7 @@ enum : int { ST_END = 0, ST_PACKED = 1, ST_RAW = 2, ST_CUR = 3 };
 struct Step {
     int kind, seg, g, t, len;
     int new_group;  // first step of K-group g in this walk
+    int bits;       // the segment's bit-width (16: raw)
 };
 
 __device__ __forceinline__ Step uniform(Step s) {
@@ -72,65 +73,90 @@ __device__ __forceinline__ Step uniform(Step s) {
     s.t = __builtin_amdgcn_readfirstlane(s.t);
     s.len = __builtin_amdgcn_readfirstlane(s.len);
     s.new_group = __builtin_amdgcn_readfirstlane(s.new_group);
+    s.bits = __builtin_amdgcn_readfirstlane(s.bits);
     return s;
 }
 
 // Walks the segments, then the current chunk, over the token range [tb, te), in steps
-// that never cross a K-group. Uniform across the wave.
+// that never cross a K-group. Uniform across the wave. A segment's fields are read once,
+// when the walk enters it, and the end of the group after next is read a group ahead, so
+// a step inside a group costs a few scalar instructions.
 struct Walker {
     int si, t, e, g, last_g, inited;
-    __device__ __forceinline__ void init() { si = 0; inited = 0; last_g = -1; t = e = g = 0; }
+    int sbits, sng, sn;   // the current segment's bit-width, K-groups, tokens
+    int ge, gen;          // end token of group g and of group g + 1
+    const int32_t *tab;   // its K-group table
+    __device__ __forceinline__ void init() {
+        si = 0; inited = 0; last_g = -1; t = e = g = 0;
+        sbits = 16; sng = sn = ge = gen = 0; tab = nullptr;
+    }
+    // end token of group gg, clamped: a corrupt table must not send reads outside the segment
+    __device__ __forceinline__ int group_end(int gg) const {
+        return gg < sng ? min(max(group_start(tab, gg + 1), 0), sn) : sn;
+    }
     __device__ Step next(const AttnParams &p, int tb, int te) {
         while (true) {
-            if (si > p.n_segs) return Step{ST_END, 0, 0, 0, 0, 0};
+            if (si > p.n_segs) return Step{ST_END, 0, 0, 0, 0, 0, 16};
             if (!inited) {
                 int a;
                 if (si == p.n_segs) {
                     const int cb = p.n_total - p.n_cur;
                     a = max(tb, cb) - cb;
                     e = min(te, p.n_total) - cb;
+                    sbits = 16;
                 } else {
                     const SegmentView &sg = p.segs[si];
                     a = max(tb, sg.token_begin) - sg.token_begin;
                     e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
+                    sbits = sg.bits;
+                    sng = sg.n_kgroups;
+                    sn = sg.n_tokens;
+                    tab = sg.kgroup_start;
                 }
                 if (a >= e) { ++si; continue; }
                 t = a;
                 inited = 1;
-                if (si < p.n_segs && p.segs[si].bits != 16) {
-                    const SegmentView &sg = p.segs[si];
-                    int lo = 0, hi = sg.n_kgroups - 1;
+                if (si < p.n_segs && sbits != 16) {
+                    int lo = 0, hi = sng - 1;
                     while (lo < hi) {
                         const int mid = (lo + hi) >> 1;
-                        if (group_start(sg.kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
+                        if (group_start(tab, mid + 1) <= a) lo = mid + 1; else hi = mid;
                     }
                     g = lo;
                     last_g = -1;
+                    ge = group_end(g);
+                    gen = group_end(g + 1);
                 }
             }
             if (t >= e) { ++si; inited = 0; continue; }
             if (si == p.n_segs) {
                 const int len = min(TR, e - t);
-                Step r{ST_CUR, si, 0, t, len, 0};
+                const Step r{ST_CUR, si, 0, t, len, 0, 16};
                 t += len;
                 return r;
             }
-            const SegmentView &sg = p.segs[si];
-            if (sg.bits == 16) {
+            if (sbits == 16) {
                 const int len = min(TR, e - t);
-                Step r{ST_RAW, si, 0, t, len, 0};
+                const Step r{ST_RAW, si, 0, t, len, 0, 16};
                 t += len;
                 return r;
             }
-            if (g >= sg.n_kgroups) { t = e; continue; }
-            // clamped: a corrupt table must not send reads outside the segment
-            const int ge = min(max(group_start(sg.kgroup_start, g + 1), 0), sg.n_tokens);
-            if (ge <= t) { ++g; continue; }
-            const int len = min(sg.bits == 4 ? TP / 2 : TP, min(ge, e) - t);
-            Step r{ST_PACKED, si, g, t, len, g != last_g};
+            if (g >= sng) { t = e; continue; }
+            if (ge <= t) {
+                ++g;
+                ge = gen;
+                gen = group_end(g + 1);
+                continue;
+            }
+            const int len = min(sbits == 4 ? TP / 2 : TP, min(ge, e) - t);
+            const Step r{ST_PACKED, si, g, t, len, g != last_g, sbits};
             last_g = g;
             t += len;
-            if (t >= ge) ++g;
+            if (t >= ge) {
+                ++g;
+                ge = gen;
+                gen = group_end(g + 1);
+            }
             return r;
         }
     }
@@ -170,7 +196,7 @@ __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step 
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k);
-    if (sg.bits == 2) {
+    if (st.bits == 2) {
         constexpr int WPR = HD / 16, WL = WPR / 4;   // words per row, per quarter
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -205,7 +231,7 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
-    if (sg.bits == 2) {
+    if (st.bits == 2) {
         constexpr int WPR = HD / 16;
         const int tok = min(lane, st.len - 1);
         const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR);
@@ -299,7 +325,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     typedef __attribute__((ext_vector_type(4))) short s16x4;
     const int lane = threadIdx.x % kWave, r16 = lane % 16, j = lane / 16;
     const bool packed = st.kind == ST_PACKED;
-    const int bits = packed ? p.segs[st.seg].bits : 16;
+    const int bits = st.bits;
     const int len = st.len;
     const bool nx_packed = nx.kind == ST_PACKED;
 
