@@ -199,6 +199,31 @@ def cpu_baseline(step: ChunkStep, target_s: float = 15.0):
             "est_step_s": round(t_step, 2)}
 
 
+def probe_hbm(mib=2048, reps=5):
+    """Measured HBM bandwidth of this device, for context beside the published peak: a sum
+    over a 2 GiB buffer (reads) and a copy of 1 GiB (reads + writes), best of a few runs,
+    timed with events on the current stream. Buffers exceed the last-level cache."""
+    n = (mib << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device="cuda")
+    y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    best_read = best_copy = float("inf")
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record()
+        x.sum()
+        e[1].record()
+        y.copy_(x[: n // 2])
+        e[2].record()
+        torch.cuda.synchronize()
+        best_read = min(best_read, e[0].elapsed_time(e[1]))
+        best_copy = min(best_copy, e[1].elapsed_time(e[2]))
+    read_gbps = (n * 4) / (best_read * 1e-3) / 1e9
+    copy_gbps = (n // 2 * 4 * 2) / (best_copy * 1e-3) / 1e9
+    del x, y
+    return {"read_gbps": round(read_gbps, 1), "copy_gbps": round(copy_gbps, 1), "buffer_mib": mib,
+            "note": "torch sum (read) and copy (read + write), best of %d" % reps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -278,6 +303,7 @@ def main():
         "append": {"ms": round(app_avg, 4), "bytes": step.append_bytes(),
                    "gbps": round(step.append_bytes() / (app_avg * 1e-3) / 1e9, 1) if step.append else None},
     }
+    res["probe_hbm"] = probe_hbm()
     if args.probe_copy_mib:
         n = args.probe_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
