@@ -172,9 +172,10 @@ kvq_status kvq_attention_workspace_size(const kvq_attn_args *a, size_t *bytes) {
     long long n_total = 0;
     kvq_status st = check_attention_shape(a, &n_total);
     if (st != KVQ_OK) return st;
-    int ns, stoks;
-    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, use_decode(a), &ns,
-                        &stoks, bytes);
+    kvq::AttnPlan plan;
+    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, use_decode(a),
+                        &plan);
+    *bytes = plan.workspace_bytes;
     return KVQ_OK;
 }
 
@@ -187,11 +188,10 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
         return KVQ_ERR_ARG;
     for (int i = 0; i < a->n_segs; ++i)
         if (a->segs[i].n_tokens > 0 && (st = check_segment_ptrs(a->segs[i])) != KVQ_OK) return st;
-    int ns = 1, stoks = 0;
-    size_t need = 0;
     const bool decode = use_decode(a);
-    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, decode, &ns,
-                        &stoks, &need);
+    kvq::AttnPlan plan;
+    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, decode, &plan);
+    const size_t need = plan.workspace_bytes;
     if (need > 0 && (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace)))
         return KVQ_ERR_WORKSPACE;
 
@@ -236,8 +236,12 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
     p.out = a->out;
     p.out_dtype = a->out_dtype;
     p.lse = a->lse;
-    p.n_split = ns;
-    p.split_tokens = stoks;
+    p.n_split = plan.n_split;
+    p.split_tokens = plan.split_tokens;
+    p.n_rb = plan.n_rb;
+    p.tok_pad = plan.tok_pad;
+    p.quota = plan.quota;
+    p.work = plan.work;
     p.partial = reinterpret_cast<float *>(a->workspace);
     p.decode = decode ? 1 : 0;
     return kvq::launch_attention(p, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;

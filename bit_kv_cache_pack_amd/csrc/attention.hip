@@ -665,12 +665,32 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: wave_ok branches on scalars
     const int r32 = lane % 32, hh = lane / 32;
-    const int b = blockIdx.y / p.n_kv_heads, h = blockIdx.y % p.n_kv_heads;
     const int gqa = p.n_q_heads / p.n_kv_heads;
     const int rows = gqa * p.n_q;
-    const int row = blockIdx.x * BM + wave * 32 + r32;
+    __shared__ Tile desc[4];
+    __shared__ Walker walk_state;
+
+    // The workgroup's share of the work space: row block rb owns positions
+    // [rb tok_pad, (rb + 1) tok_pad), position t of it standing for token t. A share is
+    // cut into pieces at row-block ends; a piece that is a whole row block writes the
+    // output, any other one of the two partial slots of its workgroup (0: the share's
+    // first piece, 1: its last).
+    const int64_t u0 = (int64_t)blockIdx.x * p.quota;
+    const int64_t u1 = min(u0 + p.quota, p.work);
+    for (int64_t u = u0; u < u1;) {
+    const int64_t rb = u / p.tok_pad;
+    const int64_t rbeg = rb * p.tok_pad;
+    const int64_t ue = min(u1, rbeg + p.tok_pad);
+    const int tb = (int)(u - rbeg);
+    const int te = min((int)(ue - rbeg), p.n_total);
+    const bool whole = tb == 0 && ue == rbeg + p.tok_pad;
+    const int pslot = u == u0 ? 0 : 1;
+    u = ue;
+    const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
+    const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
+    const int row = rbi * BM + wave * 32 + r32;
     const bool row_ok = row < rows;
-    const bool wave_ok = blockIdx.x * BM + wave * 32 < rows;
+    const bool wave_ok = rbi * BM + wave * 32 < rows;
     const int hq = h * gqa + (row_ok ? row / p.n_q : 0);
     const int qi = row_ok ? row % p.n_q : 0;
     const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
@@ -706,15 +726,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     cx.l = 0.f;
     cx.beta = 0.f;
 
-    const int tb = blockIdx.z * p.split_tokens;
-    const int te = min(p.n_total, tb + p.split_tokens);
     // Wave 0 alone walks the tiles, three ahead, and publishes them in a 4-slot LDS ring:
     // the walk is scalar work, and a CU's scalar unit is shared by all its waves. Tile k is
     // written before barrier k - 3 and read after it; its slot is rewritten only after
     // barrier k, by when every wave has read it. The walk's state lives in LDS between
     // walks, so it holds no registers across the loop.
-    __shared__ Tile desc[4];
-    __shared__ Walker walk_state;
     if (wave == 0) {
         Walker wk;
         wk.init(p, tb, te);
@@ -786,8 +802,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 
     // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
     const float lt = cx.l + other_half(cx.l);
-    if (!row_ok) return;
-    if (p.n_split == 1) {
+    if (row_ok && whole) {
         const float inv = 1.0f / lt;
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
@@ -800,9 +815,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
                 else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_f16_bits(v);
             }
         if (p.lse != nullptr && hh == 0) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
-    } else {
-        const size_t n_rows_total = (size_t)p.batch * p.n_q_heads * p.n_q;
-        float *pp = p.partial + ((size_t)blockIdx.z * n_rows_total + qrow) * (HD + 2);
+    } else if (row_ok) {
+        float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 2);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -813,6 +827,49 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             pp[HD + 1] = lt;
         }
     }
+    // the next piece restages the LDS buffers and the walk ring
+    if (u < u1) __syncthreads();
+    }
+}
+
+// Merge the pieces of the row blocks that the shares split. Job y (one per workgroup of
+// the attention launch) takes the row block holding position y quota if share y is the
+// first to start in it; the row block's pieces are in shares w0..w1.
+template <int HD>
+__global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
+    constexpr int RPB = 256 / HD;  // rows per block
+    const int64_t U = p.quota, Np = p.tok_pad;
+    const int64_t y = blockIdx.x;
+    const int64_t rb = y * U / Np;
+    if ((rb * Np + U - 1) / U != y) return;
+    const int64_t w0 = rb * Np / U, w1 = ((rb + 1) * Np - 1) / U;
+    if (w1 == w0) return;
+    const int r = blockIdx.y * RPB + threadIdx.x / HD, c = threadIdx.x % HD;
+    const int gqa = p.n_q_heads / p.n_kv_heads;
+    const int rows = gqa * p.n_q;
+    const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
+    const int row = rbi * BM + r;
+    if (row >= rows) return;
+    const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
+    const size_t qrow = ((size_t)b * p.n_q_heads + h * gqa + row / p.n_q) * p.n_q + row % p.n_q;
+    // the row block's piece in share w is that share's first piece iff the share starts in it
+    auto piece = [&](int64_t w) {
+        return p.partial + (((size_t)w * 2 + (w * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 2);
+    };
+    float M = -__builtin_inff();
+    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, piece(w)[HD]);
+    float L = 0.f, acc = 0.f;
+    for (int64_t w = w0; w <= w1; ++w) {
+        const float *pp = piece(w);
+        const float wt = exp2f(pp[HD] - M);
+        L = fmaf(wt, pp[HD + 1], L);
+        acc = fmaf(wt, pp[c], acc);
+    }
+    const float v = acc / L;
+    if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + c] = v;
+    else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_bf16_bits(v);
+    else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_f16_bits(v);
+    if (c == 0 && p.lse != nullptr) p.lse[qrow] = (M + __log2f(L)) * kLn2;
 }
 
 // Merge token splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
@@ -839,12 +896,12 @@ __global__ __launch_bounds__(HD) void combine_kernel(AttnParams p) {
 
 template <int HD, bool BF16>
 hipError_t launch_t(const AttnParams &p, hipStream_t s) {
-    const int rows = (p.n_q_heads / p.n_kv_heads) * p.n_q;
-    dim3 grid((rows + BM - 1) / BM, p.batch * p.n_kv_heads, p.n_split);
-    hipLaunchKernelGGL((attention_kernel<HD, BF16>), grid, dim3(kThreads), 0, s, p);
+    const unsigned n_wg = (unsigned)((p.work + p.quota - 1) / p.quota);
+    hipLaunchKernelGGL((attention_kernel<HD, BF16>), dim3(n_wg), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
-    if (e != hipSuccess || p.n_split == 1) return e;
-    return launch_combine(p, s);
+    if (e != hipSuccess || p.quota % p.tok_pad == 0) return e;   // no row block was split
+    hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / HD)), dim3(256), 0, s, p);
+    return hipGetLastError();
 }
 
 }  // namespace
@@ -856,33 +913,61 @@ hipError_t launch_combine(const AttnParams &p, hipStream_t s) {
     return hipGetLastError();
 }
 
+// Compute units of the current device (one chunk-attention workgroup runs per CU); 256,
+// the full gfx950 part, when there is no device to ask.
+static int device_cus() {
+    static int cached[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 256;
+    }
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            n = 256;
+        }
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total, bool decode,
-                    int *n_split, int *split_tokens, size_t *workspace_bytes) {
+                    AttnPlan *plan) {
+    *plan = AttnPlan{};
+    const size_t row_bytes = (size_t)(head_dim + 2) * sizeof(float);
     if (decode) {
         int nw, wt;
         decode_plan(batch, n_kv_heads, n_total, &nw, &wt);
-        *n_split = nw;
-        *split_tokens = wt;
-        *workspace_bytes = nw > 1 ? (size_t)nw * batch * n_q_heads * n_q * (head_dim + 2) * sizeof(float) : 0;
+        plan->n_split = nw;
+        plan->split_tokens = wt;
+        plan->workspace_bytes = nw > 1 ? (size_t)nw * batch * n_q_heads * n_q * row_bytes : 0;
         return;
     }
+    // Chunk kernel: R row blocks, each against all n_total tokens, on G CUs. When whole row
+    // blocks fill the CUs' rounds to within 3 %, a workgroup takes one row block; otherwise
+    // every workgroup takes an equal share of the R x n_total work (in 64-token steps, at
+    // least 4 tiles), and row blocks cut between shares are merged afterwards.
     const long rows = (long)(n_q_heads / n_kv_heads) * n_q;
-    const long base = (rows + BM - 1) / BM * (long)batch * n_kv_heads;
-    long ns = 1;
-    if (base < 256) {
-        const long want = (512 + base - 1) / base;
-        const long cap = (n_total + 255) / 256;  // at least 256 tokens per split
-        ns = want < cap ? want : cap;
-        if (ns < 1) ns = 1;
+    const long n_rb = (rows + BM - 1) / BM;
+    const long R = n_rb * batch * n_kv_heads;
+    const long np = ((long)n_total + TT - 1) / TT * TT;
+    const long G = device_cus();
+    const long rounds = (R + G - 1) / G;
+    const int64_t work = (int64_t)R * np;
+    int64_t quota = np;
+    if ((double)R / (double)(rounds * G) < 0.97) {
+        quota = (work + G - 1) / G;
+        quota = (quota + TT - 1) / TT * TT;
+        if (quota < 4 * TT) quota = 4 * TT;
     }
-    long st = (n_total + ns - 1) / ns;
-    st = (st + TT - 1) / TT * TT;
-    if (st < TT) st = TT;
-    ns = (n_total + st - 1) / st;
-    if (ns < 1) ns = 1;
-    *n_split = (int)ns;
-    *split_tokens = (int)st;
-    *workspace_bytes = ns > 1 ? (size_t)ns * batch * n_q_heads * n_q * (head_dim + 2) * sizeof(float) : 0;
+    plan->n_split = 1;
+    plan->n_rb = (int32_t)n_rb;
+    plan->tok_pad = (int32_t)np;
+    plan->quota = quota;
+    plan->work = work;
+    if (quota % np != 0) plan->workspace_bytes = (size_t)((work + quota - 1) / quota) * 2 * BM * row_bytes;
 }
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {

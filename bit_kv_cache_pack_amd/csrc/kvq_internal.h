@@ -61,16 +61,28 @@ struct AttnParams {
     void *out;
     int32_t out_dtype;
     float *lse;
-    int32_t n_split;               // token splits (decode: workgroups per (batch, KV head));
-                                   // > 1 writes partials to the workspace
-    int32_t split_tokens;          // tokens per split (decode: per wave), multiple of 64
-    float *partial;                // [n_split][rows][head_dim + 2]
+    // decode kernel
+    int32_t n_split;               // workgroups per (batch, KV head); > 1 writes partials
+    int32_t split_tokens;          // tokens per wave, multiple of 64
+    // chunk kernel: row block rb (of n_rb per (batch, KV head)) owns work positions
+    // [rb tok_pad, (rb + 1) tok_pad); workgroup w takes [w quota, (w + 1) quota) of the
+    // work positions
+    int32_t n_rb, tok_pad;
+    int64_t quota, work;
+    float *partial;                // decode: [n_split][rows][head_dim + 2];
+                                   // chunk: [workgroup][2][row in block][head_dim + 2]
     int32_t decode;                // run the decode-shaped kernel (decided by decode_eligible)
 };
-// Number of token splits and the workspace they need (either kernel; decode selects the
-// decode-shaped one).
+struct AttnPlan {
+    int32_t n_split, split_tokens;   // decode kernel
+    int32_t n_rb, tok_pad;           // chunk kernel
+    int64_t quota, work;
+    size_t workspace_bytes;
+};
+// How either kernel divides the work (decode selects the decode-shaped one), and the
+// workspace its partials need.
 void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total, bool decode,
-                    int *n_split, int *split_tokens, size_t *workspace_bytes);
+                    AttnPlan *plan);
 hipError_t launch_attention(const AttnParams &p, hipStream_t s);
 // Log-sum-exp merge of n_split partials into the output.
 hipError_t launch_combine(const AttnParams &p, hipStream_t s);

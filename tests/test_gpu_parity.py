@@ -99,6 +99,17 @@ def test_attention_gqa_decode_splits(d):
     assert np.abs(gl - ol).max() <= TOL
 
 
+def test_attention_shares_span_row_blocks():
+    """600 row blocks (the last one ragged) over 130 tokens: more than two rounds of
+    workgroups, so every workgroup takes an equal share of about 2.3 row blocks -- a cut
+    first piece, whole row blocks, a cut last piece, and pieces that hold only the padding
+    past the last token -- and the cut row blocks are merged afterwards."""
+    go, gl, oo, ol = _attention_case(2, "bf16", 1, 4, 1, 64, appends=(100,), n_cur=30, n_q=38390, jensen=1,
+                                     seed=19)
+    assert np.abs(go - oo).max() <= TOL
+    assert np.abs(gl - ol).max() <= TOL
+
+
 def test_attention_fp16_and_only_current_chunk():
     go, gl, oo, ol = _attention_case(4, "f16", 1, 4, 4, 64, appends=(), n_cur=77, n_q=33, jensen=1, seed=13)
     assert np.abs(go - oo).max() <= TOL
