@@ -5,8 +5,9 @@
 Every translation unit is compiled with -ffp-contract=off (the quantizer and the window
 scores are bit-reproducible only without contraction; the attention kernels spell their
 fused multiply-adds explicitly) and with packed fp32 instructions disabled. The attention
-kernels are also compiled with -fno-honor-nans: their inputs are finite, so a running
-maximum needs no NaN quieting of its operands (which doubles its instruction count).
+kernels and the quantizer are also compiled with -fno-honor-nans: their inputs are taken
+to be finite, so a running minimum or maximum needs no NaN quieting of its operands
+(which doubles its instruction count).
 """
 import concurrent.futures
 import os
@@ -21,7 +22,7 @@ INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["api.hip", "quant.hip", "attention.hip", "decode.hip", "windows.hip"]
-PER_SOURCE = {"attention.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"]}
+PER_SOURCE = {"attention.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"], "quant.hip": ["-fno-honor-nans"]}
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 
 

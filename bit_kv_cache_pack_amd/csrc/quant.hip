@@ -24,21 +24,27 @@ namespace kvq {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch1 = 8;   // rows per thread in flight while the K extremes are taken
+constexpr int kBatch2 = 4;   // rows per thread in flight while codes are made
 
+// 8 consecutive source elements starting at p (16-byte aligned): load() fetches them as
+// stored, unpack() widens them to fp32.
 template <typename T> struct Src;
 template <> struct Src<float> {
-    // 8 consecutive elements starting at p (16-byte aligned for 8 floats = 32 bytes)
-    static __device__ __forceinline__ void load8(const float *p, float (&x)[8]) {
-        f32x4 a = *reinterpret_cast<const f32x4 *>(p);
-        f32x4 b = *reinterpret_cast<const f32x4 *>(p + 4);
-        x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-        x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    struct Raw { f32x4 a, b; };
+    static __device__ __forceinline__ Raw load(const float *p) {
+        return Raw{*reinterpret_cast<const f32x4 *>(p), *reinterpret_cast<const f32x4 *>(p + 4)};
+    }
+    static __device__ __forceinline__ void unpack(const Raw &r, float (&x)[8]) {
+        x[0] = r.a.x; x[1] = r.a.y; x[2] = r.a.z; x[3] = r.a.w;
+        x[4] = r.b.x; x[5] = r.b.y; x[6] = r.b.z; x[7] = r.b.w;
     }
 };
 template <> struct Src<__bf16> {
-    static __device__ __forceinline__ void load8(const __bf16 *p, float (&x)[8]) {
-        u32x4 w = *reinterpret_cast<const u32x4 *>(p);
-        uint32_t a[4] = {w.x, w.y, w.z, w.w};
+    typedef u32x4 Raw;
+    static __device__ __forceinline__ Raw load(const __bf16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
+    static __device__ __forceinline__ void unpack(const Raw &w, float (&x)[8]) {
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = __uint_as_float(a[i] << 16);
@@ -47,9 +53,10 @@ template <> struct Src<__bf16> {
     }
 };
 template <> struct Src<_Float16> {
-    static __device__ __forceinline__ void load8(const _Float16 *p, float (&x)[8]) {
-        u32x4 w = *reinterpret_cast<const u32x4 *>(p);
-        uint32_t a[4] = {w.x, w.y, w.z, w.w};
+    typedef u32x4 Raw;
+    static __device__ __forceinline__ Raw load(const _Float16 *p) { return *reinterpret_cast<const u32x4 *>(p); }
+    static __device__ __forceinline__ void unpack(const Raw &w, float (&x)[8]) {
+        const uint32_t a[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             x[2 * i] = f16_bits_to_f32(a[i] & 0xffffu);
@@ -80,7 +87,53 @@ struct Quant {
         r = fminf(fmaxf(r, 0.0f), (float)L);
         return (uint32_t)r;
     }
+    // 1 / step within 1 ulp (the hardware reciprocal; step is a normal fp32 number), 0 for
+    // a zero step (whose codes are all 0)
+    __device__ __forceinline__ float inv() const { return step == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(step); }
 };
+
+// The same code through the reciprocal, without a division per element. With r within
+// 1 ulp (2^-23 relative) of 1/step, t' = fl32(fl32(x - zero) r) is within 2^-22 |t| of
+// the IEEE quotient t = fl32(fl32(x - zero) / step) (r's error plus one rounding of the
+// product and one of t, 2^-24 each), i.e. within 2^-18 for |t| < 16, so
+// rint(t') == rint(t) unless t' lies within 2^-17 of a half-integer; such elements raise
+// `near` and the caller recomputes with the division. For |t| >= 16 both clamp to the same
+// end of [0, L] (L <= 15).
+// A zero step gives r = 0, t' = 0, code 0, as the division path does. The code comes
+// back as a float (an integer 0..L).
+__device__ __forceinline__ float fast_code(float x, float zero, float r, int L, bool &near) {
+    const float t = (x - zero) * r;
+    const float c = __builtin_rintf(t);
+    near |= __builtin_fabsf(t - c) > 0.5f - 0x1p-17f;
+    return __builtin_amdgcn_fmed3f(c, 0.0f, (float)L);
+}
+
+// Packs 8 codes at BITS bits each (code i at bit BITS i). The codes are summed as exact
+// floats, c_i 2^(BITS i) over at most 16 bits per sum, and converted once.
+template <int BITS>
+__device__ __forceinline__ uint32_t pack_codes(const float (&c)[8]) {
+    constexpr int PER = 16 / BITS;   // codes per 16-bit sum
+    uint32_t w = 0;
+#pragma unroll
+    for (int h = 0; h < 8 / PER; ++h) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < PER; ++i) acc = __builtin_fmaf(c[h * PER + i], (float)(1u << (BITS * i)), acc);
+        w |= (uint32_t)acc << (16 * h);
+    }
+    return w;
+}
+
+// value of the lane whose index differs in bit 0 (XOR1) or bit 1 (XOR2), within a quad
+__device__ __forceinline__ float quad_xor1(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float quad_xor2(float v) {
+    return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), 0x4E, 0xf, 0xf, false));
+}
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+    return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xf, 0xf, false);
+}
 
 // Source span and destination offset of appended group g. Contiguous appends cut
 // the source into k_group_tokens-long groups; gather appends take the listed spans in
@@ -137,14 +190,24 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParam
     uint32_t *vcodes = reinterpret_cast<uint32_t *>(p.v_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
 
     // ---- K: per-channel extremes over the group's tokens ----
+    // Rows are read in batches whose loads are all in flight together; a thread's rows
+    // past the group end read the group's last row again (a repeat leaves the extremes
+    // unchanged), so every load is unconditional.
+    typedef typename Src<T>::Raw Raw;
     float mn[8], mx[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) { mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-    for (int r = rp; r < len; r += RP) {
-        float x[8];
-        Src<T>::load8(ks + (size_t)r * HD, x);
+    for (int b0 = 0; b0 < len; b0 += kBatch1 * RP) {
+        Raw raw[kBatch1];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+        for (int u = 0; u < kBatch1; ++u) raw[u] = Src<T>::load(ks + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+#pragma unroll
+        for (int u = 0; u < kBatch1; ++u) {
+            float x[8];
+            Src<T>::unpack(raw[u], x);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+        }
     }
     // lanes holding the same channels differ in the bits above log2(CC)
 #pragma unroll
@@ -182,38 +245,62 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParam
     }
 
     // ---- K codes and V (per token, per 32-channel run) ----
+    float kinv[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kinv[i] = kq[i].inv();
     uint32_t *vm_base = reinterpret_cast<uint32_t *>(p.v_meta) + (bh * p.capacity + p.n_tokens + dst0) * (HD / VG);
-    for (int r = rp; r < len; r += RP) {
-        float x[8];
-        Src<T>::load8(ks + (size_t)r * HD, x);
-        uint32_t kbits = 0;
+    // Batches of rows as above, K and V loads all in flight; a thread's rows past the group
+    // end are recomputed from the last row and not stored. The four lanes of a quad hold
+    // one row (CC is a multiple of 4), so the quad exchanges below see one row's lanes.
+    for (int b0 = 0; b0 < len; b0 += kBatch2 * RP) {
+        Raw kraw[kBatch2], vraw[kBatch2];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) kbits |= kq[i].code(x[i], L) << (BITS * i);
+        for (int u = 0; u < kBatch2; ++u) {
+            const int rr = min(b0 + u * RP + rp, len - 1);
+            kraw[u] = Src<T>::load(ks + (size_t)rr * HD);
+            vraw[u] = Src<T>::load(vs + (size_t)rr * HD);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch2; ++u) {
+            const int r = b0 + u * RP + rp;
+            float x[8], y[8];
+            Src<T>::unpack(kraw[u], x);
+            Src<T>::unpack(vraw[u], y);
+            float a = y[0], z = y[0];
+#pragma unroll
+            for (int i = 1; i < 8; ++i) { a = fminf(a, y[i]); z = fmaxf(z, y[i]); }
+            // the 4 lanes of one 32-channel run are a quad (CC % 4 == 0)
+            a = fminf(a, quad_xor1(a)); z = fmaxf(z, quad_xor1(z));
+            a = fminf(a, quad_xor2(a)); z = fmaxf(z, quad_xor2(z));
+            Quant vq;
+            vq.set(a, z, L);
+            const float vinv = vq.inv();
 
-        float y[8];
-        Src<T>::load8(vs + (size_t)r * HD, y);
-        float a = y[0], z = y[0];
+            bool near = false;
+            float kc[8], vc[8];
 #pragma unroll
-        for (int i = 1; i < 8; ++i) { a = fminf(a, y[i]); z = fmaxf(z, y[i]); }
-        // the 4 lanes of one 32-channel run are tid^1, tid^2 neighbours (CC % 4 == 0)
-        a = fminf(a, __shfl_xor(a, 1)); z = fmaxf(z, __shfl_xor(z, 1));
-        a = fminf(a, __shfl_xor(a, 2)); z = fmaxf(z, __shfl_xor(z, 2));
-        Quant vq;
-        vq.set(a, z, L);
-        uint32_t vbits = 0;
+            for (int i = 0; i < 8; ++i) kc[i] = fast_code(x[i], kq[i].zero, kinv[i], L, near);
 #pragma unroll
-        for (int i = 0; i < 8; ++i) vbits |= vq.code(y[i], L) << (BITS * i);
-        if ((cc & 3) == 0) vm_base[(size_t)r * (HD / VG) + cc / 4] = vq.meta;
-
-        if (BITS == 4) {
-            kcodes[(size_t)r * WPR + cc] = kbits;
-            vcodes[(size_t)r * WPR + cc] = vbits;
-        } else {
-            // 16 channels per word: the even chunk takes its odd neighbour's half
-            uint32_t kn = __shfl_xor(kbits, 1), vn = __shfl_xor(vbits, 1);
-            if ((cc & 1) == 0) {
-                kcodes[(size_t)r * WPR + cc / 2] = kbits | (kn << 16);
-                vcodes[(size_t)r * WPR + cc / 2] = vbits | (vn << 16);
+            for (int i = 0; i < 8; ++i) vc[i] = fast_code(y[i], vq.zero, vinv, L, near);
+            uint32_t kbits = pack_codes<BITS>(kc), vbits = pack_codes<BITS>(vc);
+            if (__builtin_expect(__any(near), 0)) {
+                kbits = vbits = 0;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) kbits |= kq[i].code(x[i], L) << (BITS * i);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) vbits |= vq.code(y[i], L) << (BITS * i);
+            }
+            // 16 channels per INT2 word: the even chunk takes its odd neighbour's half
+            const uint32_t kn = quad_xor1(kbits), vn = quad_xor1(vbits);
+            if (r < len) {
+                if ((cc & 3) == 0) vm_base[(size_t)r * (HD / VG) + cc / 4] = vq.meta;
+                if (BITS == 4) {
+                    kcodes[(size_t)r * WPR + cc] = kbits;
+                    vcodes[(size_t)r * WPR + cc] = vbits;
+                } else if ((cc & 1) == 0) {
+                    kcodes[(size_t)r * WPR + cc / 2] = kbits | (kn << 16);
+                    vcodes[(size_t)r * WPR + cc / 2] = vbits | (vn << 16);
+                }
             }
         }
     }
@@ -236,8 +323,8 @@ __global__ __launch_bounds__(kThreads) void raw_append_kernel(QuantAppendParams 
     uint16_t *vd = reinterpret_cast<uint16_t *>(p.v_dst) + (bh * p.capacity + p.n_tokens + dst0) * HD + cc * 8;
     for (int r = rp; r < len; r += RP) {
         float x[8], y[8];
-        Src<T>::load8(ks + (size_t)r * HD, x);
-        Src<T>::load8(vs + (size_t)r * HD, y);
+        Src<T>::unpack(Src<T>::load(ks + (size_t)r * HD), x);
+        Src<T>::unpack(Src<T>::load(vs + (size_t)r * HD), y);
         u32x4 ko, vo;
         uint32_t kw[4], vw[4];
 #pragma unroll
