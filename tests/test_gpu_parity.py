@@ -49,6 +49,23 @@ def test_quantize_append_gather_bit_exact(bits):
     assert_segments_equal(gseg, oseg)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("d", [64, 128])
+def test_quantize_exact_ties_bit_exact(bits, d):
+    """Quotients (x - zero) / step that are exact half-integers in every K and V group:
+    multiples of step / 2 between 0 and L step, so the codes depend on round-half-to-even
+    (the quantizer's fast reciprocal path must hand these to the division)."""
+    B, H, n = 1, 2, 200
+    L = (1 << bits) - 1
+    t = torch.arange(n).view(n, 1)
+    c = torch.arange(d).view(1, d)
+    half = (t * 3 + c * 5) % (2 * L + 1)          # 0 .. 2L, both ends in every group
+    x = (half.float() * 0.25).expand(B, H, n, d).contiguous()   # step 0.5: x / step = half / 2
+    gseg, oseg = make_pair(bits, "bf16", B, H, d, capacity=n, Gk=128 if d == 128 else 32, kgroup_capacity=8)
+    append_both(gseg, oseg, x.to(torch.bfloat16), (x * 2.0).to(torch.bfloat16))
+    assert_segments_equal(gseg, oseg)
+
+
 def test_quantize_constant_and_zero_groups():
     """Degenerate groups: constant channels (step 0), signed zeros."""
     B, H, d, n = 1, 1, 64, 64
