@@ -15,9 +15,10 @@
 // each such segment is walked with its own bit-width.
 //
 // Workgroup: 8 waves, 256 query rows (32 per wave; the rows of one KV head's query heads
-// are packed, so GQA decode fills rows), one (batch, KV head), one token split. Tokens
-// are walked in 64-token tiles that never straddle a K-group. Pipeline per tile, one
-// barrier per tile:
+// are packed, so GQA decode fills rows) of one (batch, KV head). A workgroup runs a share
+// of the (row block, token) work, in pieces cut at row-block ends. A piece's tokens are
+// taken in 64-token tiles that never straddle a K-group, listed in bulk in LDS by all
+// threads. Pipeline per tile, one barrier per tile:
 //   - the packed codes / raw elements of tile i+1 are loaded into registers,
 //   - every wave computes tile i out of LDS buffer i%2: S^T = K Q^T with MFMA 32x32x16
 //     (lanes own queries, so softmax statistics and the Jensen term are per-lane
@@ -34,8 +35,8 @@
 // The Jensen terms of 32 consecutive K-groups are computed at once as a small matrix
 // product (step^2 x q^2, each split into bf16 high and low parts, three MFMAs per
 // k-step) and read back per group.
-// With several token splits, unnormalized partials go to the workspace and a combine
-// kernel merges them by log-sum-exp.
+// A row block cut between workgroups leaves unnormalized partials in the workspace, and
+// a combine kernel merges them by log-sum-exp.
 #include "kvq_internal.h"
 #include "kvq_tile.cuh"
 
@@ -63,7 +64,7 @@ template <int HD> struct Geo {
     static constexpr int UNITS = TT * NBLK;   // (token, block) units per tile, <= kThreads
 };
 
-// ---------------------------------------------------------------- tile walk
+// ---------------------------------------------------------------- tile list
 enum : int { TILE_END = 0, TILE_PACKED = 1, TILE_RAW = 2, TILE_CUR = 3 };
 
 // A tile descriptor in four words: kind, segment, flags, Jensen row and bit-width in one.
@@ -72,7 +73,7 @@ struct Tile {
     int g, t, len;   // K-group, first token (segment-relative), tokens
     __device__ __forceinline__ int kind() const { return info & 15; }
     __device__ __forceinline__ int seg() const { return (info >> 4) & 15; }
-    // first tile of K-group g in this walk
+    // first tile of K-group g in this piece
     __device__ __forceinline__ bool new_group() const { return (info >> 8) & 1; }
     // a new block of 32 Jensen terms starts at group g
     __device__ __forceinline__ bool batch() const { return (info >> 9) & 1; }
@@ -95,124 +96,145 @@ __device__ __forceinline__ Tile uniform(Tile t) {
     return t;
 }
 
-// Entry g of a K-group table through the scalar cache, for a uniform address. The kernel
-// never writes the table, but the barriers' fences keep the compiler from proving that, so
-// it would read it with a vector load: hundreds of cycles, behind every vector load in
-// flight. The load waits for itself inside the same asm statement.
-__device__ __forceinline__ int group_start_scalar(const int32_t *tab, int g) {
-    const int32_t *ptr = tab + g;
-    int v;
-    asm volatile("s_load_dword %0, %1, 0x0\n\ts_waitcnt lgkmcnt(0)" : "=s"(v) : "s"(ptr) : "memory");
-    return v;
+// The tiles of a piece are listed in bulk in LDS. A unit is a K-group of a packed segment
+// (in the piece) or TT tokens of a raw segment or of the current chunk; every thread takes
+// one unit, cuts it into tiles of at most TT tokens that never cross a K-group, and a
+// block-wide prefix sum of the tile counts places the tiles in order: segments in order,
+// then the current chunk. A list holds at most kListCap tiles; the next one is built when
+// the pipeline reaches the end of the current one.
+constexpr int kListCap = 512;
+
+struct SegInfo {
+    const int32_t *tab;   // K-group table (packed segments)
+    int bits, n, ng;      // bit-width (16: raw elements), tokens, K-groups
+    int a, e;             // tokens of the piece inside the segment, [a, e)
+    int g_lo;             // K-group of token a (packed segments)
+    int units;            // units of the segment in the piece
+};
+
+struct TileList {
+    Tile t[kListCap];
+    SegInfo seg[kMaxSegments + 1];   // the segments, then the current chunk
+    int wsum[kWaves];                // prefix-sum scratch: per-wave totals
+    int n_tiles;                     // tiles of the list just built
+};
+
+// The K-group holding token a: the largest g in [0, ng) whose start is <= a (0 if none),
+// for a sorted table. Uniform across the wave; each round reads 64 starts, one per lane,
+// and narrows the range 64-fold.
+__device__ __forceinline__ int find_group(const int32_t *tab, int ng, int a) {
+    const int lane = threadIdx.x % kWave;
+    int lo = 0, hi = ng - 1;
+    while (lo < hi) {
+        const int step = (hi - lo + kWave) / kWave;
+        const int g = lo + lane * step;
+        const bool ok = g <= hi && group_start(tab, g) <= a;
+        const unsigned long long m = __ballot(ok);
+        const int k = m ? 63 - __builtin_clzll(m) : 0;
+        lo = __builtin_amdgcn_readfirstlane(lo + k * step);
+        hi = __builtin_amdgcn_readfirstlane(min(hi, lo + step - 1));
+    }
+    return lo;
 }
 
-// Walks the segments, then the current chunk, over the token split [tb, te), in tiles
-// that never cross a K-group. Uniform across the workgroup: the walk's state, and the
-// call's scalars it compares against, are re-read as uniform on every call, since the
-// compiler may route them through joins of per-lane branches (e.g. the staging code's idle
-// threads), which it would otherwise treat as per-lane values.
-struct Walker {
-    int si, t, e, g, gfirst, last_g, inited;
-    int ns, cb, nt, tb, te;   // segments, first current-chunk token, all tokens, the split
-    int sbits, sn, sng;       // the current segment's bit-width, tokens, K-groups
-    int ge, gen;              // end token of group g, and of group g + 1 (fetched a group ahead)
-    __device__ __forceinline__ void init(const AttnParams &p, int tb_, int te_) {
-        si = 0; inited = 0; last_g = -1; t = e = g = gfirst = 0;
-        ns = p.n_segs; nt = p.n_total; cb = p.n_total - p.n_cur; tb = tb_; te = te_;
-        sbits = 16; sn = sng = ge = gen = 0;
-    }
-    __device__ __forceinline__ void make_uniform() {
-        si = __builtin_amdgcn_readfirstlane(si);
-        t = __builtin_amdgcn_readfirstlane(t);
-        e = __builtin_amdgcn_readfirstlane(e);
-        g = __builtin_amdgcn_readfirstlane(g);
-        gfirst = __builtin_amdgcn_readfirstlane(gfirst);
-        last_g = __builtin_amdgcn_readfirstlane(last_g);
-        inited = __builtin_amdgcn_readfirstlane(inited);
-        ns = __builtin_amdgcn_readfirstlane(ns);
-        cb = __builtin_amdgcn_readfirstlane(cb);
-        nt = __builtin_amdgcn_readfirstlane(nt);
-        tb = __builtin_amdgcn_readfirstlane(tb);
-        te = __builtin_amdgcn_readfirstlane(te);
-        sbits = __builtin_amdgcn_readfirstlane(sbits);
-        sn = __builtin_amdgcn_readfirstlane(sn);
-        sng = __builtin_amdgcn_readfirstlane(sng);
-        ge = __builtin_amdgcn_readfirstlane(ge);
-        gen = __builtin_amdgcn_readfirstlane(gen);
-    }
-    // end token of group gg of the current segment, clamped: a corrupt table must not send
-    // reads outside the segment
-    __device__ __forceinline__ int group_end(const AttnParams &p, int gg) const {
-        return gg < sng ? min(max(group_start_scalar(p.segs[si].kgroup_start, gg + 1), 0), sn) : sn;
-    }
-    __device__ Tile next(const AttnParams &p) {
-        make_uniform();
-        while (true) {
-            if (si > ns) return Tile::make(TILE_END, 0, 0, 0, 0, 0, 0, 16);
-            if (!inited) {
-                int a;
-                if (si == ns) {
-                    a = max(tb, cb) - cb;
-                    e = min(te, nt) - cb;
-                    sbits = 16;
-                } else {
-                    const SegmentView &sg = p.segs[si];
-                    a = max(tb, sg.token_begin) - sg.token_begin;
-                    e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
-                    sbits = sg.bits;
-                    sn = sg.n_tokens;
-                    sng = sg.n_kgroups;
-                }
-                if (a >= e) { ++si; continue; }
-                t = a;
-                inited = 1;
-                if (si < ns && sbits != 16) {
-                    int lo = 0, hi = sng - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi) >> 1;
-                        if (group_start_scalar(p.segs[si].kgroup_start, mid + 1) <= a) lo = mid + 1; else hi = mid;
-                    }
-                    g = lo;
-                    gfirst = lo;
-                    last_g = -1;
-                    ge = group_end(p, g);
-                    gen = group_end(p, g + 1);
+// Per piece [tb, te): the range and unit count of each segment, one wave per segment.
+// Ends with a barrier.
+__device__ void list_setup(const AttnParams &p, int tb, int te, TileList &L) {
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
+    for (int si = wave; si <= p.n_segs; si += kWaves) {
+        SegInfo f{nullptr, 16, 0, 0, 0, 0, 0, 0};
+        if (si == p.n_segs) {
+            const int cb = p.n_total - p.n_cur;
+            f.n = p.n_cur;
+            f.a = max(tb, cb) - cb;
+            f.e = min(te, p.n_total) - cb;
+            if (f.e > f.a) f.units = (f.e - f.a + TT - 1) / TT;
+        } else {
+            const SegmentView &sg = p.segs[si];
+            f.tab = sg.kgroup_start;
+            f.bits = sg.bits;
+            f.n = sg.n_tokens;
+            f.ng = sg.bits == 16 ? 0 : sg.n_kgroups;
+            f.a = max(tb, sg.token_begin) - sg.token_begin;
+            f.e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
+            if (f.e > f.a) {
+                if (f.bits == 16) {
+                    f.units = (f.e - f.a + TT - 1) / TT;
+                } else if (f.ng > 0) {
+                    f.g_lo = f.a == 0 ? 0 : find_group(f.tab, f.ng, f.a);
+                    const int g_hi = f.e == f.n ? f.ng - 1 : find_group(f.tab, f.ng, f.e - 1);
+                    f.units = max(g_hi - f.g_lo + 1, 0);
                 }
             }
-            if (t >= e) { ++si; inited = 0; continue; }
-            if (si == ns) {
-                const int len = min(TT, e - t);
-                const Tile r = Tile::make(TILE_CUR, si, 0, t, len, 0, 0, 16);
-                t += len;
-                return r;
+        }
+        if (lane == 0) L.seg[si] = f;
+    }
+    __syncthreads();
+}
+
+// Builds the list of the tiles of units u0, u0 + 1, ... (as many as fit) and returns how
+// many units it took; L.n_tiles is its length. All threads call it together; it begins
+// by overwriting the list (no wave may still read it) and ends with a barrier.
+__device__ int list_build(const AttnParams &p, TileList &L, int u0, int u_total) {
+    const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int u = u0 + tid;
+    int n = 0, s = 0, g = 0, t0 = 0, t1 = 0, jrow = 0, kind = TILE_END, bits = 16;
+    if (u < u_total) {
+        int base = 0, i = 0;
+        for (int si = 0; si <= p.n_segs; ++si) {
+            const int nu = L.seg[si].units;
+            if (u >= base && u < base + nu) {
+                s = si;
+                i = u - base;
             }
-            if (sbits == 16) {
-                const int len = min(TT, e - t);
-                const Tile r = Tile::make(TILE_RAW, si, 0, t, len, 0, 0, 16);
-                t += len;
-                return r;
-            }
-            if (g >= sng) { t = e; continue; }
-            if (ge <= t) {
-                ++g;
-                ge = gen;
-                gen = group_end(p, g + 1);
-                continue;
-            }
-            const int len = min(TT, min(ge, e) - t);
-            const int ng = g != last_g;
-            const Tile r = Tile::make(TILE_PACKED, si, g, t, len, ng, (g - gfirst) % 32, sbits);
-            last_g = g;
-            t += len;
-            if (t >= ge) {
-                ++g;
-                ge = gen;
-                gen = group_end(p, g + 1);
-            }
-            return r;
+            base += nu;
+        }
+        const SegInfo &f = L.seg[s];
+        if (s == p.n_segs || f.bits == 16) {
+            kind = s == p.n_segs ? TILE_CUR : TILE_RAW;
+            t0 = f.a + TT * i;
+            t1 = min(t0 + TT, f.e);
+            n = 1;
+        } else {
+            kind = TILE_PACKED;
+            bits = f.bits;
+            g = f.g_lo + i;
+            // group bounds clamped into the segment: a corrupt table must not send reads outside it
+            const int gs = i == 0 ? f.a : min(max(group_start(f.tab, g), 0), f.n);
+            const int ge = g + 1 < f.ng ? min(max(group_start(f.tab, g + 1), 0), f.n) : f.n;
+            t0 = max(gs, f.a);
+            t1 = min(ge, f.e);
+            // a valid group has at most 1024 / TT tiles; the cap keeps a corrupt table (one
+            // group over a whole segment) from stalling the build
+            n = t1 > t0 ? min((t1 - t0 + TT - 1) / TT, kListCap) : 0;
+            jrow = i % 32;
         }
     }
-};
+    // exclusive prefix sum of n over the block
+    int x = n;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+        const int y = __shfl_up(x, o);
+        if (lane >= o) x += y;
+    }
+    if (lane == kWave - 1) L.wsum[wave] = x;
+    __syncthreads();
+    int off = x - n;
+    for (int w = 0; w < wave; ++w) off += L.wsum[w];
+    // the units that fit are a prefix of the batch
+    const bool inc = u < u_total && off + n <= kListCap;
+    for (int k = 0; inc && k < n; ++k)
+        L.t[off + k] = Tile::make(kind, s, g, t0 + TT * k, min(TT, t1 - t0 - TT * k), kind == TILE_PACKED && k == 0,
+                                  jrow, bits);
+    const int taken = __syncthreads_count(inc);
+    if (taken == 0) {
+        if (tid == 0) L.n_tiles = 0;
+    } else if (tid == taken - 1) {
+        L.n_tiles = off + n;
+    }
+    __syncthreads();
+    return taken;
+}
 
 // ---------------------------------------------------------------- prefetch (global -> registers)
 // Thread tid owns the unit (token r = tid / NBLK, 16-channel block b = tid % NBLK).
@@ -667,8 +689,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     const int r32 = lane % 32, hh = lane / 32;
     const int gqa = p.n_q_heads / p.n_kv_heads;
     const int rows = gqa * p.n_q;
-    __shared__ Tile desc[4];
-    __shared__ Walker walk_state;
+    __shared__ TileList tlist;
 
     // The workgroup's share of the work space: row block rb owns positions
     // [rb tok_pad, (rb + 1) tok_pad), position t of it standing for token t. A share is
@@ -726,28 +747,25 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     cx.l = 0.f;
     cx.beta = 0.f;
 
-    // Wave 0 alone walks the tiles, three ahead, and publishes them in a 4-slot LDS ring:
-    // the walk is scalar work, and a CU's scalar unit is shared by all its waves. Tile k is
-    // written before barrier k - 3 and read after it; its slot is rewritten only after
-    // barrier k, by when every wave has read it. The walk's state lives in LDS between
-    // walks, so it holds no registers across the loop.
-    if (wave == 0) {
-        Walker wk;
-        wk.init(p, tb, te);
-        const Tile t0 = uniform(wk.next(p));
-        const Tile t1 = t0.kind() == TILE_END ? t0 : uniform(wk.next(p));
-        const Tile t2 = t1.kind() == TILE_END ? t1 : uniform(wk.next(p));
-        if (lane == 0) {
-            desc[0] = t0;
-            desc[1] = t1;
-            desc[2] = t2;
-            walk_state = wk;
+    // The piece's tiles, from lists built in bulk (all threads call fetch() together, in
+    // order of i; a new list is built only after every wave has read the tiles it needs from
+    // the old one: the ones it holds in cur, nxt and far).
+    list_setup(p, tb, te, tlist);
+    int u_total = 0;
+    for (int si = 0; si <= p.n_segs; ++si) u_total += tlist.seg[si].units;
+    u_total = __builtin_amdgcn_readfirstlane(u_total);
+    int u_next = 0, list_base = 0, list_n = 0;
+    auto fetch = [&](int i) -> Tile {
+        while (i >= list_base + list_n && u_next < u_total) {
+            list_base += list_n;
+            u_next = __builtin_amdgcn_readfirstlane(u_next + list_build(p, tlist, u_next, u_total));
+            list_n = __builtin_amdgcn_readfirstlane(tlist.n_tiles);
         }
-    }
-    __syncthreads();
-    Tile cur = uniform(desc[0]);
-    Tile nxt = uniform(desc[1]);
-    Tile far = uniform(desc[2]);
+        return i < list_base + list_n ? uniform(tlist.t[i - list_base]) : Tile::make(TILE_END, 0, 0, 0, 0, 0, 0, 16);
+    };
+    Tile cur = fetch(0);
+    Tile nxt = fetch(1);
+    Tile far = fetch(2);
     // Pipeline per tile i (one barrier per tile): tile i is computed out of LDS buffer i%2
     // while tile i+1, loaded into registers during tile i-1, is dequantized into buffer
     // (i+1)%2; then tile i+2 is loaded into the registers.
@@ -758,18 +776,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     }
     if (nxt.kind() != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
     __syncthreads();
-    int buf = 0, slot = 3;  // the ring slot of tile i + 3
+    int buf = 0, it = 0;  // cur is tile it of the piece
     while (cur.kind() != TILE_END) {
-        if (wave == 0 && far.kind() != TILE_END) {
-            Walker wk = walk_state;
-            const Tile t3 = uniform(wk.next(p));
-            if (lane == 0) {
-                desc[slot] = t3;
-                walk_state = wk;
-            }
-        } else if (wave == 0) {
-            if (lane == 0) desc[slot] = far;
-        }
         const int sk = stage_kind(nxt);
         const uint16_t *cbuf = smem + buf * G::BUF;
         uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
@@ -796,8 +804,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         buf ^= 1;
         cur = nxt;
         nxt = far;
-        far = uniform(desc[slot]);
-        slot = (slot + 1) & 3;
+        far = fetch(++it + 2);
     }
 
     // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
@@ -827,7 +834,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             pp[HD + 1] = lt;
         }
     }
-    // the next piece restages the LDS buffers and the walk ring
+    // the next piece restages the LDS buffers and rebuilds the tile list
     if (u < u1) __syncthreads();
     }
 }
