@@ -823,7 +823,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             }
         if (p.lse != nullptr && hh == 0) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
     } else if (row_ok) {
-        float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 2);
+        float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 4);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db)
 #pragma unroll
@@ -841,17 +841,20 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 
 // Merge the pieces of the row blocks that the shares split. Job y (one per workgroup of
 // the attention launch) takes the row block holding position y quota if share y is the
-// first to start in it; the row block's pieces are in shares w0..w1.
+// first to start in it; the row block's pieces are in shares w0..w1. One pass over the
+// pieces with a running maximum; a thread merges 4 channels of one row (partial rows are
+// HD + 4 floats: O, then m and l, 16-byte aligned).
 template <int HD>
 __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
-    constexpr int RPB = 256 / HD;  // rows per block
+    constexpr int TPR = HD / 4;     // threads per row
+    constexpr int RPB = 256 / TPR;  // rows per block
     const int64_t U = p.quota, Np = p.tok_pad;
     const int64_t y = blockIdx.x;
     const int64_t rb = y * U / Np;
     if ((rb * Np + U - 1) / U != y) return;
     const int64_t w0 = rb * Np / U, w1 = ((rb + 1) * Np - 1) / U;
     if (w1 == w0) return;
-    const int r = blockIdx.y * RPB + threadIdx.x / HD, c = threadIdx.x % HD;
+    const int r = blockIdx.y * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * 4;
     const int gqa = p.n_q_heads / p.n_kv_heads;
     const int rows = gqa * p.n_q;
     const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
@@ -859,23 +862,32 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     if (row >= rows) return;
     const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
     const size_t qrow = ((size_t)b * p.n_q_heads + h * gqa + row / p.n_q) * p.n_q + row % p.n_q;
-    // the row block's piece in share w is that share's first piece iff the share starts in it
-    auto piece = [&](int64_t w) {
-        return p.partial + (((size_t)w * 2 + (w * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 2);
-    };
-    float M = -__builtin_inff();
-    for (int64_t w = w0; w <= w1; ++w) M = fmaxf(M, piece(w)[HD]);
-    float L = 0.f, acc = 0.f;
+    float M = -__builtin_inff(), L = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int64_t w = w0; w <= w1; ++w) {
-        const float *pp = piece(w);
-        const float wt = exp2f(pp[HD] - M);
-        L = fmaf(wt, pp[HD + 1], L);
-        acc = fmaf(wt, pp[c], acc);
+        // the row block's piece in share w is that share's first piece iff the share starts in it
+        const float *pp = p.partial + (((size_t)w * 2 + (w * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 4);
+        const f32x4 o = *reinterpret_cast<const f32x4 *>(pp + c);
+        const float m = pp[HD], l = pp[HD + 1];
+        if (m == -__builtin_inff()) continue;   // a piece past the last token
+        const float mn = fmaxf(M, m);
+        const float sa = exp2f(M - mn), sb = exp2f(m - mn);
+        acc = acc * sa + o * sb;
+        L = L * sa + l * sb;
+        M = mn;
     }
-    const float v = acc / L;
-    if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + c] = v;
-    else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_bf16_bits(v);
-    else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_f16_bits(v);
+    const float inv = 1.0f / L;
+    const size_t o0 = qrow * HD + c;
+    if (p.out_dtype == DT_F32) {
+        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + o0) = acc * inv;
+    } else {
+        uint16_t e[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            e[i] = p.out_dtype == DT_BF16 ? f32_to_bf16_bits(acc[i] * inv) : f32_to_f16_bits(acc[i] * inv);
+        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.out) + o0) =
+            u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+    }
     if (c == 0 && p.lse != nullptr) p.lse[qrow] = (M + __log2f(L)) * kLn2;
 }
 
@@ -907,7 +919,7 @@ hipError_t launch_t(const AttnParams &p, hipStream_t s) {
     hipLaunchKernelGGL((attention_kernel<HD, BF16>), dim3(n_wg), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.quota % p.tok_pad == 0) return e;   // no row block was split
-    hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / HD)), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / (HD / 4))), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -974,7 +986,8 @@ void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int 
     plan->tok_pad = (int32_t)np;
     plan->quota = quota;
     plan->work = work;
-    if (quota % np != 0) plan->workspace_bytes = (size_t)((work + quota - 1) / quota) * 2 * BM * row_bytes;
+    if (quota % np != 0)
+        plan->workspace_bytes = (size_t)((work + quota - 1) / quota) * 2 * BM * (head_dim + 4) * sizeof(float);
 }
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {

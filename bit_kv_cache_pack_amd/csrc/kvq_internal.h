@@ -70,7 +70,7 @@ struct AttnParams {
     int32_t n_rb, tok_pad;
     int64_t quota, work;
     float *partial;                // decode: [n_split][rows][head_dim + 2];
-                                   // chunk: [workgroup][2][row in block][head_dim + 2]
+                                   // chunk: [workgroup][2][row in block][head_dim + 4]
     int32_t decode;                // run the decode-shaped kernel (decided by decode_eligible)
 };
 struct AttnPlan {

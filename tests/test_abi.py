@@ -168,10 +168,10 @@ def test_workspace_size_and_check():
     a, arr = _attn(n_q=8192, n_q_heads=16, n_kv_heads=16, segs=[_seg(n_kv_heads=16, n_tokens=900, n_kgroups=8)])
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK and n.value == 0
     # 384 row blocks would leave half of the second round idle: every workgroup takes an
-    # equal share and keeps two partial slots of 256 rows x (d + 2) floats
+    # equal share and keeps two partial slots of 256 rows x (d + 4) floats
     a, arr = _attn(n_q=8192, n_q_heads=12, n_kv_heads=12, segs=[_seg(n_kv_heads=12, n_tokens=900, n_kgroups=8)])
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK
-    assert n.value > 0 and n.value % (2 * 256 * 4 * 130) == 0 and n.value // (2 * 256 * 4 * 130) <= 256
+    assert n.value > 0 and n.value % (2 * 256 * 4 * 132) == 0 and n.value // (2 * 256 * 4 * 132) <= 256
 
 
 def test_window_validation():
