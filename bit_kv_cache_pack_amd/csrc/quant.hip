@@ -162,6 +162,66 @@ __device__ __forceinline__ void group_span(const QuantAppendParams &p, int g, in
     len = min(len, p.n_new - dst0);
 }
 
+// Codes of one row's 8 channels of V (a quad holds one 32-channel group) and their
+// store. Rows past the group end (r >= len) are clamped copies: computed, not stored.
+// Called by whole quads in uniform control flow.
+template <int HD, int BITS>
+__device__ __forceinline__ void v_row(const float (&y)[8], int r, int len, int cc, uint32_t *vcodes,
+                                      uint32_t *vm_base) {
+    constexpr int L = (1 << BITS) - 1;
+    constexpr int WPR = HD * BITS / 32;
+    constexpr int VG = 32;
+    float a = y[0], z = y[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) { a = fminf(a, y[i]); z = fmaxf(z, y[i]); }
+    a = fminf(a, quad_xor1(a)); z = fmaxf(z, quad_xor1(z));
+    a = fminf(a, quad_xor2(a)); z = fmaxf(z, quad_xor2(z));
+    Quant vq;
+    vq.set(a, z, L);
+    const float vinv = vq.inv();
+    bool near = false;
+    float vc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) vc[i] = fast_code(y[i], vq.zero, vinv, L, near);
+    uint32_t vbits = pack_codes<BITS>(vc);
+    if (__builtin_expect(__any(near), 0)) {
+        vbits = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) vbits |= vq.code(y[i], L) << (BITS * i);
+    }
+    // 16 channels per INT2 word: the even chunk takes its odd neighbour's half
+    const uint32_t vn = quad_xor1(vbits);
+    if (r < len) {
+        if ((cc & 3) == 0) vm_base[(size_t)r * (HD / VG) + cc / 4] = vq.meta;
+        if (BITS == 4) vcodes[(size_t)r * WPR + cc] = vbits;
+        else if ((cc & 1) == 0) vcodes[(size_t)r * WPR + cc / 2] = vbits | (vn << 16);
+    }
+}
+
+// Codes of one row's 8 channels of K against the group's per-channel step/zero, and
+// their store (as v_row).
+template <int HD, int BITS>
+__device__ __forceinline__ void k_row(const float (&x)[8], int r, int len, int cc, const Quant (&kq)[8],
+                                      const float (&kinv)[8], uint32_t *kcodes) {
+    constexpr int L = (1 << BITS) - 1;
+    constexpr int WPR = HD * BITS / 32;
+    bool near = false;
+    float kc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kc[i] = fast_code(x[i], kq[i].zero, kinv[i], L, near);
+    uint32_t kbits = pack_codes<BITS>(kc);
+    if (__builtin_expect(__any(near), 0)) {
+        kbits = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kbits |= kq[i].code(x[i], L) << (BITS * i);
+    }
+    const uint32_t kn = quad_xor1(kbits);
+    if (r < len) {
+        if (BITS == 4) kcodes[(size_t)r * WPR + cc] = kbits;
+        else if ((cc & 1) == 0) kcodes[(size_t)r * WPR + cc / 2] = kbits | (kn << 16);
+    }
+}
+
 template <typename T, int HD, int BITS>
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParams p) {
     constexpr int L = (1 << BITS) - 1;
@@ -169,6 +229,7 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParam
     constexpr int RP = kThreads / CC;     // rows processed per pass
     constexpr int WPR = HD * BITS / 32;   // packed words per token row
     constexpr int VG = 32;                // V-group width
+    typedef typename Src<T>::Raw Raw;
     const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x;
     const int cc = tid % CC, rp = tid / CC;
@@ -188,25 +249,58 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParam
     const T *vs = reinterpret_cast<const T *>(p.v_src) + (bh * p.src_tokens + src0) * HD + cc * 8;
     uint32_t *kcodes = reinterpret_cast<uint32_t *>(p.k_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
     uint32_t *vcodes = reinterpret_cast<uint32_t *>(p.v_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
+    uint32_t *vm_base = reinterpret_cast<uint32_t *>(p.v_meta) + (bh * p.capacity + p.n_tokens + dst0) * (HD / VG);
 
     // ---- K: per-channel extremes over the group's tokens ----
     // Rows are read in batches whose loads are all in flight together; a thread's rows
     // past the group end read the group's last row again (a repeat leaves the extremes
-    // unchanged), so every load is unconditional.
-    typedef typename Src<T>::Raw Raw;
+    // unchanged, and its codes are not stored), so every load is unconditional. With
+    // 16-bit sources and a group of at most kBatch1 rows per thread, the K rows stay in
+    // registers until their codes are made, and the first V rows (which do not depend on
+    // the K statistics) are coded while the K loads land.
+    const bool resident = sizeof(Raw) == 16 && len <= kBatch1 * RP;
     float mn[8], mx[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) { mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
-    for (int b0 = 0; b0 < len; b0 += kBatch1 * RP) {
-        Raw raw[kBatch1];
+    Raw kres[kBatch1];
+    if (resident) {
 #pragma unroll
-        for (int u = 0; u < kBatch1; ++u) raw[u] = Src<T>::load(ks + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+        for (int u = 0; u < kBatch1; ++u)
+            if (u * RP < len) kres[u] = Src<T>::load(ks + (size_t)min(u * RP + rp, len - 1) * HD);
+        Raw vraw[kBatch2];
+#pragma unroll
+        for (int u = 0; u < kBatch2; ++u)
+            if (u * RP < len) vraw[u] = Src<T>::load(vs + (size_t)min(u * RP + rp, len - 1) * HD);
+#pragma unroll
+        for (int u = 0; u < kBatch2; ++u) {
+            if (u * RP < len) {
+                float y[8];
+                Src<T>::unpack(vraw[u], y);
+                v_row<HD, BITS>(y, u * RP + rp, len, cc, vcodes, vm_base);
+            }
+        }
 #pragma unroll
         for (int u = 0; u < kBatch1; ++u) {
-            float x[8];
-            Src<T>::unpack(raw[u], x);
+            if (u * RP < len) {
+                float x[8];
+                Src<T>::unpack(kres[u], x);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+                for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+            }
+        }
+    } else {
+        for (int b0 = 0; b0 < len; b0 += kBatch1 * RP) {
+            Raw raw[kBatch1];
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u)
+                raw[u] = Src<T>::load(ks + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u) {
+                float x[8];
+                Src<T>::unpack(raw[u], x);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+            }
         }
     }
     // lanes holding the same channels differ in the bits above log2(CC)
@@ -243,64 +337,49 @@ __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParam
         *reinterpret_cast<u32x4 *>(km) = m0;
         *reinterpret_cast<u32x4 *>(km + 4) = m1;
     }
-
-    // ---- K codes and V (per token, per 32-channel run) ----
     float kinv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i) kinv[i] = kq[i].inv();
-    uint32_t *vm_base = reinterpret_cast<uint32_t *>(p.v_meta) + (bh * p.capacity + p.n_tokens + dst0) * (HD / VG);
-    // Batches of rows as above, K and V loads all in flight; a thread's rows past the group
-    // end are recomputed from the last row and not stored. The four lanes of a quad hold
-    // one row (CC is a multiple of 4), so the quad exchanges below see one row's lanes.
-    for (int b0 = 0; b0 < len; b0 += kBatch2 * RP) {
-        Raw kraw[kBatch2], vraw[kBatch2];
+
+    // ---- codes: the remaining V rows, then K ----
+    // Batches of rows as above. The four lanes of a quad hold one row (CC is a multiple of
+    // 4), so the quad exchanges in the row helpers see one row's lanes.
+    if (resident) {
+        for (int b0 = kBatch2 * RP; b0 < len; b0 += kBatch2 * RP) {
+            Raw vraw[kBatch2];
 #pragma unroll
-        for (int u = 0; u < kBatch2; ++u) {
-            const int rr = min(b0 + u * RP + rp, len - 1);
-            kraw[u] = Src<T>::load(ks + (size_t)rr * HD);
-            vraw[u] = Src<T>::load(vs + (size_t)rr * HD);
+            for (int u = 0; u < kBatch2; ++u) vraw[u] = Src<T>::load(vs + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+#pragma unroll
+            for (int u = 0; u < kBatch2; ++u) {
+                float y[8];
+                Src<T>::unpack(vraw[u], y);
+                v_row<HD, BITS>(y, b0 + u * RP + rp, len, cc, vcodes, vm_base);
+            }
         }
 #pragma unroll
-        for (int u = 0; u < kBatch2; ++u) {
-            const int r = b0 + u * RP + rp;
-            float x[8], y[8];
-            Src<T>::unpack(kraw[u], x);
-            Src<T>::unpack(vraw[u], y);
-            float a = y[0], z = y[0];
-#pragma unroll
-            for (int i = 1; i < 8; ++i) { a = fminf(a, y[i]); z = fmaxf(z, y[i]); }
-            // the 4 lanes of one 32-channel run are a quad (CC % 4 == 0)
-            a = fminf(a, quad_xor1(a)); z = fmaxf(z, quad_xor1(z));
-            a = fminf(a, quad_xor2(a)); z = fmaxf(z, quad_xor2(z));
-            Quant vq;
-            vq.set(a, z, L);
-            const float vinv = vq.inv();
-
-            bool near = false;
-            float kc[8], vc[8];
-#pragma unroll
-            for (int i = 0; i < 8; ++i) kc[i] = fast_code(x[i], kq[i].zero, kinv[i], L, near);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) vc[i] = fast_code(y[i], vq.zero, vinv, L, near);
-            uint32_t kbits = pack_codes<BITS>(kc), vbits = pack_codes<BITS>(vc);
-            if (__builtin_expect(__any(near), 0)) {
-                kbits = vbits = 0;
-#pragma unroll
-                for (int i = 0; i < 8; ++i) kbits |= kq[i].code(x[i], L) << (BITS * i);
-#pragma unroll
-                for (int i = 0; i < 8; ++i) vbits |= vq.code(y[i], L) << (BITS * i);
+        for (int u = 0; u < kBatch1; ++u) {
+            if (u * RP < len) {
+                float x[8];
+                Src<T>::unpack(kres[u], x);
+                k_row<HD, BITS>(x, u * RP + rp, len, cc, kq, kinv, kcodes);
             }
-            // 16 channels per INT2 word: the even chunk takes its odd neighbour's half
-            const uint32_t kn = quad_xor1(kbits), vn = quad_xor1(vbits);
-            if (r < len) {
-                if ((cc & 3) == 0) vm_base[(size_t)r * (HD / VG) + cc / 4] = vq.meta;
-                if (BITS == 4) {
-                    kcodes[(size_t)r * WPR + cc] = kbits;
-                    vcodes[(size_t)r * WPR + cc] = vbits;
-                } else if ((cc & 1) == 0) {
-                    kcodes[(size_t)r * WPR + cc / 2] = kbits | (kn << 16);
-                    vcodes[(size_t)r * WPR + cc / 2] = vbits | (vn << 16);
-                }
+        }
+    } else {
+        for (int b0 = 0; b0 < len; b0 += kBatch2 * RP) {
+            Raw kraw[kBatch2], vraw[kBatch2];
+#pragma unroll
+            for (int u = 0; u < kBatch2; ++u) {
+                const int rr = min(b0 + u * RP + rp, len - 1);
+                kraw[u] = Src<T>::load(ks + (size_t)rr * HD);
+                vraw[u] = Src<T>::load(vs + (size_t)rr * HD);
+            }
+#pragma unroll
+            for (int u = 0; u < kBatch2; ++u) {
+                float x[8], y[8];
+                Src<T>::unpack(kraw[u], x);
+                Src<T>::unpack(vraw[u], y);
+                v_row<HD, BITS>(y, b0 + u * RP + rp, len, cc, vcodes, vm_base);
+                k_row<HD, BITS>(x, b0 + u * RP + rp, len, cc, kq, kinv, kcodes);
             }
         }
     }
