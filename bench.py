@@ -231,6 +231,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="video_chunk_int2_h12_d128", choices=sorted(workloads.WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe-hbm", action="store_true",
+                    help="skip the HBM read/copy probe (its copies would mix into a counter run's copy calibration)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the reference dispatch "
@@ -303,7 +305,8 @@ def main():
         "append": {"ms": round(app_avg, 4), "bytes": step.append_bytes(),
                    "gbps": round(step.append_bytes() / (app_avg * 1e-3) / 1e9, 1) if step.append else None},
     }
-    res["probe_hbm"] = probe_hbm()
+    if not args.no_probe_hbm:
+        res["probe_hbm"] = probe_hbm()
     if args.probe_copy_mib:
         n = args.probe_copy_mib << 20
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
