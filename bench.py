@@ -117,6 +117,139 @@ class ChunkStep:
             events[2].record()
 
 
+class WindowStep:
+    """WindowQuant, one step: window scores and the FP16/INT4/INT2 assignment on the GPU, the
+    per-class gather lists on the host (bits and order come back), the three grouped segments
+    rebuilt by gathered appends, then the decode attention over them."""
+
+    def __init__(self, w: workloads.Workload):
+        self.w = w
+        t0 = time.time()
+        self.data = data = workloads.generate(w)
+        log("generated inputs in %.1fs" % (time.time() - t0))
+        self.k = data["cache_k"].cuda()            # [1][Hkv][N][d]
+        self.v = data["cache_v"].cuda()
+        self.text = data["text"].cuda()
+        self.q = data["q"].cuda()
+        self.n16, self.n4 = kvq.window_budget(w.n_windows, w.pct_fp16, w.pct_int4)
+        bits, order, _ = kvq.assign_windows(self.k[0], self.text, self.n16, self.n4, window=w.window)
+        classes = kvq.window_groups(order.cpu().tolist(), bits.cpu().tolist(), w.n_cache, w.window)
+        dt = workloads.DTYPES[w.dtype]
+        self.segs = []
+        self.tokens = {}
+        for b in (16, 4, 2):
+            groups, n_tok = classes[b]
+            self.tokens[b] = n_tok
+            self.segs.append(kvq.Segment(b, dt, 1, w.n_kv_heads, w.head_dim, n_tok, k_group_tokens=w.window,
+                                         kgroup_capacity=max(len(groups), 1)))
+        self.out = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
+        self.ws = None   # sized on the first run, once the segments hold tokens
+
+    def attention_bytes(self) -> float:
+        """The mixed cache (FP16 rows; INT4 / INT2 codes, V step/zero, K step/zero per window)
+        and Q, O, each once."""
+        w = self.w
+        d, H = w.head_dim, w.n_kv_heads
+        total = 2 * H * self.tokens[16] * d * 2
+        for b in (4, 2):
+            n = self.tokens[b]
+            total += H * (n * (2 * d * b / 8 + 4 * (d // 32)) + 4 * d * -(-n // w.window))
+        return total + w.n_q_heads * w.n_q * d * (2 + 4)
+
+    def run(self, ev=None):
+        w = self.w
+        if ev is not None:
+            ev[0].record()
+        bits, order, _ = kvq.assign_windows(self.k[0], self.text, self.n16, self.n4, window=w.window)
+        if ev is not None:
+            ev[1].record()
+        classes = kvq.window_groups(order.cpu().tolist(), bits.cpu().tolist(), w.n_cache, w.window)
+        lists = [(torch.tensor(classes[b][0], dtype=torch.int32).reshape(-1, 2).cuda(), classes[b][1])
+                 for b in (16, 4, 2)]
+        if ev is not None:
+            ev[2].record()
+        for seg, (lst, n_new) in zip(self.segs, lists):
+            seg.reset()
+            kvq.quantize_append(seg, self.k, self.v, n_new=n_new, src_groups=lst)
+        if ev is not None:
+            ev[3].record()
+        if self.ws is None:
+            need = kvq.attention_workspace_size(self.q, self.segs, 0, n_kv_heads=w.n_kv_heads, jensen=w.jensen)
+            self.ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        kvq.chunk_attention(self.q, self.segs, n_kv_heads=w.n_kv_heads, jensen=w.jensen, out=self.out,
+                            workspace=self.ws)
+        if ev is not None:
+            ev[4].record()
+
+
+def window_cpu_baseline(step: WindowStep):
+    """The oracle's whole WindowQuant step once, on the host: scores, assignment, the three
+    gathered appends and the attention of every query row."""
+    import oracle
+    w = step.w
+    threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or os.cpu_count()
+    k = step.data["cache_k"].float().numpy()
+    v = step.data["cache_v"].float().numpy()
+    t0 = time.perf_counter()
+    score = oracle.window_scores(k[0], step.data["text"].numpy(), w.window)
+    bits, order = oracle.assign_windows(score, step.n16, step.n4)
+    segs = []
+    for b in (16, 4, 2):
+        groups = [(int(x) * w.window, min(w.window, w.n_cache - int(x) * w.window)) for x in order if bits[x] == b]
+        n_tok = sum(g[1] for g in groups)
+        seg = oracle.new_segment(b, w.dtype, 1, w.n_kv_heads, w.head_dim, capacity=max(n_tok, 1),
+                                 k_group_tokens=w.window, kgroup_capacity=max(len(groups), 1))
+        oracle.append(seg, k, v, groups=np.asarray(groups, np.int32).reshape(-1, 2))
+        segs.append(seg)
+    oracle.attention(step.data["q"].float().numpy(), segs, n_kv_heads=w.n_kv_heads, jensen=bool(w.jensen))
+    t = time.perf_counter() - t0
+    return {"value": round(t * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+            "sample": "the whole step once: window scores and assignment, the three gathered appends "
+                      "(%d FP16 / %d INT4 / %d INT2 windows) and the attention of all %d query rows"
+                      % (step.n16, step.n4, w.n_windows - step.n16 - step.n4, w.n_q_heads * w.n_q)}
+
+
+def window_main(args, w: workloads.Workload) -> None:
+    step = WindowStep(w)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step.run(evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+    st = {k: [] for k in ("assign", "host_lists", "appends", "attention")}
+    for e in evs:
+        st["assign"].append(e[0].elapsed_time(e[1]) * 1e3)
+        st["host_lists"].append(e[1].elapsed_time(e[2]) * 1e3)
+        st["appends"].append(e[2].elapsed_time(e[3]) * 1e3)
+        st["attention"].append(e[3].elapsed_time(e[4]) * 1e3)
+    med = {k: float(np.median(v)) for k, v in st.items()}
+    device_us = med["assign"] + med["appends"] + med["attention"]
+    gbps = step.attention_bytes() / (med["attention"] * 1e-6) / 1e9
+    res = {"metric": "WindowQuant decode step latency (window scores + FP16/INT4/INT2 assignment, grouped "
+                     "appends, attention), device time",
+           "value": round(device_us, 2), "unit": "us", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+           "ms_per_step": round(wall * 1e3, 4), "higher_is_better": False, "scaling": "weak", "vs_baseline": None,
+           "dtype": "f16", "data": "synthetic",
+           "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
+                      "head_dim": w.head_dim, "cache_tokens": w.n_cache, "window": w.window,
+                      "windows": w.n_windows, "fp16_int4_int2_windows": [step.n16, step.n4,
+                                                                        w.n_windows - step.n16 - step.n4],
+                      "jensen": bool(w.jensen)},
+           "stages_us": {k: round(v, 2) for k, v in med.items()},
+           "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                        "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "attention_kernel",
+                        "note": "launch-bound: %.2f MB per attention launch is %.2f us at peak, so the "
+                                "fraction says nothing about the kernel" % (
+                                    step.attention_bytes() / 1e6, step.attention_bytes() / 8e6)}}
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = window_cpu_baseline(step)
+    print(json.dumps(res), flush=True)
+
+
 def kernel_source_digest() -> str:
     """sha256 over the HIP sources of the library (any change invalidates stored counters)."""
     import hashlib
@@ -249,8 +382,8 @@ def main():
     kvq.lib()
     w = workloads.WORKLOADS[args.workload]
     if w.bits == 0:
-        print("the WindowQuant workload is a parity case, not a bench line", file=sys.stderr)
-        sys.exit(2)
+        window_main(args, w)
+        return
     # decode caches can sit in the 256 MB last-level cache: rotate copies > 2x that size
     copies = args.copies
     if copies == 0:

@@ -864,17 +864,30 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     const size_t qrow = ((size_t)b * p.n_q_heads + h * gqa + row / p.n_q) * p.n_q + row % p.n_q;
     float M = -__builtin_inff(), L = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    for (int64_t w = w0; w <= w1; ++w) {
-        // the row block's piece in share w is that share's first piece iff the share starts in it
-        const float *pp = p.partial + (((size_t)w * 2 + (w * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 4);
-        const f32x4 o = *reinterpret_cast<const f32x4 *>(pp + c);
-        const float m = pp[HD], l = pp[HD + 1];
-        if (m == -__builtin_inff()) continue;   // a piece past the last token
-        const float mn = fmaxf(M, m);
-        const float sa = exp2f(M - mn), sb = exp2f(m - mn);
-        acc = acc * sa + o * sb;
-        L = L * sa + l * sb;
-        M = mn;
+    // pieces in groups of 8 whose loads are in flight together (a row block of a few rows can
+    // be cut into many pieces)
+    constexpr int NP = 8;
+    for (int64_t w = w0; w <= w1; w += NP) {
+        f32x4 o[NP];
+        float m[NP], l[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            const int64_t ww = min(w + k, w1);   // past w1: a repeat, skipped below
+            // the row block's piece in share ww is that share's first piece iff the share starts in it
+            const float *pp = p.partial + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 4);
+            o[k] = *reinterpret_cast<const f32x4 *>(pp + c);
+            m[k] = pp[HD];
+            l[k] = pp[HD + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            if (w + k > w1 || m[k] == -__builtin_inff()) continue;   // a repeat, or a piece past the last token
+            const float mn = fmaxf(M, m[k]);
+            const float sa = exp2f(M - mn), sb = exp2f(m[k] - mn);
+            acc = acc * sa + o[k] * sb;
+            L = L * sa + l[k] * sb;
+            M = mn;
+        }
     }
     const float inv = 1.0f / L;
     const size_t o0 = qrow * HD + c;
