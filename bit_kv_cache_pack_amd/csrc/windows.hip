@@ -73,37 +73,98 @@ __global__ __launch_bounds__(kScoreThreads) void window_score_kernel(WindowParam
     if (tid == 0) p.score[w] = acc / (double)H;
 }
 
-// one workgroup: rank windows 1..W-1 (score descending, ties to the lower index), cut
-// into FP16 / INT4 / INT2 by the budget, then list each class ascending.
+constexpr int kSortMax = 8192;   // windows ranked by a sort in LDS; more are ranked by counting
+
+// window a comes before window b: higher score, ties to the lower index
+__device__ __forceinline__ bool before(double sa, int ia, double sb, int ib) {
+    return sa > sb || (sa == sb && ia < ib);
+}
+
+// One workgroup: rank windows 1..W-1 (score descending, ties to the lower index), cut
+// into FP16 / INT4 / INT2 by the budget (window 0 is FP16), then list each class in
+// ascending window order. The ranking is a bitonic sort of (score, index) in LDS; the
+// lists come from a block prefix sum, over the windows in index order, of three class
+// counters packed in one 64-bit word.
 __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowParams p) {
     __shared__ int8_t cls[kMaxWindows];
-    __shared__ double sc[kMaxWindows];   // the scores, read W times each by the ranking
-    const int W = p.n_windows;
-    for (int w = threadIdx.x; w < W; w += kSelectThreads) sc[w] = p.score[w];
-    __syncthreads();
-    for (int w = threadIdx.x; w < W; w += kSelectThreads) {
-        int8_t bits = 16;
-        if (w > 0) {
-            const double s = sc[w];
+    __shared__ double key[kSortMax];
+    __shared__ int idx[kSortMax];
+    __shared__ unsigned long long wsum[kSelectThreads / kWave];
+    const int W = p.n_windows, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+    const int n16 = p.n_fp16, n4 = p.n_int4;
+    const int M = W - 1;
+    auto class_of = [&](int rank) -> int8_t { return rank < n16 - 1 ? 16 : (rank < n16 - 1 + n4 ? 4 : 2); };
+    if (M <= kSortMax) {
+        int N = 1;
+        while (N < M) N <<= 1;
+        for (int i = tid; i < N; i += kSelectThreads) {
+            key[i] = i < M ? p.score[i + 1] : -__builtin_inf();
+            idx[i] = i < M ? i + 1 : 0x7fffffff;   // pads sort last
+        }
+        __syncthreads();
+        for (int k = 2; k <= N; k <<= 1) {
+            for (int j = k >> 1; j > 0; j >>= 1) {
+                for (int i = tid; i < N; i += kSelectThreads) {
+                    const int l = i ^ j;
+                    if (l > i) {
+                        const double si = key[i], sl = key[l];
+                        const int ii = idx[i], il = idx[l];
+                        // blocks with bit k clear end in "before" order, the others in reverse
+                        const bool swap = (i & k) == 0 ? before(sl, il, si, ii) : before(si, ii, sl, il);
+                        if (swap) {
+                            key[i] = sl; key[l] = si;
+                            idx[i] = il; idx[l] = ii;
+                        }
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        // position r holds the window of rank r
+        for (int r = tid; r < M; r += kSelectThreads) cls[idx[r]] = class_of(r);
+    } else {
+        for (int w = threadIdx.x; w < W; w += kSelectThreads) {
+            if (w == 0) continue;
+            const double s = p.score[w];
             int rank = 0;
             for (int v = 1; v < W; ++v) {
-                const double t = sc[v];
-                rank += (t > s || (t == s && v < w)) ? 1 : 0;
+                const double t = p.score[v];
+                rank += before(t, v, s, w) ? 1 : 0;
             }
-            bits = rank < p.n_fp16 - 1 ? 16 : (rank < p.n_fp16 - 1 + p.n_int4 ? 4 : 2);
+            cls[w] = class_of(rank);
         }
-        cls[w] = bits;
-        p.bits_out[w] = bits;
     }
+    if (tid == 0) cls[0] = 16;
     __syncthreads();
-    const int n16 = p.n_fp16, n4 = p.n_int4;
-    for (int w = threadIdx.x; w < W; w += kSelectThreads) {
-        const int8_t b = cls[w];
-        int before = 0;
-        for (int v = 0; v < w; ++v) before += cls[v] == b ? 1 : 0;
-        const int base = b == 16 ? 0 : (b == 4 ? n16 : n16 + n4);
-        // ranks form a permutation unless scores are NaN; never write outside the list
-        if (base + before < W) p.order_out[base + before] = w;
+    // class lists, each in ascending window order: FP16 at 0, INT4 at n16, INT2 at n16 + n4
+    unsigned long long carry = 0;   // counts of the windows before this chunk, 21 bits per class
+    for (int w0 = 0; w0 < W; w0 += kSelectThreads) {
+        const int w = w0 + tid;
+        const int8_t b = w < W ? cls[w] : 0;
+        if (w < W) p.bits_out[w] = b;
+        const int sh = b == 16 ? 0 : (b == 4 ? 21 : 42);
+        const unsigned long long v = w < W ? 1ull << sh : 0ull;
+        unsigned long long x = v;
+#pragma unroll
+        for (int o = 1; o < kWave; o <<= 1) {
+            const unsigned long long y = __shfl_up(x, o);
+            if (lane >= o) x += y;
+        }
+        if (lane == kWave - 1) wsum[wave] = x;
+        __syncthreads();
+        unsigned long long pre = carry + x - v, tot = carry;
+        for (int k = 0; k < kSelectThreads / kWave; ++k) {
+            if (k < wave) pre += wsum[k];
+            tot += wsum[k];
+        }
+        if (w < W) {
+            const int before_w = (int)((pre >> sh) & 0x1fffff);
+            const int base = b == 16 ? 0 : (b == 4 ? n16 : n16 + n4);
+            // ranks form a permutation, so this stays inside the list; never write outside it
+            if (base + before_w < W) p.order_out[base + before_w] = w;
+        }
+        carry = tot;
+        __syncthreads();
     }
 }
 
