@@ -164,8 +164,7 @@ class WindowStep:
         if ev is not None:
             ev[1].record()
         classes = kvq.window_groups(order.cpu().tolist(), bits.cpu().tolist(), w.n_cache, w.window)
-        lists = [(torch.tensor(classes[b][0], dtype=torch.int32).reshape(-1, 2).cuda(), classes[b][1])
-                 for b in (16, 4, 2)]
+        lists = [(torch.from_numpy(classes[b][0]).cuda(), classes[b][1]) for b in (16, 4, 2)]
         if ev is not None:
             ev[2].record()
         for seg, (lst, n_new) in zip(self.segs, lists):

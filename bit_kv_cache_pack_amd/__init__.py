@@ -20,6 +20,7 @@ import math
 import os
 from typing import List, Optional, Sequence
 
+import numpy as np
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
@@ -265,9 +266,13 @@ def window_budget(n_windows: int, pct_fp16: int, pct_int4: int):
 
 def window_groups(order: Sequence[int], bits: Sequence[int], n_tokens: int, window: int = 32):
     """Host helper: per bit-width class, the {first token, length} gather list of its windows
-    in grouped storage order, and the class's token count."""
+    in grouped storage order (an int32 [n][2] array, the layout kvq_quantize_append takes),
+    and the class's token count."""
+    order = np.asarray(order, dtype=np.int64).reshape(-1)
+    bits = np.asarray(bits).reshape(-1)
     out = {}
     for b in (16, 4, 2):
-        g = [(w * window, min(window, n_tokens - w * window)) for w in order if bits[w] == b]
-        out[b] = (g, sum(x[1] for x in g))
+        starts = order[bits[order] == b] * window
+        g = np.stack([starts, np.minimum(window, n_tokens - starts)], axis=1).astype(np.int32).reshape(-1, 2)
+        out[b] = (g, int(g[:, 1].sum()))
     return out

@@ -6,6 +6,7 @@ import os
 import re
 import subprocess
 
+import numpy as np
 import pytest
 
 import bit_kv_cache_pack_amd as kvq
@@ -193,4 +194,7 @@ def test_window_validation():
 def test_binding_window_budget():
     assert kvq.window_budget(613, 10, 30) == (61, 184)
     g = kvq.window_groups([0, 2, 1, 3], [16, 4, 16, 2], n_tokens=100)
-    assert g[16] == ([(0, 32), (64, 32)], 64) and g[4] == ([(32, 32)], 32) and g[2] == ([(96, 4)], 4)
+    assert g[16][0].tolist() == [[0, 32], [64, 32]] and g[16][1] == 64
+    assert g[4][0].tolist() == [[32, 32]] and g[4][1] == 32
+    assert g[2][0].tolist() == [[96, 4]] and g[2][1] == 4
+    assert all(g[b][0].dtype == np.int32 and g[b][0].shape[1] == 2 for b in (16, 4, 2))
