@@ -38,6 +38,18 @@ def test_quantize_append_bit_exact(bits, d, src):
     assert_segments_equal(gseg, oseg)
 
 
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("d,Gk", [(128, 512), (64, 1024)])
+def test_quantize_append_long_groups_bit_exact(bits, d, Gk):
+    """K-groups longer than a thread's rows held in registers (more than 8 rows per thread):
+    16-bit sources take the batched reload path, with ragged tails."""
+    B, H = 1, 2
+    gseg, oseg = make_pair(bits, "bf16", B, H, d, capacity=2 * Gk + 300, Gk=Gk, kgroup_capacity=8)
+    for i, n in enumerate((Gk + 37, Gk - 5)):
+        append_both(gseg, oseg, _rand((B, H, n, d), "bf16", 40 + i, 3.0), _rand((B, H, n, d), "bf16", 50 + i))
+    assert_segments_equal(gseg, oseg)
+
+
 @pytest.mark.parametrize("bits", [2, 4, 16])
 def test_quantize_append_gather_bit_exact(bits):
     B, H, d, N = 1, 2, 64, 200
