@@ -699,143 +699,143 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     const int64_t u0 = (int64_t)blockIdx.x * p.quota;
     const int64_t u1 = min(u0 + p.quota, p.work);
     for (int64_t u = u0; u < u1;) {
-    const int64_t rb = u / p.tok_pad;
-    const int64_t rbeg = rb * p.tok_pad;
-    const int64_t ue = min(u1, rbeg + p.tok_pad);
-    const int tb = (int)(u - rbeg);
-    const int te = min((int)(ue - rbeg), p.n_total);
-    const bool whole = tb == 0 && ue == rbeg + p.tok_pad;
-    const int pslot = u == u0 ? 0 : 1;
-    u = ue;
-    const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
-    const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
-    const int row = rbi * BM + wave * 32 + r32;
-    const bool row_ok = row < rows;
-    const bool wave_ok = rbi * BM + wave * 32 < rows;
-    const int hq = h * gqa + (row_ok ? row / p.n_q : 0);
-    const int qi = row_ok ? row % p.n_q : 0;
-    const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
-    const size_t bh = (size_t)b * p.n_kv_heads + h;
+        const int64_t rb = u / p.tok_pad;
+        const int64_t rbeg = rb * p.tok_pad;
+        const int64_t ue = min(u1, rbeg + p.tok_pad);
+        const int tb = (int)(u - rbeg);
+        const int te = min((int)(ue - rbeg), p.n_total);
+        const bool whole = tb == 0 && ue == rbeg + p.tok_pad;
+        const int pslot = u == u0 ? 0 : 1;
+        u = ue;
+        const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
+        const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
+        const int row = rbi * BM + wave * 32 + r32;
+        const bool row_ok = row < rows;
+        const bool wave_ok = rbi * BM + wave * 32 < rows;
+        const int hq = h * gqa + (row_ok ? row / p.n_q : 0);
+        const int qi = row_ok ? row % p.n_q : 0;
+        const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
+        const size_t bh = (size_t)b * p.n_kv_heads + h;
 
-    C cx;
-    {
-        // positions 16 ks + 8 hh + i hold channels 16 ks + 4 (i % 4) + 2 hh + i / 4:
-        // element pairs (ch 2hh, 4+2hh), (8+2hh, 12+2hh), (2hh+1, 5+2hh), (9+2hh, 13+2hh)
-        // dword m of a block holds channels 2m, 2m+1: this lane uses dwords hh + 2k, k = 0..3
-        const uint32_t *qp = reinterpret_cast<const uint32_t *>(p.q) + qrow * (HD / 2) + hh;
+        C cx;
+        {
+            // positions 16 ks + 8 hh + i hold channels 16 ks + 4 (i % 4) + 2 hh + i / 4:
+            // element pairs (ch 2hh, 4+2hh), (8+2hh, 12+2hh), (2hh+1, 5+2hh), (9+2hh, 13+2hh)
+            // dword m of a block holds channels 2m, 2m+1: this lane uses dwords hh + 2k, k = 0..3
+            const uint32_t *qp = reinterpret_cast<const uint32_t *>(p.q) + qrow * (HD / 2) + hh;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            uint32_t d0 = 0u, d2 = 0u, d4 = 0u, d6 = 0u;
-            if (row_ok) {
-                d0 = qp[8 * ks];
-                d2 = qp[8 * ks + 2];
-                d4 = qp[8 * ks + 4];
-                d6 = qp[8 * ks + 6];
+            for (int ks = 0; ks < C::KS; ++ks) {
+                uint32_t d0 = 0u, d2 = 0u, d4 = 0u, d6 = 0u;
+                if (row_ok) {
+                    d0 = qp[8 * ks];
+                    d2 = qp[8 * ks + 2];
+                    d4 = qp[8 * ks + 4];
+                    d6 = qp[8 * ks + 6];
+                }
+                u32x4 o;
+                o.x = perm(d2, d0, 0x05040100u);
+                o.y = perm(d6, d4, 0x05040100u);
+                o.z = perm(d2, d0, 0x07060302u);
+                o.w = perm(d6, d4, 0x07060302u);
+                cx.q[ks] = __builtin_bit_cast(vec, o);
             }
-            u32x4 o;
-            o.x = perm(d2, d0, 0x05040100u);
-            o.y = perm(d6, d4, 0x05040100u);
-            o.z = perm(d2, d0, 0x07060302u);
-            o.w = perm(d6, d4, 0x07060302u);
-            cx.q[ks] = __builtin_bit_cast(vec, o);
         }
-    }
 #pragma unroll
-    for (int db = 0; db < C::DB; ++db) cx.o[db] = f32x16{};
-    cx.btab = btab_all[wave];
-    cx.m = -__builtin_inff();
-    cx.l = 0.f;
-    cx.beta = 0.f;
+        for (int db = 0; db < C::DB; ++db) cx.o[db] = f32x16{};
+        cx.btab = btab_all[wave];
+        cx.m = -__builtin_inff();
+        cx.l = 0.f;
+        cx.beta = 0.f;
 
-    // The piece's tiles, from lists built in bulk (all threads call fetch() together, in
-    // order of i; a new list is built only after every wave has read the tiles it needs from
-    // the old one: the ones it holds in cur, nxt and far).
-    list_setup(p, tb, te, tlist);
-    int u_total = 0;
-    for (int si = 0; si <= p.n_segs; ++si) u_total += tlist.seg[si].units;
-    u_total = __builtin_amdgcn_readfirstlane(u_total);
-    int u_next = 0, list_base = 0, list_n = 0;
-    auto fetch = [&](int i) -> Tile {
-        while (i >= list_base + list_n && u_next < u_total) {
-            list_base += list_n;
-            u_next = __builtin_amdgcn_readfirstlane(u_next + list_build(p, tlist, u_next, u_total));
-            list_n = __builtin_amdgcn_readfirstlane(tlist.n_tiles);
-        }
-        return i < list_base + list_n ? uniform(tlist.t[i - list_base]) : Tile::make(TILE_END, 0, 0, 0, 0, 0, 0, 16);
-    };
-    Tile cur = fetch(0);
-    Tile nxt = fetch(1);
-    Tile far = fetch(2);
-    // Pipeline per tile i (one barrier per tile): tile i is computed out of LDS buffer i%2
-    // while tile i+1, loaded into registers during tile i-1, is dequantized into buffer
-    // (i+1)%2; then tile i+2 is loaded into the registers.
-    Prefetch pf;
-    if (cur.kind() != TILE_END) {
-        prefetch_tile<HD>(pf, p, cur, bh);
-        stage_tile<HD, BF16>(smem, pf, stage_kind(cur));
-    }
-    if (nxt.kind() != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
-    __syncthreads();
-    int buf = 0, it = 0;  // cur is tile it of the piece
-    while (cur.kind() != TILE_END) {
-        const int sk = stage_kind(nxt);
-        const uint16_t *cbuf = smem + buf * G::BUF;
-        uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
-        if (wave_ok) {
-            if (cur.kind() == TILE_PACKED) {
-                if (cur.batch()) beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g);
-                if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.jrow());
-            } else {
-                cx.beta = 0.f;
+        // The piece's tiles, from lists built in bulk (all threads call fetch() together, in
+        // order of i; a new list is built only after every wave has read the tiles it needs from
+        // the old one: the ones it holds in cur, nxt and far).
+        list_setup(p, tb, te, tlist);
+        int u_total = 0;
+        for (int si = 0; si <= p.n_segs; ++si) u_total += tlist.seg[si].units;
+        u_total = __builtin_amdgcn_readfirstlane(u_total);
+        int u_next = 0, list_base = 0, list_n = 0;
+        auto fetch = [&](int i) -> Tile {
+            while (i >= list_base + list_n && u_next < u_total) {
+                list_base += list_n;
+                u_next = __builtin_amdgcn_readfirstlane(u_next + list_build(p, tlist, u_next, u_total));
+                list_n = __builtin_amdgcn_readfirstlane(tlist.n_tiles);
             }
-            f32x16 s[2];
-            if (sk == STAGE_INT2) qk_stage<HD, BF16, STAGE_INT2>(cx, cbuf, nbuf, pf, s);
-            else if (sk == STAGE_INT4) qk_stage<HD, BF16, STAGE_INT4>(cx, cbuf, nbuf, pf, s);
-            else if (sk == STAGE_RAW) qk_stage<HD, BF16, STAGE_RAW>(cx, cbuf, nbuf, pf, s);
-            else qk_stage<HD, BF16, STAGE_NONE>(cx, cbuf, nbuf, pf, s);
-            softmax_pv<HD, BF16>(cx, cbuf + G::KBUF, s, cur.len, p.scale_log2);
-            if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
-        } else {
-            stage_tile<HD, BF16>(nbuf, pf, sk);
-            if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
+            return i < list_base + list_n ? uniform(tlist.t[i - list_base]) : Tile::make(TILE_END, 0, 0, 0, 0, 0, 0, 16);
+        };
+        Tile cur = fetch(0);
+        Tile nxt = fetch(1);
+        Tile far = fetch(2);
+        // Pipeline per tile i (one barrier per tile): tile i is computed out of LDS buffer i%2
+        // while tile i+1, loaded into registers during tile i-1, is dequantized into buffer
+        // (i+1)%2; then tile i+2 is loaded into the registers.
+        Prefetch pf;
+        if (cur.kind() != TILE_END) {
+            prefetch_tile<HD>(pf, p, cur, bh);
+            stage_tile<HD, BF16>(smem, pf, stage_kind(cur));
         }
-        if (nxt.kind() == TILE_END) break;
+        if (nxt.kind() != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
         __syncthreads();
-        buf ^= 1;
-        cur = nxt;
-        nxt = far;
-        far = fetch(++it + 2);
-    }
-
-    // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
-    const float lt = cx.l + other_half(cx.l);
-    if (row_ok && whole) {
-        const float inv = 1.0f / lt;
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int ch = swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4));
-                const float v = cx.o[db][j] * inv;
-                if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + ch] = v;
-                else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_bf16_bits(v);
-                else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_f16_bits(v);
+        int buf = 0, it = 0;  // cur is tile it of the piece
+        while (cur.kind() != TILE_END) {
+            const int sk = stage_kind(nxt);
+            const uint16_t *cbuf = smem + buf * G::BUF;
+            uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
+            if (wave_ok) {
+                if (cur.kind() == TILE_PACKED) {
+                    if (cur.batch()) beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g);
+                    if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.jrow());
+                } else {
+                    cx.beta = 0.f;
+                }
+                f32x16 s[2];
+                if (sk == STAGE_INT2) qk_stage<HD, BF16, STAGE_INT2>(cx, cbuf, nbuf, pf, s);
+                else if (sk == STAGE_INT4) qk_stage<HD, BF16, STAGE_INT4>(cx, cbuf, nbuf, pf, s);
+                else if (sk == STAGE_RAW) qk_stage<HD, BF16, STAGE_RAW>(cx, cbuf, nbuf, pf, s);
+                else qk_stage<HD, BF16, STAGE_NONE>(cx, cbuf, nbuf, pf, s);
+                softmax_pv<HD, BF16>(cx, cbuf + G::KBUF, s, cur.len, p.scale_log2);
+                if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
+            } else {
+                stage_tile<HD, BF16>(nbuf, pf, sk);
+                if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
             }
-        if (p.lse != nullptr && hh == 0) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
-    } else if (row_ok) {
-        float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 4);
-#pragma unroll
-        for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-                pp[swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4))] = cx.o[db][j];
-        if (hh == 0) {
-            pp[HD] = cx.m;
-            pp[HD + 1] = lt;
+            if (nxt.kind() == TILE_END) break;
+            __syncthreads();
+            buf ^= 1;
+            cur = nxt;
+            nxt = far;
+            far = fetch(++it + 2);
         }
-    }
-    // the next piece restages the LDS buffers and rebuilds the tile list
-    if (u < u1) __syncthreads();
+
+        // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
+        const float lt = cx.l + other_half(cx.l);
+        if (row_ok && whole) {
+            const float inv = 1.0f / lt;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) {
+                    const int ch = swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4));
+                    const float v = cx.o[db][j] * inv;
+                    if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + ch] = v;
+                    else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_bf16_bits(v);
+                    else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_f16_bits(v);
+                }
+            if (p.lse != nullptr && hh == 0) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
+        } else if (row_ok) {
+            float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 4);
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j)
+                    pp[swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4))] = cx.o[db][j];
+            if (hh == 0) {
+                pp[HD] = cx.m;
+                pp[HD + 1] = lt;
+            }
+        }
+        // the next piece restages the LDS buffers and rebuilds the tile list
+        if (u < u1) __syncthreads();
     }
 }
 
