@@ -53,7 +53,8 @@ def _compile(src: str, verbose: bool, obj_dir: str = OBJ_DIR, extra=()) -> str:
 
 
 def build(verbose: bool = False, out: str = LIB, defines=()) -> str:
-    """Compile and link; ``defines`` (e.g. KVQ_ATTN_BLOCKS_PER_CU=1) build a tuning variant."""
+    """Compile and link; ``defines`` (NAME=VALUE strings) are passed as -D flags and compiled
+    into an object folder of their own, so a variant does not overwrite the default objects."""
     extra = ["-D" + d for d in defines]
     obj_dir = OBJ_DIR if not defines else OBJ_DIR + "_" + "_".join(d.replace("=", "") for d in defines)
     os.makedirs(obj_dir, exist_ok=True)
