@@ -423,7 +423,10 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
             m[k] = v.x;
             m[4 + k] = v.y;
         }
-        const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+        // opaque: the squares below are derived here, not hoisted out of the tile loop (the
+        // queries do not change within a piece) and kept in scratch memory
+        u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+        asm volatile("" : "+v"(qw));
         bf16x8 ah, al, bh8, bl8;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
