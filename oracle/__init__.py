@@ -212,10 +212,11 @@ def dequant_segment(seg: Dict, b: int = 0, h: int = 0, exact: bool = False):
 # -------------------------------------------------------------------- attention
 def attention(q: np.ndarray, segs: List[Dict], k_cur: Optional[np.ndarray] = None,
               v_cur: Optional[np.ndarray] = None, n_kv_heads: Optional[int] = None,
-              scale: Optional[float] = None, jensen: bool = True, exact: bool = False,
+              scale: Optional[float] = None, jensen: int = 1, exact: bool = False,
               rows: Optional[Sequence[int]] = None, want_mass: bool = False):
-    """A1-A3 in double. q float [B][Hq][nq][d]. Returns (out [B][Hq][n_rows][d] float64,
-    lse [B][Hq][n_rows]) and, with want_mass, the softmax mass on cached tokens."""
+    """A1-A3 in double. q float [B][Hq][nq][d]. jensen: 0 off, 1 the channel-weighted
+    second-order term, 2 its isotropic (query-norm) form. Returns (out [B][Hq][n_rows][d]
+    float64, lse [B][Hq][n_rows]) and, with want_mass, the softmax mass on cached tokens."""
     q = _c(q, np.float32)
     B, Hq, nq, d = q.shape
     if n_kv_heads is None:
@@ -243,9 +244,10 @@ def attention(q: np.ndarray, segs: List[Dict], k_cur: Optional[np.ndarray] = Non
 
 
 def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, tok_group: np.ndarray,
-               step_sq: np.ndarray, scale: float, jensen: bool):
+               step_sq: np.ndarray, scale: float, jensen: int):
     """One query over a dense key/value list (real-valued keys, e.g. keys plus sampled
-    rounding noise). Returns (out [d], lse, mass on grouped tokens)."""
+    rounding noise); jensen as in attention(). Returns (out [d], lse, mass on grouped
+    tokens)."""
     q = _c(q, np.float64); K = _c(K, np.float64); V = _c(V, np.float64)
     tg = _c(tok_group, np.int32); ssq = _c(step_sq, np.float64)
     d = q.size

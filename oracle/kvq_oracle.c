@@ -301,11 +301,15 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
 /* Attention of one query row over a dense key/value list (A2, A3).
  *   s_j = scale * q . k_j - beta(q, group(j))        token j in a quantized K-group
  *   s_j = scale * q . k_j                            raw token (group < 0)
- *   beta(q, g) = scale^2 / 24 * sum_c q_c^2 * step_{g,c}^2    (jensen != 0)
+ *   beta(q, g) = scale^2 / 24 * sum_c q_c^2 * step_{g,c}^2    (jensen == 1)
+ *   beta(q, g) = scale^2 / 24 * |q|^2 * mean_c step_{g,c}^2   (jensen == 2)
  * beta is half the variance of the logit noise scale * q . e when each key
  * channel's rounding error e_c is uniform on [-step/2, step/2] (variance step^2/12)
  * and independent: the second-order term of log E[exp(scale * q . e)], which is what
- * quantization noise adds to a cached key's logit on average [JB].
+ * quantization noise adds to a cached key's logit on average [JB]. The second form
+ * is the one [JB] states through the query's norm: each channel's step^2 replaced by
+ * its mean over the group's channels (the two agree when the steps are equal across
+ * channels).
  * out_c = sum_j softmax(s)_j v_jc; lse = log sum_j exp(s_j); mass = softmax mass
  * on tokens with group >= 0 (the quantized history). Everything in double. */
 void orc_attend_row(const double *q, int d, const double *K, const double *V,
@@ -315,10 +319,18 @@ void orc_attend_row(const double *q, int d, const double *K, const double *V,
     double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     double *beta = (double *)malloc(sizeof(double) * (size_t)(n_groups > 0 ? n_groups : 1));
     for (int g = 0; g < n_groups; ++g) {
-        double acc = 0.0;
-        for (int c = 0; c < d; ++c)
+        double acc = 0.0, qq = 0.0, ss = 0.0;
+        for (int c = 0; c < d; ++c) {
             acc += q[c] * q[c] * step_sq[(size_t)g * d + c];
-        beta[g] = jensen ? scale * scale / 24.0 * acc : 0.0;
+            qq += q[c] * q[c];
+            ss += step_sq[(size_t)g * d + c];
+        }
+        if (jensen == 1)
+            beta[g] = scale * scale / 24.0 * acc;
+        else if (jensen == 2)
+            beta[g] = scale * scale / 24.0 * qq * (ss / d);
+        else
+            beta[g] = 0.0;
     }
     double m = -INFINITY;
     for (int64_t j = 0; j < N; ++j) {

@@ -69,7 +69,12 @@ def sdpa_reference(q, segs, k_cur, v_cur, Hkv, scale, jensen):
             for r in range(gqa):
                 hq = h * gqa + r
                 qq = q[b, hq].astype(np.float64)                       # [nq][d]
-                beta = scale * scale / 24.0 * (qq * qq) @ S2.T if jensen else np.zeros((nq, K.shape[0]))
+                if jensen == 1:
+                    beta = scale * scale / 24.0 * (qq * qq) @ S2.T
+                elif jensen == 2:
+                    beta = scale * scale / 24.0 * np.outer((qq * qq).sum(1), S2.mean(1))
+                else:
+                    beta = np.zeros((nq, K.shape[0]))
                 o = F.scaled_dot_product_attention(
                     torch.from_numpy(qq)[None, None], torch.from_numpy(K)[None, None],
                     torch.from_numpy(V)[None, None], attn_mask=torch.from_numpy(-beta)[None, None],
@@ -89,7 +94,7 @@ def build_cache(orc, w, data):
     return seg
 
 
-@pytest.mark.parametrize("jensen", [0, 1])
+@pytest.mark.parametrize("jensen", [0, 1, 2])
 def test_tiny_workload_vs_sdpa(orc, jensen):
     w = workloads.WORKLOADS["tiny_int2_h1_d64"]
     data = workloads.generate(w)
@@ -114,7 +119,7 @@ def test_gqa_mixed_segments_vs_sdpa(orc):
     q = torch.from_numpy(rng.standard_normal((B, Hq, 5, d)).astype(np.float32)).bfloat16().float().numpy()
     kc = torch.from_numpy(rng.standard_normal((B, Hkv, 10, d)).astype(np.float32)).bfloat16().float().numpy()
     vc = torch.from_numpy(rng.standard_normal((B, Hkv, 10, d)).astype(np.float32)).bfloat16().float().numpy()
-    for jensen in (0, 1):
+    for jensen in (0, 1, 2):
         out, lse = orc.attention(q, segs, kc, vc, scale=0.125, jensen=jensen)
         ref = sdpa_reference(q, segs, kc, vc, Hkv, 0.125, jensen)
         assert np.abs(out - ref).max() < 1e-12
