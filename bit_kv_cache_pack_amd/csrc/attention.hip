@@ -404,15 +404,32 @@ template <int HD, bool BF16> struct Ctx {
 };
 
 // Jensen sums of K-groups g0 .. g0+31 of a segment for the wave's 32 queries:
-// sum over positions of step^2 * q^2, as three bf16 MFMAs on high/low splits.
+// sum over positions of step^2 * q^2, as three bf16 MFMAs on high/low splits. In the
+// isotropic form every position's step^2 is the group's mean over its channels, which
+// makes the sum |q|^2 * mean_c step_c^2.
 template <int HD, bool BF16>
-__device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0) {
+__device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0, bool iso) {
     typedef Ctx<HD, BF16> C;
     const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
     const int g = g0 + r32;
     const bool ok = g < sg.n_kgroups;
     // this lane's channels in block ks: 4k + 2hh (elements i = k) and 4k + 2hh + 1 (i = 4 + k)
     const uint32_t *km = sg.k_meta + (bh * sg.kgroup_capacity + (ok ? g : 0)) * HD + 2 * hh;
+    float mean = 0.f;
+    if (iso) {
+        // this lane's half of the group's channels, then the other half (lane ^ 32)
+        float sum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks)
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const u32x2 v = ok ? *reinterpret_cast<const u32x2 *>(km + 16 * ks + 4 * k) : u32x2{0u, 0u};
+                const float s0 = f16_bits_to_f32(v.x & 0xffffu), s1 = f16_bits_to_f32(v.y & 0xffffu);
+                sum = __builtin_fmaf(s0, s0, sum);
+                sum = __builtin_fmaf(s1, s1, sum);
+            }
+        mean = (sum + other_half(sum)) * (1.0f / HD);
+    }
     f32x16 acc = {};
 #pragma unroll
     for (int ks = 0; ks < C::KS; ++ks) {
@@ -432,7 +449,7 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
         for (int i = 0; i < 8; ++i) {
             // position 16 ks + 8 hh + i holds channel 4 (i % 4) + 2 hh + i / 4 of the block
             const float st = f16_bits_to_f32(m[i] & 0xffffu);
-            const float s2 = st * st;
+            const float s2 = iso ? mean : st * st;
             const __bf16 s2h = (__bf16)s2;
             ah[i] = s2h;
             al[i] = (__bf16)(s2 - (float)s2h);
@@ -786,7 +803,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
             if (wave_ok) {
                 if (cur.kind() == TILE_PACKED) {
-                    if (cur.batch()) beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g);
+                    if (cur.batch()) beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, p.jensen == JENSEN_ISO);
                     if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.jrow());
                 } else {
                     cx.beta = 0.f;

@@ -294,11 +294,12 @@ __device__ __forceinline__ void kmeta_block(const u32x4 (&km)[4 * DGeo<HD>::NBL]
     }
 }
 
-// sum over the row's channels of (q_c step_c)^2, for the lane's row
+// sum over the row's channels of (q_c step_c)^2, for the lane's row; in the isotropic
+// form |q|^2 * mean_c step_c^2 instead
 template <int HD, bool BF16>
-__device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx) {
+__device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx, bool iso) {
     typedef DGeo<HD> G;
-    float acc = 0.f;
+    float acc = 0.f, qq = 0.f, ss = 0.f;
 #pragma unroll
     for (int ks = 0; ks < G::KS; ++ks) {
         const u32x4 qw = __builtin_bit_cast(u32x4, cx.qb[ks]);
@@ -307,9 +308,22 @@ __device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx) {
             const int pos = 8 * (ks & 1) + i;                // position inside block ks / 2
             const int ch = 16 * (ks >> 1) + swap_pos(pos);   // channel inside the quarter
             const uint32_t qbits = (qw[i / 2] >> (16 * (i % 2))) & 0xffffu;
-            const float t = mul_step(Elem<BF16>::val(qbits), cx.km[ch / 4][ch % 4]);
+            const float qv = Elem<BF16>::val(qbits);
+            const float t = mul_step(qv, cx.km[ch / 4][ch % 4]);
             acc = __builtin_fmaf(t, t, acc);
+            if (iso) {
+                const float st = mul_step(1.0f, cx.km[ch / 4][ch % 4]);
+                qq = __builtin_fmaf(qv, qv, qq);
+                ss = __builtin_fmaf(st, st, ss);
+            }
         }
+    }
+    if (iso) {
+        qq += __shfl_xor(qq, 16);
+        qq += other_half(qq);
+        ss += __shfl_xor(ss, 16);
+        ss += other_half(ss);
+        return qq * ss * (1.0f / HD);
     }
     acc += __shfl_xor(acc, 16);
     acc += other_half(acc);
@@ -329,7 +343,8 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     const int len = st.len;
     const bool nx_packed = nx.kind == ST_PACKED;
 
-    if (packed && st.new_group) cx.beta = p.jensen ? p.beta_log2 * jensen_sum<HD, BF16>(cx) : 0.f;
+    if (packed && st.new_group)
+        cx.beta = p.jensen ? p.beta_log2 * jensen_sum<HD, BF16>(cx, p.jensen == JENSEN_ISO) : 0.f;
     if (!packed) cx.beta = 0.f;
 
     // ---- S^T = K^ Q^T: s[b][i] = logit of token 16 b + 4 j + i for row r16

@@ -57,7 +57,7 @@ struct AttnParams {
     int32_t n_total;               // history + current tokens
     float scale_log2;              // softmax scale * log2(e)
     float beta_log2;               // scale^2 / 24 * log2(e) when Jensen is on, else 0
-    int32_t jensen;
+    int32_t jensen;                // kvq_jensen
     void *out;
     int32_t out_dtype;
     float *lse;

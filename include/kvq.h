@@ -67,7 +67,12 @@ typedef enum kvq_jensen {
      * token of K-group g: half the variance of the logit noise tau * q . e when each key
      * channel's rounding error e_c is uniform on [-step/2, step/2], i.e. the second-order
      * term of log E[exp(tau q . e)]. step is the stored fp16 step; no extra memory. */
-    KVQ_JENSEN_TAYLOR2 = 1
+    KVQ_JENSEN_TAYLOR2 = 1,
+    /* beta(i, g) = tau^2 / 24 * |q_i|^2 * mean_c step_gc^2: the form [JB] states through
+     * the query's norm, i.e. TAYLOR2 with every channel's step^2 replaced by its mean over
+     * the group's channels (equal to TAYLOR2 when a group's steps are equal across
+     * channels; the mean of TAYLOR2 over cyclic shifts of the step vector otherwise). */
+    KVQ_JENSEN_ISO = 2
 } kvq_jensen;
 
 /*
@@ -202,7 +207,7 @@ kvq_status kvq_assign_windows(const kvq_window_args *args, void *stream);
  *            NULL when that size is 0). Contents on entry do not matter.
  * Errors: KVQ_ERR_ARG (nulls, shape mismatch, no tokens at all, n_q_heads not a
  * multiple of n_kv_heads), KVQ_ERR_UNSUPPORTED (dtypes, head_dim, bits, too many
- * segments), KVQ_ERR_WORKSPACE.
+ * segments, jensen not a kvq_jensen value), KVQ_ERR_WORKSPACE.
  */
 typedef struct kvq_attn_args {
     const void *q;

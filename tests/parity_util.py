@@ -83,7 +83,7 @@ def gpu_attention(q, gsegs, k_cur=None, v_cur=None, n_kv_heads=None, jensen=1, o
 def oracle_attention(q, osegs, k_cur=None, v_cur=None, n_kv_heads=None, jensen=1, rows=None, scale=None):
     kc = None if k_cur is None else f32(k_cur)
     vc = None if v_cur is None else f32(v_cur)
-    return oracle.attention(f32(q), osegs, kc, vc, n_kv_heads=n_kv_heads, jensen=bool(jensen), rows=rows,
+    return oracle.attention(f32(q), osegs, kc, vc, n_kv_heads=n_kv_heads, jensen=int(jensen), rows=rows,
                             scale=scale)
 
 

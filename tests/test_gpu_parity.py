@@ -110,7 +110,7 @@ def _attention_case(bits, dtype, B, Hq, Hkv, d, appends, n_cur, n_q, jensen, see
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("jensen", [0, 1])
+@pytest.mark.parametrize("jensen", [0, 1, 2])
 def test_attention_chunk_small(bits, jensen):
     go, gl, oo, ol = _attention_case(bits, "bf16", 1, 2, 2, 128, appends=(200, 200), n_cur=100, n_q=150,
                                      jensen=jensen, seed=7)
@@ -120,9 +120,10 @@ def test_attention_chunk_small(bits, jensen):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-def test_attention_gqa_decode_splits(d):
+@pytest.mark.parametrize("jensen", [1, 2])
+def test_attention_gqa_decode_splits(d, jensen):
     """GQA decode: one query per head, rows packed per KV head, token splits + combine."""
-    go, gl, oo, ol = _attention_case(2, "bf16", 2, 8, 2, d, appends=(1500, 700), n_cur=0, n_q=1, jensen=1,
+    go, gl, oo, ol = _attention_case(2, "bf16", 2, 8, 2, d, appends=(1500, 700), n_cur=0, n_q=1, jensen=jensen,
                                      seed=11)
     assert np.abs(go - oo).max() <= TOL
     assert np.abs(gl - ol).max() <= TOL
@@ -150,7 +151,7 @@ def test_attention_bf16_output():
     assert np.all(np.abs(go - oo) <= TOL + bf16_half_ulp(oo))
 
 
-@pytest.mark.parametrize("jensen", [0, 1])
+@pytest.mark.parametrize("jensen", [0, 1, 2])
 def test_tiny_workload(jensen):
     w = workloads.WORKLOADS["tiny_int2_h1_d64"]
     data = workloads.generate(w)
