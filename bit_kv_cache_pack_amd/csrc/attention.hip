@@ -629,6 +629,10 @@ __device__ __forceinline__ void softmax_pv(Ctx<HD, BF16> &cx, const uint16_t *vl
     typedef Geo<HD> G;
     constexpr int DB = C::DB;
     const int lane = threadIdx.x % kWave, hh = lane / 32, l16 = lane % 16;
+    // The serial part (row maximum, rescale, first probabilities) runs at a raised wave
+    // priority, lowered before the products: the SIMD's other wave then issues around
+    // this chain rather than alongside it.
+    __builtin_amdgcn_s_setprio(1);
     // token of s[rb][j] = 32 rb + 8 (j / 4) + 4 hh + j % 4; tokens past len do not exist
     if (len < TT) {
 #pragma unroll
@@ -664,6 +668,7 @@ __device__ __forceinline__ void softmax_pv(Ctx<HD, BF16> &cx, const uint16_t *vl
     for (int db = 0; db < DB; ++db) va[0][db] = load_v_operand<HD>(vr, 0, db);
 #pragma unroll
     for (int k = 0; k < 4; ++k) exp_pair(s, 0, k, scale_log2, off, pv[0], ps);
+    __builtin_amdgcn_s_setprio(0);
 #pragma unroll
     for (int st = 0; st < 4; ++st) {
         const int c = st & 1, n = c ^ 1;
