@@ -16,6 +16,7 @@ kernel against the bf16 dense MFMA peak, its duration taken with HIP events reco
 the stream the kernels run on. ``cpu_baseline`` times the CPU oracle on a bounded sample.
 """
 import argparse
+import dataclasses
 import json
 import os
 import sys
@@ -200,7 +201,7 @@ def window_cpu_baseline(step: WindowStep):
                                  k_group_tokens=w.window, kgroup_capacity=max(len(groups), 1))
         oracle.append(seg, k, v, groups=np.asarray(groups, np.int32).reshape(-1, 2))
         segs.append(seg)
-    oracle.attention(step.data["q"].float().numpy(), segs, n_kv_heads=w.n_kv_heads, jensen=bool(w.jensen))
+    oracle.attention(step.data["q"].float().numpy(), segs, n_kv_heads=w.n_kv_heads, jensen=int(w.jensen))
     t = time.perf_counter() - t0
     return {"value": round(t * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
             "sample": "the whole step once: window scores and assignment, the three gathered appends "
@@ -237,7 +238,7 @@ def window_main(args, w: workloads.Workload) -> None:
                       "head_dim": w.head_dim, "cache_tokens": w.n_cache, "window": w.window,
                       "windows": w.n_windows, "fp16_int4_int2_windows": [step.n16, step.n4,
                                                                         w.n_windows - step.n16 - step.n4],
-                      "jensen": bool(w.jensen)},
+                      "jensen": int(w.jensen)},
            "stages_us": {k: round(v, 2) for k, v in med.items()},
            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                         "frac": round(gbps / PEAK_HBM_GBPS, 4), "traffic": None, "kernel": "attention_kernel",
@@ -302,7 +303,7 @@ def cpu_baseline(step: ChunkStep, target_s: float = 15.0):
     # calibrate: one row (the per-head dequantization of the history dominates) and 33 rows
     def timed(rows):
         t0 = time.perf_counter()
-        oracle.attention(q, [seg], kc, vc, n_kv_heads=w.n_kv_heads, jensen=bool(w.jensen), rows=rows)
+        oracle.attention(q, [seg], kc, vc, n_kv_heads=w.n_kv_heads, jensen=int(w.jensen), rows=rows)
         return time.perf_counter() - t0
     t1 = timed([0])
     t33 = timed(list(range(0, min(w.n_q, 33))))
@@ -366,6 +367,8 @@ def main():
     ap.add_argument("--no-probe-hbm", action="store_true",
                     help="skip the HBM read/copy probe (its copies would mix into a counter run's copy calibration)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
+    ap.add_argument("--jensen", type=int, choices=(0, 1, 2), default=None,
+                    help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic); default: the workload's")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the reference dispatch "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
@@ -380,6 +383,10 @@ def main():
     torch.cuda.set_device(0)
     kvq.lib()
     w = workloads.WORKLOADS[args.workload]
+    if args.jensen is not None:
+        w = dataclasses.replace(w, jensen=args.jensen)
+    # the stored counter summaries were taken in the workload's own Jensen mode
+    default_mode = w.jensen == workloads.WORKLOADS[args.workload].jensen
     if w.bits == 0:
         window_main(args, w)
         return
@@ -415,11 +422,11 @@ def main():
         alg = kvb + step.qo_bytes()
         ach = alg / (attn_avg * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": stored_traffic(w.name, "decode_kernel"),
+                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": stored_traffic(w.name, "decode_kernel") if default_mode else None,
                 "kernel": "decode_kernel"}
     else:
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(w.name, "attention_kernel"),
+                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(w.name, "attention_kernel") if default_mode else None,
                 "kernel": "attention_kernel"}
     res = {
         "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
@@ -428,7 +435,7 @@ def main():
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "cache_tokens": w.n_cache, "cur_tokens": w.n_cur, "queries": w.n_q,
                    "bits": w.bits, "k_group_tokens": w.k_group_tokens, "v_group_channels": w.v_group_channels,
-                   "jensen": bool(w.jensen), "cache_copies": copies},
+                   "jensen": int(w.jensen), "cache_copies": copies},
         "roofline": roof,
         "attention": {"ms": round(attn_avg, 4), "ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
                       "ms_p90": round(float(np.percentile(attn_ms, 90)), 4), "tflops": round(attn_tflops, 2),
