@@ -51,12 +51,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;  // log2 headroom before the running max is moved
 
 // Row strides (halves) chosen for the 64 LDS banks: key rows 68 dwords apart make the
-// 32 MFMA operand reads of a wave conflict-free; value rows 76 (HD 128) or 52 (HD 64)
-// dwords apart keep both the 16-byte stage writes and the 4-row transposed reads free of
-// conflicts.
+// 32 MFMA operand reads of a wave conflict-free; value rows 80 (HD 128) or 52 (HD 64)
+// dwords apart keep the 4-row transposed reads of each 32-lane half free of conflicts
+// (the 16-byte stage writes are, for any stride: each group of 8 lanes writes one row).
 template <int HD> struct Geo {
     static constexpr int KROW = HD + 8;
-    static constexpr int VROW = HD == 128 ? HD + 24 : HD + 40;
+    static constexpr int VROW = HD == 128 ? HD + 32 : HD + 40;
     static constexpr int KBUF = TT * KROW;
     static constexpr int VBUF = TT * VROW;
     static constexpr int BUF = KBUF + VBUF;   // halves per stage buffer
