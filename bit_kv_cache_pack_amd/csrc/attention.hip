@@ -897,7 +897,13 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
         float m[NP], l[NP];
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            const int64_t ww = min(w + k, w1);   // past w1: a repeat, skipped below
+            const int64_t ww = w + k;
+            if (ww > w1) {   // past the last piece (uniform over the workgroup): no load
+                o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+                m[k] = -__builtin_inff();
+                l[k] = 0.f;
+                continue;
+            }
             // the row block's piece in share ww is that share's first piece iff the share starts in it
             const float *pp = p.partial + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 4);
             o[k] = *reinterpret_cast<const f32x4 *>(pp + c);
@@ -906,7 +912,7 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
         }
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            if (w + k > w1 || m[k] == -__builtin_inff()) continue;   // a repeat, or a piece past the last token
+            if (m[k] == -__builtin_inff()) continue;   // past the last piece, or a piece past the last token
             const float mn = fmaxf(M, m[k]);
             const float sa = exp2f(M - mn), sb = exp2f(m[k] - mn);
             acc = acc * sa + o[k] * sb;
