@@ -867,11 +867,13 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 // Merge the pieces of the row blocks that the shares split. Job y (one per workgroup of
 // the attention launch) takes the row block holding position y quota if share y is the
 // first to start in it; the row block's pieces are in shares w0..w1. One pass over the
-// pieces with a running maximum; a thread merges 4 channels of one row (partial rows are
+// pieces with a running maximum; a thread merges 8 channels of one row (partial rows are
 // HD + 4 floats: O, then m and l, 16-byte aligned).
 template <int HD>
 __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
-    constexpr int TPR = HD / 4;     // threads per row
+    constexpr int CPT = 8;          // channels per thread
+    constexpr int NQ = CPT / 4;     // 16-byte loads per piece
+    constexpr int TPR = HD / CPT;   // threads per row
     constexpr int RPB = 256 / TPR;  // rows per block
     const int64_t U = p.quota, Np = p.tok_pad;
     const int64_t y = blockIdx.x;
@@ -879,7 +881,7 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     if ((rb * Np + U - 1) / U != y) return;
     const int64_t w0 = rb * Np / U, w1 = ((rb + 1) * Np - 1) / U;
     if (w1 == w0) return;
-    const int r = blockIdx.y * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * 4;
+    const int r = blockIdx.y * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * CPT;
     const int gqa = p.n_q_heads / p.n_kv_heads;
     const int rows = gqa * p.n_q;
     const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
@@ -888,25 +890,29 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
     const size_t qrow = ((size_t)b * p.n_q_heads + h * gqa + row / p.n_q) * p.n_q + row % p.n_q;
     float M = -__builtin_inff(), L = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
     // pieces in groups of 8 whose loads are in flight together (a row block of a few rows can
     // be cut into many pieces)
     constexpr int NP = 8;
     for (int64_t w = w0; w <= w1; w += NP) {
-        f32x4 o[NP];
+        f32x4 o[NP][NQ];
         float m[NP], l[NP];
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
             const int64_t ww = w + k;
             if (ww > w1) {   // past the last piece (uniform over the workgroup): no load
-                o[k] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int q = 0; q < NQ; ++q) o[k][q] = f32x4{0.f, 0.f, 0.f, 0.f};
                 m[k] = -__builtin_inff();
                 l[k] = 0.f;
                 continue;
             }
             // the row block's piece in share ww is that share's first piece iff the share starts in it
             const float *pp = p.partial + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 4);
-            o[k] = *reinterpret_cast<const f32x4 *>(pp + c);
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) o[k][q] = *reinterpret_cast<const f32x4 *>(pp + c + 4 * q);
             m[k] = pp[HD];
             l[k] = pp[HD + 1];
         }
@@ -915,22 +921,26 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
             if (m[k] == -__builtin_inff()) continue;   // past the last piece, or a piece past the last token
             const float mn = fmaxf(M, m[k]);
             const float sa = exp2f(M - mn), sb = exp2f(m[k] - mn);
-            acc = acc * sa + o[k] * sb;
+#pragma unroll
+            for (int q = 0; q < NQ; ++q) acc[q] = acc[q] * sa + o[k][q] * sb;
             L = L * sa + l[k] * sb;
             M = mn;
         }
     }
     const float inv = 1.0f / L;
-    const size_t o0 = qrow * HD + c;
-    if (p.out_dtype == DT_F32) {
-        *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + o0) = acc * inv;
-    } else {
-        uint16_t e[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            e[i] = p.out_dtype == DT_BF16 ? f32_to_bf16_bits(acc[i] * inv) : f32_to_f16_bits(acc[i] * inv);
-        *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.out) + o0) =
-            u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+    for (int q = 0; q < NQ; ++q) {
+        const size_t o0 = qrow * HD + c + 4 * q;
+        if (p.out_dtype == DT_F32) {
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + o0) = acc[q] * inv;
+        } else {
+            uint16_t e[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                e[i] = p.out_dtype == DT_BF16 ? f32_to_bf16_bits(acc[q][i] * inv) : f32_to_f16_bits(acc[q][i] * inv);
+            *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.out) + o0) =
+                u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
+        }
     }
     if (c == 0 && p.lse != nullptr) p.lse[qrow] = (M + __log2f(L)) * kLn2;
 }
@@ -963,7 +973,7 @@ hipError_t launch_t(const AttnParams &p, hipStream_t s) {
     hipLaunchKernelGGL((attention_kernel<HD, BF16>), dim3(n_wg), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.quota % p.tok_pad == 0) return e;   // no row block was split
-    hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / (HD / 4))), dim3(256), 0, s, p);
+    hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / (HD / 8))), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
