@@ -832,29 +832,56 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             far = fetch(++it + 2);
         }
 
-        // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4]
+        // epilogue: lane (query r32, half hh) holds O^T[position 32 db + 8 (j/4) + 4 hh + j%4].
+        // Each 32-channel block goes through the wave's Jensen table in LDS (free after the
+        // tile loop; the next piece's first packed tile rebuilds it), 32 rows x 32 channels
+        // with the 4-channel groups of row r at group g ^ (r % 8) (fewer bank conflicts on
+        // the column writes), and leaves as 16-byte row segments. The wave alone writes and
+        // reads its table; its LDS operations complete in order.
         const float lt = cx.l + other_half(cx.l);
-        if (row_ok && whole) {
-            const float inv = 1.0f / lt;
+        const float scale = whole ? 1.0f / lt : 1.0f;
+        float *lo = cx.btab;
+        // this lane's four chunks of a block: rows lane / 8 + 8 i, channels 4 (lane % 8) + 0..3
+        const int crow = lane / 8, c4 = 4 * (lane % 8);
+        const int c4s = c4 ^ (4 * (crow % 8));   // its position in the swizzled rows
+        size_t dst[4];
+        bool dst_ok[4];
 #pragma unroll
-            for (int db = 0; db < C::DB; ++db)
+        for (int i = 0; i < 4; ++i) {
+            const int rg = rbi * BM + wave * 32 + crow + 8 * i;
+            dst_ok[i] = rg < rows;
+            const int rgc = dst_ok[i] ? rg : 0;
+            dst[i] = whole ? ((size_t)b * p.n_q_heads + h * gqa + rgc / p.n_q) * p.n_q + rgc % p.n_q
+                           : ((size_t)blockIdx.x * 2 + pslot) * BM + (rgc - rbi * BM);
+        }
 #pragma unroll
-                for (int j = 0; j < 16; ++j) {
-                    const int ch = swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4));
-                    const float v = cx.o[db][j] * inv;
-                    if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + ch] = v;
-                    else if (p.out_dtype == DT_BF16) reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_bf16_bits(v);
-                    else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + ch] = f32_to_f16_bits(v);
+        for (int db = 0; db < C::DB; ++db) {
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+                lo[r32 * 32 + (swap_pos(8 * (j / 4) + 4 * hh + (j % 4)) ^ (4 * (r32 % 8)))] = cx.o[db][j] * scale;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const f32x4 v = *reinterpret_cast<const f32x4 *>(lo + (crow + 8 * i) * 32 + c4s);
+                if (!dst_ok[i]) continue;
+                const int ch = 32 * db + c4;
+                if (!whole) {
+                    *reinterpret_cast<f32x4 *>(p.partial + dst[i] * (HD + 4) + ch) = v;
+                } else if (p.out_dtype == DT_F32) {
+                    *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + dst[i] * HD + ch) = v;
+                } else {
+                    uint16_t e[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t) e[t] = p.out_dtype == DT_BF16 ? f32_to_bf16_bits(v[t]) : f32_to_f16_bits(v[t]);
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.out) + dst[i] * HD + ch) =
+                        u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
                 }
-            if (p.lse != nullptr && hh == 0) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
-        } else if (row_ok) {
-            float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 4);
-#pragma unroll
-            for (int db = 0; db < C::DB; ++db)
-#pragma unroll
-                for (int j = 0; j < 16; ++j)
-                    pp[swap_pos(32 * db + 8 * (j / 4) + 4 * hh + (j % 4))] = cx.o[db][j];
-            if (hh == 0) {
+            }
+        }
+        if (row_ok && hh == 0) {
+            if (whole) {
+                if (p.lse != nullptr) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
+            } else {
+                float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 4);
                 pp[HD] = cx.m;
                 pp[HD + 1] = lt;
             }
