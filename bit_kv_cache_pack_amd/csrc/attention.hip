@@ -972,20 +972,39 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     if (c == 0 && p.lse != nullptr) p.lse[qrow] = (M + __log2f(L)) * kLn2;
 }
 
-// Merge token splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s.
+// Merge token splits: O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s, in one pass with a
+// running maximum over splits taken eight at a time (their loads in flight together).
 template <int HD>
 __global__ __launch_bounds__(HD) void combine_kernel(AttnParams p) {
     const size_t row = blockIdx.x;
     const size_t n_rows_total = (size_t)p.batch * p.n_q_heads * p.n_q;
     const int c = threadIdx.x;
-    float M = -__builtin_inff();
-    for (int s = 0; s < p.n_split; ++s) M = fmaxf(M, p.partial[((size_t)s * n_rows_total + row) * (HD + 2) + HD]);
-    float L = 0.f, acc = 0.f;
-    for (int s = 0; s < p.n_split; ++s) {
-        const float *pp = p.partial + ((size_t)s * n_rows_total + row) * (HD + 2);
-        const float w = exp2f(pp[HD] - M);
-        L = fmaf(w, pp[HD + 1], L);
-        acc = fmaf(w, pp[c], acc);
+    constexpr int NP = 8;
+    float M = -__builtin_inff(), L = 0.f, acc = 0.f;
+    for (int s0 = 0; s0 < p.n_split; s0 += NP) {
+        float o[NP], m[NP], l[NP];
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            if (s0 + k >= p.n_split) {   // uniform: past the last split
+                o[k] = 0.f;
+                m[k] = -__builtin_inff();
+                l[k] = 0.f;
+                continue;
+            }
+            const float *pp = p.partial + ((size_t)(s0 + k) * n_rows_total + row) * (HD + 2);
+            o[k] = pp[c];
+            m[k] = pp[HD];
+            l[k] = pp[HD + 1];
+        }
+#pragma unroll
+        for (int k = 0; k < NP; ++k) {
+            if (m[k] == -__builtin_inff()) continue;   // past the last split, or a split with no tokens
+            const float mn = fmaxf(M, m[k]);
+            const float sa = exp2f(M - mn), sb = exp2f(m[k] - mn);
+            acc = acc * sa + o[k] * sb;
+            L = L * sa + l[k] * sb;
+            M = mn;
+        }
     }
     const float v = acc / L;
     if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[row * HD + c] = v;
