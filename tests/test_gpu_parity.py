@@ -151,6 +151,20 @@ def test_attention_bf16_output():
     assert np.all(np.abs(go - oo) <= TOL + bf16_half_ulp(oo))
 
 
+@pytest.mark.parametrize("out_dtype", [torch.bfloat16, torch.float16])
+def test_attention_whole_row_blocks_half_outputs(out_dtype):
+    """256 row blocks over a short history: on a 256-CU part each workgroup takes one whole
+    row block and writes the final 2-byte output itself (no piece merge)."""
+    go, gl, oo, ol = _attention_case(2, "bf16", 1, 1, 1, 64, appends=(64,), n_cur=16, n_q=256 * 256, jensen=1,
+                                     seed=23, out_dtype=out_dtype)
+    if out_dtype == torch.bfloat16:
+        half_ulp = bf16_half_ulp(oo)
+    else:
+        half_ulp = np.spacing(np.abs(oo).astype(np.float16)).astype(np.float64) / 2
+    assert np.all(np.abs(go - oo) <= TOL + half_ulp)
+    assert np.abs(gl - ol).max() <= TOL
+
+
 @pytest.mark.parametrize("jensen", [0, 1, 2])
 def test_tiny_workload(jensen):
     w = workloads.WORKLOADS["tiny_int2_h1_d64"]
