@@ -695,7 +695,8 @@ __device__ __forceinline__ void softmax_pv(Ctx<HD, BF16> &cx, const uint16_t *vl
 #pragma unroll
         for (int db = 0; db < DB; ++db) {
             __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-            if (st < 3) __builtin_amdgcn_sched_group_barrier(kSchedValu, 24 / DB, 0);
+            // 4 vector instructions per product (HD 128): 6 or 8 measured slower on the long rollout
+            if (st < 3) __builtin_amdgcn_sched_group_barrier(kSchedValu, 16 / DB, 0);
         }
     }
     __builtin_amdgcn_sched_barrier(0);
