@@ -34,9 +34,12 @@
 // fp16 step/zero directly in mixed-precision fused multiply-adds.
 // The Jensen terms of 32 consecutive K-groups are computed at once as a small matrix
 // product (step^2 x q^2, each split into bf16 high and low parts, three MFMAs per
-// k-step) and read back per group.
-// A row block cut between workgroups leaves unnormalized partials in the workspace, and
-// a combine kernel merges them by log-sum-exp.
+// k-step) and read back per group; the isotropic form feeds the group's channel mean of
+// step^2 to the same product.
+// The serial part of each tile's softmax runs at a raised wave priority, so that the
+// other wave of the SIMD issues around it. A piece's output leaves through the wave's
+// table in LDS as 16-byte row segments: the final output for a whole row block, otherwise
+// unnormalized partials in the workspace, which a combine kernel merges by log-sum-exp.
 #include "kvq_internal.h"
 #include "kvq_tile.cuh"
 
