@@ -75,14 +75,13 @@ def _declare(L):
     L.orc_window_scores.restype = None
     L.orc_assign_windows.argtypes = [P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
     L.orc_assign_windows.restype = ctypes.c_int
+    L.orc_window_groups.argtypes = [P, P, ctypes.c_int, ctypes.c_int, ctypes.c_int, P, P]
+    L.orc_window_groups.restype = None
     L.orc_window_budget.argtypes = [ctypes.c_int] * 3 + [P, P]
     L.orc_window_budget.restype = None
     for n in ("orc_f32_to_f16_n", "orc_f32_to_bf16_n", "orc_f16_to_f64_n"):
         getattr(L, n).argtypes = [P, I64, P]
         getattr(L, n).restype = None
-    L.orc_dequant_segment.argtypes = [ctypes.POINTER(OrcSegment), ctypes.c_int, ctypes.c_int,
-                                      ctypes.c_int, P, P]
-    L.orc_dequant_segment.restype = None
 
 
 def _ptr(a: Optional[np.ndarray]):
@@ -199,16 +198,6 @@ def _orc_seg(seg: Dict) -> OrcSegment:
                       _ptr(seg.get("v_raw")))
 
 
-def dequant_segment(seg: Dict, b: int = 0, h: int = 0, exact: bool = False):
-    """Dense K, V [n_tokens][d] (float64) of one (batch, head) of a segment, cache order."""
-    n, d = seg["n_tokens"], seg["d"]
-    K = np.zeros((max(n, 1), d), np.float64)
-    V = np.zeros((max(n, 1), d), np.float64)
-    sg = _orc_seg(seg)
-    lib().orc_dequant_segment(ctypes.byref(sg), d, b * seg["H"] + h, int(exact), _ptr(K), _ptr(V))
-    return K[:n], V[:n]
-
-
 # -------------------------------------------------------------------- attention
 def attention(q: np.ndarray, segs: List[Dict], k_cur: Optional[np.ndarray] = None,
               v_cur: Optional[np.ndarray] = None, n_kv_heads: Optional[int] = None,
@@ -283,3 +272,15 @@ def window_budget(n_windows: int, pct_fp16: int, pct_int4: int):
     a, b = ctypes.c_int(), ctypes.c_int()
     lib().orc_window_budget(n_windows, pct_fp16, pct_int4, ctypes.byref(a), ctypes.byref(b))
     return a.value, b.value
+
+
+def window_groups(bits: np.ndarray, order: np.ndarray, n_tokens: int, window: int = 32):
+    """A6: gather lists in grouped order (int32 [W][2]: first token, length) and the token
+    counts of the FP16, INT4 and INT2 classes."""
+    bits = _c(bits, np.int8)
+    order = _c(order, np.int32)
+    W = bits.size
+    groups = np.zeros((W, 2), np.int32)
+    ct = np.zeros(3, np.int32)
+    lib().orc_window_groups(_ptr(bits), _ptr(order), W, int(n_tokens), int(window), _ptr(groups), _ptr(ct))
+    return groups, ct

@@ -531,6 +531,26 @@ int orc_assign_windows(const double *score, int W, int n_fp16, int n_int4, int8_
     return 0;
 }
 
+/* A6: the grouped layout's gather lists [WQ "技術的に面白い点": windows of one bit-width
+ * are stored together]. Row i of groups is {first token, length} of window order[i], so
+ * the FP16, INT4 and INT2 lists follow one another in the order assign_windows makes;
+ * class_tokens holds the tokens of the FP16, INT4 and INT2 windows (the last window may
+ * be short). */
+void orc_window_groups(const int8_t *bits, const int32_t *order, int W, int N, int window,
+                       int32_t *groups, int32_t *class_tokens)
+{
+    class_tokens[0] = class_tokens[1] = class_tokens[2] = 0;
+    for (int i = 0; i < W; ++i) {
+        const int w = order[i];
+        const int start = w * window;
+        const int len = (start + window <= N) ? window : N - start;
+        groups[2 * i] = start;
+        groups[2 * i + 1] = len;
+        const int k = bits[w] == 16 ? 0 : (bits[w] == 4 ? 1 : 2);
+        class_tokens[k] += len;
+    }
+}
+
 /* FP16 and INT4 window counts from percentages: floor over all W in integer
  * arithmetic, window 0 counted within the FP16 share, at least one FP16 window. */
 void orc_window_budget(int W, int pct_fp16, int pct_int4, int *n_fp16, int *n_int4)
@@ -562,34 +582,4 @@ void orc_f16_to_f64_n(const uint16_t *h, int64_t n, double *out)
 {
     for (int64_t i = 0; i < n; ++i)
         out[i] = orc_f16_to_f64(h[i]);
-}
-
-/* Dequantize a whole packed segment of one (batch, head) into dense float rows,
- * in cache order: K [n_tokens][d], V [n_tokens][d] (A1 spec values, or exact). */
-void orc_dequant_segment(const orc_segment *sg, int d, int bh, int exact, double *K, double *V)
-{
-    const size_t row0 = (size_t)bh * sg->capacity;
-    if (sg->bits == 16) {
-        for (int t = 0; t < sg->n_tokens; ++t)
-            for (int c = 0; c < d; ++c) {
-                uint16_t kb = sg->k_raw[(row0 + t) * d + c], vb = sg->v_raw[(row0 + t) * d + c];
-                K[(size_t)t * d + c] = sg->elem_dtype == ORC_F16 ? orc_f16_to_f64(kb) : orc_bf16_to_f32(kb);
-                V[(size_t)t * d + c] = sg->elem_dtype == ORC_F16 ? orc_f16_to_f64(vb) : orc_bf16_to_f32(vb);
-            }
-        return;
-    }
-    const int wpr = d * sg->bits / 32, Gv = sg->v_group_channels;
-    uint8_t kc[256], vc[256];
-    for (int g = 0; g < sg->n_kgroups; ++g) {
-        const uint16_t *km = sg->k_meta + ((size_t)bh * sg->kgroup_capacity + (size_t)g) * d * 2;
-        for (int t = sg->kgroup_start[g]; t < sg->kgroup_start[g + 1]; ++t) {
-            orc_unpack_row(sg->k_codes + (row0 + t) * wpr, d, sg->bits, kc);
-            orc_unpack_row(sg->v_codes + (row0 + t) * wpr, d, sg->bits, vc);
-            for (int c = 0; c < d; ++c) {
-                const uint16_t *vm = sg->v_meta + ((row0 + t) * (d / Gv) + c / Gv) * 2;
-                K[(size_t)t * d + c] = orc_dequant(kc[c], km[2 * c], km[2 * c + 1], sg->elem_dtype, exact);
-                V[(size_t)t * d + c] = orc_dequant(vc[c], vm[0], vm[1], sg->elem_dtype, exact);
-            }
-        }
-    }
 }

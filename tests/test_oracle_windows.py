@@ -94,3 +94,32 @@ def test_zero_vectors_score_zero(orc):
     s = orc.window_scores(K, text, 32)
     assert s[0] == 0.0 and s[1] == pytest.approx(1.0, abs=1e-15)
     assert np.all(orc.window_scores(K, np.zeros(64, np.float32), 32) == 0.0)
+
+
+def test_grouped_layout_lists(orc):
+    """A6: the gather lists cover every token exactly once, FP16 windows first, then INT4,
+    then INT2, ascending inside each class; the short last window counts its own length;
+    the class token counts add up to N. Hand case: 5 windows of 4 tokens over N = 18."""
+    bits = np.array([16, 2, 4, 16, 2], np.int8)
+    order = np.array([0, 3, 2, 1, 4], np.int32)
+    groups, ct = orc.window_groups(bits, order, 18, 4)
+    assert groups.tolist() == [[0, 4], [12, 4], [8, 4], [4, 4], [16, 2]]
+    assert ct.tolist() == [8, 4, 6]
+    rng = np.random.default_rng(7)
+    for N in (19600, 19599, 32, 33):
+        W = -(-N // 32)
+        score = rng.standard_normal(W)
+        n16, n4 = orc.window_budget(W, 10, 30)
+        b, o = orc.assign_windows(score, n16, n4)
+        g, ct = orc.window_groups(b, o, N, 32)
+        covered = np.zeros(N, np.int32)
+        for s0, ln in g:
+            covered[s0:s0 + ln] += 1
+        assert np.all(covered == 1)
+        assert ct.sum() == N
+        bounds = np.cumsum([0, n16, n4, W - n16 - n4])
+        for k, cls in enumerate((16, 4, 2)):
+            rows = g[bounds[k]:bounds[k + 1]]
+            assert np.all(np.diff(rows[:, 0]) > 0)
+            assert np.all(b[rows[:, 0] // 32] == cls)
+            assert rows[:, 1].sum() == ct[k]
