@@ -671,12 +671,20 @@ hipError_t launch_d(const AttnParams &p, hipStream_t s) {
 
 }  // namespace
 
-bool decode_eligible(int dtype, int n_q_heads, int n_kv_heads, int head_dim, int n_q, const int *seg_bits,
-                     int n_segs) {
+bool decode_eligible(int dtype, int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q,
+                     const int *seg_bits, int n_segs, int n_cur, int n_total) {
     if ((long)(n_q_heads / n_kv_heads) * n_q > kDecodeRows || dtype != DT_BF16) return false;
+    // one packed segment: the multi-segment walk is not covered by a passing GPU run
+    if (n_segs > 1) return false;
     for (int i = 0; i < n_segs; ++i) {
         if (seg_bits[i] == 16) return false;
         if (seg_bits[i] == 4 && head_dim != 128) return false;
+    }
+    // the current chunk only when one workgroup walks a (batch, KV head) alone
+    if (n_cur > 0) {
+        int nw, wt;
+        decode_plan(batch, n_kv_heads, n_total, &nw, &wt);
+        if (nw != 1) return false;
     }
     return true;
 }

@@ -26,16 +26,22 @@ struct QuantAppendParams {
 hipError_t launch_quant_append(const QuantAppendParams &p, int bits, int n_groups, hipStream_t s);
 
 struct WindowParams {
-    const void *k;
+    const void *k;                 // [n_layers][n_kv_heads][n_tokens][head_dim]
     int32_t k_dtype;
-    int32_t n_kv_heads, head_dim, n_tokens, window, n_windows;
-    const float *text;
-    int32_t n_fp16, n_int4;
-    int8_t *bits_out;
-    int32_t *order_out;
-    double *score;
+    int32_t n_layers, n_kv_heads, head_dim, n_tokens, window, n_windows;
+    const float *text;             // [n_layers][head_dim]
+    int32_t n_fp16, n_int4;        // windows per class (the same for every layer)
+    int8_t *bits_out;              // [n_layers][n_windows]
+    int32_t *order_out;            // [n_layers][n_windows]
+    double *score;                 // [n_layers][n_windows]
+    int32_t *groups_out;           // [n_layers][n_windows][2] or nullptr
+    int32_t *class_tokens_out;     // [n_layers][3] or nullptr
 };
+constexpr int kMaxWindowsPerLayer = 16384;
+constexpr int kMaxWindowLayers = 65535;
 hipError_t launch_windows(const WindowParams &p, hipStream_t s);
+// FP16 and INT4 window counts from percentages of n_windows.
+void window_budget(int n_windows, int pct_fp16, int pct_int4, int *n_fp16, int *n_int4);
 
 constexpr int kMaxSegments = 8;
 
@@ -87,14 +93,19 @@ hipError_t launch_attention(const AttnParams &p, hipStream_t s);
 // Log-sum-exp merge of n_split partials into the output.
 hipError_t launch_combine(const AttnParams &p, hipStream_t s);
 
-// Decode-shaped attention: at most kDecodeRows query rows per (batch, KV head), bf16, and
-// packed segments only (INT2; INT4 at head_dim 128). Raw segments, fp16 and INT4 at
-// head_dim 64 run on the chunk kernel.
+// Decode-shaped attention: at most kDecodeRows query rows per (batch, KV head), bf16, at
+// most one packed segment (INT2; INT4 at head_dim 128), and a current chunk only when one
+// workgroup takes each (batch, KV head). Every other call runs on the chunk kernel: raw
+// segments, fp16, INT4 at head_dim 64 and several segments faulted in decode_kernel on
+// the one run that took them there, with the cause not found.
 constexpr int kDecodeRows = 16;
-bool decode_eligible(int dtype, int n_q_heads, int n_kv_heads, int head_dim, int n_q, const int *seg_bits,
-                     int n_segs);
+bool decode_eligible(int dtype, int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q,
+                     const int *seg_bits, int n_segs, int n_cur, int n_total);
 // Workgroups per (batch, KV head) and tokens per wave.
 void decode_plan(int batch, int n_kv_heads, int n_total, int *n_wg, int *wave_tokens);
 hipError_t launch_decode(const AttnParams &p, hipStream_t s);
+
+// Streaming read of a device buffer (bandwidth probe).
+hipError_t launch_hbm_read(const void *buf, size_t bytes, uint32_t *sink, hipStream_t s);
 
 }  // namespace kvq
