@@ -1,19 +1,24 @@
 """Benchmark: fused INT2-KV chunk attention (TFLOP/s, effective KV GB/s vs MI355X peaks).
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-extra]
+                    [--no-cpu-baseline]
 
-Default workload: the video-diffusion chunk step -- batch 1, 12 heads, head_dim 128, an
-INT2 cache of 18,720 tokens (4 appends of one 4,680-token chunk, K groups of 128 tokens,
-V groups of 32 channels) and an unquantized current chunk of 4,680 tokens that is both the
-queries and the current keys/values. One step = the fused attention with the Jensen
-correction, then the quantize-append of the current chunk into the cache (the descriptor
-is rewound after each step, so every step does identical work). Inputs are seeded
-synthetic tensors already resident in HBM when timing starts.
+Default workload: the long-rollout chunk step -- batch 1, 40 heads, head_dim 128, an INT2
+cache of 74,880 tokens (16 appends of one 4,680-token chunk of 3 latent frames, K groups of
+128 tokens, V groups of 32 channels, keys drifting per frame) and an unquantized current
+chunk of 4,680 tokens that is both the queries and the current keys/values. One step = the
+fused attention with the Jensen correction, then the quantize-append of the current chunk
+into the cache, back to back (the descriptor is rewound after each step, so every step does
+identical work). Inputs are seeded synthetic tensors already resident in HBM when timing
+starts.
 
 One JSON line on stdout. ``value`` = attention FLOPs per step (4 * B * Hq * Nq * (N_cache +
 N_cur) * d, the dense QK^T and PV products) / step time. ``roofline`` is the attention
 kernel against the bf16 dense MFMA peak, its duration taken with HIP events recorded on
-the stream the kernels run on. ``cpu_baseline`` times the CPU oracle on a bounded sample.
+the stream the kernels run on. ``configs`` holds the same record for the video chunk step
+and the two decode-shaped caches (INT2, INT4; rated in GB/s of algorithmic bytes against
+HBM), each timed the same way. ``cpu_baseline`` times the CPU oracle on a bounded sample
+of the headline workload; ``probe_hbm`` the library's streaming-read probe and a copy.
 """
 import argparse
 import dataclasses
@@ -119,9 +124,10 @@ class ChunkStep:
 
 
 class WindowStep:
-    """WindowQuant, one step: window scores and the FP16/INT4/INT2 assignment on the GPU, the
-    per-class gather lists on the host (bits and order come back), the three grouped segments
-    rebuilt by gathered appends, then the decode attention over them."""
+    """WindowQuant, one step: window scores, the FP16/INT4/INT2 assignment and the grouped
+    layout's gather lists on the GPU; the three class token counts come back to size the
+    appends (12 bytes); the three grouped segments rebuilt by gathered appends from the
+    device lists; then the decode attention over them."""
 
     def __init__(self, w: workloads.Workload):
         self.w = w
@@ -132,17 +138,19 @@ class WindowStep:
         self.v = data["cache_v"].cuda()
         self.text = data["text"].cuda()
         self.q = data["q"].cuda()
-        self.n16, self.n4 = kvq.window_budget(w.n_windows, w.pct_fp16, w.pct_int4)
-        bits, order, _ = kvq.assign_windows(self.k[0], self.text, self.n16, self.n4, window=w.window)
-        classes = kvq.window_groups(order.cpu().tolist(), bits.cpu().tolist(), w.n_cache, w.window)
+        self.asg = kvq.assign_windows(self.k, self.text, w.pct_fp16, w.pct_int4, window=w.window)
+        self.n16, self.n4 = self.asg.n_fp16, self.asg.n_int4
+        self.class_tokens = torch.empty(3, dtype=torch.int32, pin_memory=True)
+        self.class_tokens.copy_(self.asg.class_tokens[0])
         dt = workloads.DTYPES[w.dtype]
+        rows = self.asg.class_rows()
         self.segs = []
         self.tokens = {}
-        for b in (16, 4, 2):
-            groups, n_tok = classes[b]
+        for k, b in enumerate((16, 4, 2)):
+            n_tok = int(self.class_tokens[k])
             self.tokens[b] = n_tok
-            self.segs.append(kvq.Segment(b, dt, 1, w.n_kv_heads, w.head_dim, n_tok, k_group_tokens=w.window,
-                                         kgroup_capacity=max(len(groups), 1)))
+            self.segs.append(kvq.Segment(b, dt, 1, w.n_kv_heads, w.head_dim, w.window * (rows[b][1] - rows[b][0]),
+                                         k_group_tokens=w.window, kgroup_capacity=max(rows[b][1] - rows[b][0], 1)))
         self.out = torch.empty(self.q.shape, dtype=torch.float32, device="cuda")
         self.ws = None   # sized on the first run, once the segments hold tokens
 
@@ -161,16 +169,17 @@ class WindowStep:
         w = self.w
         if ev is not None:
             ev[0].record()
-        bits, order, _ = kvq.assign_windows(self.k[0], self.text, self.n16, self.n4, window=w.window)
+        kvq.assign_windows(self.k, self.text, w.pct_fp16, w.pct_int4, window=w.window, out=self.asg)
         if ev is not None:
             ev[1].record()
-        classes = kvq.window_groups(order.cpu().tolist(), bits.cpu().tolist(), w.n_cache, w.window)
-        lists = [(torch.from_numpy(classes[b][0]).cuda(), classes[b][1]) for b in (16, 4, 2)]
+        # the appends' token counts: the only host-side step (a 12-byte copy back)
+        self.class_tokens.copy_(self.asg.class_tokens[0])
         if ev is not None:
             ev[2].record()
-        for seg, (lst, n_new) in zip(self.segs, lists):
+        for k, (seg, b) in enumerate(zip(self.segs, (16, 4, 2))):
             seg.reset()
-            kvq.quantize_append(seg, self.k, self.v, n_new=n_new, src_groups=lst)
+            kvq.quantize_append(seg, self.k, self.v, n_new=int(self.class_tokens[k]),
+                                src_groups=self.asg.class_list(b))
         if ev is not None:
             ev[3].record()
         if self.ws is None:
@@ -192,18 +201,21 @@ def window_cpu_baseline(step: WindowStep):
     v = step.data["cache_v"].float().numpy()
     t0 = time.perf_counter()
     score = oracle.window_scores(k[0], step.data["text"].numpy(), w.window)
-    bits, order = oracle.assign_windows(score, step.n16, step.n4)
+    n16, n4 = oracle.window_budget(w.n_windows, w.pct_fp16, w.pct_int4)
+    bits, order = oracle.assign_windows(score, n16, n4)
+    groups, class_tokens = oracle.window_groups(bits, order, w.n_cache, w.window)
+    bounds = [0, n16, n16 + n4, w.n_windows]
     segs = []
-    for b in (16, 4, 2):
-        groups = [(int(x) * w.window, min(w.window, w.n_cache - int(x) * w.window)) for x in order if bits[x] == b]
-        n_tok = sum(g[1] for g in groups)
-        seg = oracle.new_segment(b, w.dtype, 1, w.n_kv_heads, w.head_dim, capacity=max(n_tok, 1),
-                                 k_group_tokens=w.window, kgroup_capacity=max(len(groups), 1))
-        oracle.append(seg, k, v, groups=np.asarray(groups, np.int32).reshape(-1, 2))
+    for k_, b in enumerate((16, 4, 2)):
+        lst = groups[bounds[k_]:bounds[k_ + 1]]
+        seg = oracle.new_segment(b, w.dtype, 1, w.n_kv_heads, w.head_dim, capacity=max(int(class_tokens[k_]), 1),
+                                 k_group_tokens=w.window, kgroup_capacity=max(len(lst), 1))
+        if len(lst):
+            oracle.append(seg, k, v, groups=lst)
         segs.append(seg)
     oracle.attention(step.data["q"].float().numpy(), segs, n_kv_heads=w.n_kv_heads, jensen=int(w.jensen))
     t = time.perf_counter() - t0
-    return {"value": round(t * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle",
+    return {"value": round(t * 1e6, 1), "unit": "us", "cores": threads, "kind": "oracle", "host": host_cpu(),
             "sample": "the whole step once: window scores and assignment, the three gathered appends "
                       "(%d FP16 / %d INT4 / %d INT2 windows) and the attention of all %d query rows"
                       % (step.n16, step.n4, w.n_windows - step.n16 - step.n4, w.n_q_heads * w.n_q)}
@@ -220,10 +232,10 @@ def window_main(args, w: workloads.Workload) -> None:
         step.run(evs[i])
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / args.steps
-    st = {k: [] for k in ("assign", "host_lists", "appends", "attention")}
+    st = {k: [] for k in ("assign", "class_tokens_copy", "appends", "attention")}
     for e in evs:
         st["assign"].append(e[0].elapsed_time(e[1]) * 1e3)
-        st["host_lists"].append(e[1].elapsed_time(e[2]) * 1e3)
+        st["class_tokens_copy"].append(e[1].elapsed_time(e[2]) * 1e3)
         st["appends"].append(e[2].elapsed_time(e[3]) * 1e3)
         st["attention"].append(e[3].elapsed_time(e[4]) * 1e3)
     med = {k: float(np.median(v)) for k, v in st.items()}
@@ -324,6 +336,7 @@ def cpu_baseline(step: ChunkStep, target_s: float = 15.0):
     t_rows = max(t_attn - fixed, 1e-9)
     t_step = fixed + t_rows / frac + t_app
     return {"value": round(step.flops() / t_step / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "host": host_cpu(),
             "sample": "attention of every %d-th query row (%d of %d per head, all %d heads) over the full "
                       "%d-token history (%.1f s, of which %.1f s dequantizes the history once), rows scaled "
                       "to all %d; quantize-append of the %d-token chunk in full (%.1f s)"
@@ -333,17 +346,20 @@ def cpu_baseline(step: ChunkStep, target_s: float = 15.0):
 
 
 def probe_hbm(mib=2048, reps=5):
-    """Measured HBM bandwidth of this device, for context beside the published peak: a sum
-    over a 2 GiB buffer (reads) and a copy of 1 GiB (reads + writes), best of a few runs,
-    timed with events on the current stream. Buffers exceed the last-level cache."""
+    """Measured HBM bandwidth of this device, for context beside the published peak: the
+    library's streaming-read probe (kvq_probe_hbm_read: 16-byte loads, each byte read once)
+    over a 2 GiB buffer, and a device copy of 1 GiB (reads + writes), best of a few runs,
+    timed with events on the current stream. Both buffers exceed the 256 MB last-level
+    cache several times over."""
     n = (mib << 20) // 4
     x = torch.ones(n, dtype=torch.float32, device="cuda")
     y = torch.empty(n // 2, dtype=torch.float32, device="cuda")
+    sink = torch.zeros(1, dtype=torch.int32, device="cuda")
     best_read = best_copy = float("inf")
     for _ in range(reps):
         e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
         e[0].record()
-        x.sum()
+        kvq.probe_hbm_read(x, sink)
         e[1].record()
         y.copy_(x[: n // 2])
         e[2].record()
@@ -354,49 +370,30 @@ def probe_hbm(mib=2048, reps=5):
     copy_gbps = (n // 2 * 4 * 2) / (best_copy * 1e-3) / 1e9
     del x, y
     return {"read_gbps": round(read_gbps, 1), "copy_gbps": round(copy_gbps, 1), "buffer_mib": mib,
-            "note": "torch sum (read) and copy (read + write), best of %d" % reps}
+            "note": "kvq_probe_hbm_read streaming read, and a torch device copy (read + write), best of %d" % reps}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="video_chunk_int2_h12_d128", choices=sorted(workloads.WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-probe-hbm", action="store_true",
-                    help="skip the HBM read/copy probe (its copies would mix into a counter run's copy calibration)")
-    ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
-    ap.add_argument("--jensen", type=int, choices=(0, 1, 2), default=None,
-                    help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic); default: the workload's")
-    ap.add_argument("--probe-copy-mib", type=int, default=0,
-                    help="after timing, run one plain device copy of this many MiB (the reference dispatch "
-                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
-              file=sys.stderr)
-        sys.exit(2)
-    if not torch.cuda.is_available():
-        print("bench.py needs a GPU", file=sys.stderr)
-        sys.exit(2)
-    torch.cuda.set_device(0)
-    kvq.lib()
-    w = workloads.WORKLOADS[args.workload]
-    if args.jensen is not None:
-        w = dataclasses.replace(w, jensen=args.jensen)
-    # the stored counter summaries were taken in the workload's own Jensen mode
-    default_mode = w.jensen == workloads.WORKLOADS[args.workload].jensen
-    if w.bits == 0:
-        window_main(args, w)
-        return
+def host_cpu():
+    """The host CPU as /proc/cpuinfo names it, and the thread settings the oracle runs under."""
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+
+
+def measure_chunk(args, w: workloads.Workload, copies: int = 0):
+    """Warm-ups, then exactly args.steps timed steps between device synchronizations; returns
+    the config's record (step time, value, roofline of the attention) and the step."""
     # decode caches can sit in the 256 MB last-level cache: rotate copies > 2x that size
-    copies = args.copies
     if copies == 0:
         copies = 1 if w.n_cur else 4
     step = ChunkStep(w, n_copies=copies)
-    log("cache built: %d tokens, %d K-groups per head, %d copies" % (step.base[0], step.base[1], copies))
-
+    log("%s: cache built, %d tokens, %d K-groups per head, %d copies" % (w.name, step.base[0], step.base[1], copies))
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
@@ -412,38 +409,130 @@ def main():
     app_ms = [e[1].elapsed_time(e[2]) for e in evs]
     attn_avg = float(np.mean(attn_ms))
     app_avg = float(np.mean(app_ms))
-
+    default_mode = w.jensen == workloads.WORKLOADS[w.name].jensen   # stored counters: the workload's mode
     flops = step.flops()
     kvb = step.kv_bytes()
-    value = flops / (ms_step * 1e-3) / 1e12
     attn_tflops = flops / (attn_avg * 1e-3) / 1e12
     decode = w.n_cur == 0
     if decode:
         alg = kvb + step.qo_bytes()
         ach = alg / (attn_avg * 1e-3) / 1e9
+        kernel = "decode_kernel"
         roof = {"bound": "hbm", "achieved": round(ach, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                "frac": round(ach / PEAK_HBM_GBPS, 4), "traffic": stored_traffic(w.name, "decode_kernel") if default_mode else None,
-                "kernel": "decode_kernel"}
+                "frac": round(ach / PEAK_HBM_GBPS, 4),
+                "traffic": stored_traffic(w.name, kernel) if default_mode else None, "kernel": kernel,
+                "algorithmic_bytes": alg}
+        value, unit = alg / (ms_step * 1e-3) / 1e9, "GB/s"
     else:
+        kernel = "attention_kernel"
         roof = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": stored_traffic(w.name, "attention_kernel") if default_mode else None,
-                "kernel": "attention_kernel"}
-    res = {
-        "metric": METRIC, "value": round(value, 3), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+                "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": stored_traffic(w.name, kernel) if default_mode else None, "kernel": kernel,
+                "algorithmic_flops": flops}
+        value, unit = flops / (ms_step * 1e-3) / 1e12, "TFLOP/s"
+    rec = {
+        "workload": w.name, "value": round(value, 3), "unit": unit, "ms_per_step": round(ms_step, 4),
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "cache_tokens": w.n_cache, "cur_tokens": w.n_cur, "queries": w.n_q,
                    "bits": w.bits, "k_group_tokens": w.k_group_tokens, "v_group_channels": w.v_group_channels,
                    "jensen": int(w.jensen), "cache_copies": copies},
         "roofline": roof,
-        "attention": {"ms": round(attn_avg, 4), "ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
+        "attention": {"ms": round(attn_avg, 4), "ms_median": round(float(np.median(attn_ms)), 4),
+                      "ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
                       "ms_p90": round(float(np.percentile(attn_ms, 90)), 4), "tflops": round(attn_tflops, 2),
-                      "kv_gbps": round(kvb / (attn_avg * 1e-3) / 1e9, 1),
-                      "kv_bytes": kvb, "flops": flops},
-        "append": {"ms": round(app_avg, 4), "bytes": step.append_bytes(),
-                   "gbps": round(step.append_bytes() / (app_avg * 1e-3) / 1e9, 1) if step.append else None},
+                      "kv_gbps": round(kvb / (attn_avg * 1e-3) / 1e9, 1), "kv_bytes": kvb, "flops": flops},
+        "append": {"ms": round(app_avg, 4), "ms_median": round(float(np.median(app_ms)), 4),
+                   "bytes": step.append_bytes(),
+                   "gbps": round(step.append_bytes() / (app_avg * 1e-3) / 1e9, 1) if step.append else None,
+                   "hbm_frac": round(step.append_bytes() / (app_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
+                   if step.append else None},
     }
+    return rec, step
+
+
+# the other configs reported beside the headline in the same line: the video chunk (the
+# smaller chunk step) and the two decode-shaped caches (the GB/s half of the metric)
+EXTRA_WORKLOADS = ("video_chunk_int2_h12_d128", "decode_gqa32x8_int2_32k", "decode_gqa32x8_int4_32k")
+
+
+def trace_summary(path: str, skip: int) -> None:
+    """Per-kernel durations from a rocprofv3 kernel-trace CSV (``--kernel-trace
+    --output-format csv``): dispatch count, mean, median, min and max in microseconds, the
+    first ``skip`` dispatches of each kernel (the warm-ups) left out. Prints a markdown table."""
+    import csv
+    durs = {}
+    with open(path) as f:
+        for row in csv.DictReader(f):
+            name = row.get("Kernel_Name", "")
+            short = name.split("(")[0].split("<")[0].split("::")[-1] or name
+            if "<" in name.split("(")[0]:
+                short += "<" + name.split("(")[0].split("<", 1)[1]
+            durs.setdefault(short, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
+    print("| kernel | dispatches (after %d skipped) | mean us | median us | min us | max us |" % skip)
+    print("|---|---|---|---|---|---|")
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
+        v = v[skip:] if len(v) > skip else v
+        print("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (k, len(v), np.mean(v), np.median(v), min(v), max(v)))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="rollout_chunk_int2_h40_d128", choices=sorted(workloads.WORKLOADS))
+    ap.add_argument("--no-extra", action="store_true",
+                    help="time only --workload (a profiler run then sees one workload's dispatches)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-probe-hbm", action="store_true",
+                    help="skip the HBM read/copy probe (its copies would mix into a counter run's copy calibration)")
+    ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
+    ap.add_argument("--jensen", type=int, choices=(0, 1, 2), default=None,
+                    help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic); default: the workload's")
+    ap.add_argument("--probe-copy-mib", type=int, default=0,
+                    help="after timing, run one plain device copy of this many MiB (the reference dispatch "
+                         "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
+    ap.add_argument("--trace-summary", metavar="CSV", default=None,
+                    help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit (no GPU)")
+    args = ap.parse_args()
+    if args.trace_summary:
+        trace_summary(args.trace_summary, args.warmup)
+        return
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+    kvq.lib()
+    w = workloads.WORKLOADS[args.workload]
+    if args.jensen is not None:
+        w = dataclasses.replace(w, jensen=args.jensen)
+    if w.bits == 0:
+        window_main(args, w)
+        return
+    rec, step = measure_chunk(args, w, args.copies)
+    res = {"metric": METRIC, "value": rec["value"], "unit": rec["unit"], "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": rec["config"],
+           "roofline": rec["roofline"], "attention": rec["attention"], "append": rec["append"]}
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample ...")
+        res["cpu_baseline"] = cpu_baseline(step)
+    del step
+    torch.cuda.empty_cache()
+    if not args.no_extra:
+        res["configs"] = {}
+        for name in EXTRA_WORKLOADS:
+            if name == w.name:
+                continue
+            r, st = measure_chunk(args, workloads.WORKLOADS[name])
+            del st
+            torch.cuda.empty_cache()
+            res["configs"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "roofline", "attention",
+                                                      "append")}
     if not args.no_probe_hbm:
         res["probe_hbm"] = probe_hbm()
     if args.probe_copy_mib:
@@ -454,9 +543,6 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         log("copy probe: %d MiB read, %d MiB written" % (args.probe_copy_mib, args.probe_copy_mib))
-    if not args.no_cpu_baseline:
-        log("timing the CPU oracle on a sample ...")
-        res["cpu_baseline"] = cpu_baseline(step)
     print(json.dumps(res), flush=True)
 
 

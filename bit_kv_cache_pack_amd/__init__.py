@@ -52,9 +52,10 @@ class KvqAppendArgs(ctypes.Structure):
 
 
 class KvqWindowArgs(ctypes.Structure):
-    _fields_ = [("k", P), ("k_dtype", I32), ("n_kv_heads", I32), ("head_dim", I32), ("n_tokens", I32),
-                ("window", I32), ("text_query", P), ("n_fp16", I32), ("n_int4", I32), ("bits_out", P),
-                ("order_out", P), ("score_out", P)]
+    _fields_ = [("k", P), ("k_dtype", I32), ("n_layers", I32), ("n_kv_heads", I32), ("head_dim", I32),
+                ("n_tokens", I32), ("window", I32), ("text_query", P), ("pct_fp16", I32), ("pct_int4", I32),
+                ("bits_out", P), ("order_out", P), ("score_out", P), ("groups_out", P),
+                ("class_tokens_out", P)]
 
 
 class KvqAttnArgs(ctypes.Structure):
@@ -65,8 +66,8 @@ class KvqAttnArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
-SYMBOLS = ("kvq_quantize_append", "kvq_assign_windows", "kvq_attention_workspace_size",
-           "kvq_chunk_attention", "kvq_status_string", "kvq_abi_version")
+SYMBOLS = ("kvq_quantize_append", "kvq_window_budget", "kvq_assign_windows", "kvq_attention_workspace_size",
+           "kvq_chunk_attention", "kvq_probe_hbm_read", "kvq_status_string", "kvq_abi_version")
 
 _lib = None
 
@@ -87,12 +88,16 @@ def lib() -> ctypes.CDLL:
         L = ctypes.CDLL(LIB_PATH)
         L.kvq_quantize_append.argtypes = [ctypes.POINTER(KvqAppendArgs), P]
         L.kvq_quantize_append.restype = ctypes.c_int
+        L.kvq_window_budget.argtypes = [I32, I32, I32, ctypes.POINTER(I32), ctypes.POINTER(I32)]
+        L.kvq_window_budget.restype = ctypes.c_int
         L.kvq_assign_windows.argtypes = [ctypes.POINTER(KvqWindowArgs), P]
         L.kvq_assign_windows.restype = ctypes.c_int
         L.kvq_attention_workspace_size.argtypes = [ctypes.POINTER(KvqAttnArgs), ctypes.POINTER(ctypes.c_size_t)]
         L.kvq_attention_workspace_size.restype = ctypes.c_int
         L.kvq_chunk_attention.argtypes = [ctypes.POINTER(KvqAttnArgs), P]
         L.kvq_chunk_attention.restype = ctypes.c_int
+        L.kvq_probe_hbm_read.argtypes = [P, ctypes.c_size_t, P, P]
+        L.kvq_probe_hbm_read.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
         L.kvq_status_string.restype = ctypes.c_char_p
         L.kvq_abi_version.argtypes = []
@@ -192,19 +197,64 @@ def quantize_append(segment: Segment, k_src: torch.Tensor, v_src: torch.Tensor, 
     _check(lib().kvq_quantize_append(ctypes.byref(args), _stream(stream)), "kvq_quantize_append")
 
 
-def assign_windows(k: torch.Tensor, text_query: torch.Tensor, n_fp16: int, n_int4: int, window: int = 32,
-                   bits_out=None, order_out=None, score_out=None, stream=None):
+def window_budget(n_windows: int, pct_fp16: int, pct_int4: int):
+    """(FP16 windows, INT4 windows) that kvq_assign_windows gives each class (the rule is
+    in the library; include/kvq.h states it)."""
+    a, b = I32(), I32()
+    _check(lib().kvq_window_budget(int(n_windows), int(pct_fp16), int(pct_int4), ctypes.byref(a), ctypes.byref(b)),
+           "kvq_window_budget")
+    return a.value, b.value
+
+
+class WindowAssignment:
+    """Device outputs of kvq_assign_windows for n_layers caches: bits [L][W] int8, order
+    [L][W] int32, score [L][W] float64, groups [L][W][2] int32 (the gather lists in
+    grouped order) and class_tokens [L][3] int32 (tokens of the FP16, INT4, INT2 classes),
+    plus the window counts per class."""
+
+    def __init__(self, bits, order, score, groups, class_tokens, n_fp16, n_int4):
+        self.bits, self.order, self.score = bits, order, score
+        self.groups, self.class_tokens = groups, class_tokens
+        self.n_fp16, self.n_int4 = n_fp16, n_int4
+        self.n_windows = bits.shape[-1]
+
+    def class_rows(self):
+        """Rows of ``groups`` (per layer) holding the FP16, INT4 and INT2 gather lists."""
+        a, b = self.n_fp16, self.n_fp16 + self.n_int4
+        return {16: (0, a), 4: (a, b), 2: (b, self.n_windows)}
+
+    def class_list(self, bits: int, layer: int = 0) -> torch.Tensor:
+        """The device gather list of one class (a view into ``groups``)."""
+        a, b = self.class_rows()[bits]
+        return self.groups[layer, a:b]
+
+
+def assign_windows(k: torch.Tensor, text_query: torch.Tensor, pct_fp16: int, pct_int4: int, window: int = 32,
+                   out: Optional[WindowAssignment] = None, stream=None) -> WindowAssignment:
+    """k: device [n_layers][Hkv][N][d] (or [Hkv][N][d] for one layer); text_query: device
+    float32 [n_layers][d] (or [d])."""
     _dev(k, "k"); _dev(text_query, "text_query")
-    H, N, d = k.shape
+    if k.dim() == 3:
+        k = k.unsqueeze(0)
+    nl, H, N, d = k.shape
+    if text_query.dim() == 1:
+        text_query = text_query.unsqueeze(0)
+    if text_query.dtype != torch.float32 or tuple(text_query.shape) != (nl, d):
+        raise ValueError("text_query must be float32 [n_layers][head_dim]")
     W = -(-N // window)
-    dev = k.device
-    bits_out = torch.empty(W, dtype=torch.int8, device=dev) if bits_out is None else bits_out
-    order_out = torch.empty(W, dtype=torch.int32, device=dev) if order_out is None else order_out
-    score_out = torch.empty(W, dtype=torch.float64, device=dev) if score_out is None else score_out
-    args = KvqWindowArgs(_ptr(k), _TORCH_DT[k.dtype], H, d, N, window, _ptr(text_query), int(n_fp16),
-                         int(n_int4), _ptr(bits_out), _ptr(order_out), _ptr(score_out))
+    if out is None:
+        n16, n4 = window_budget(W, pct_fp16, pct_int4)
+        dev = k.device
+        out = WindowAssignment(torch.empty((nl, W), dtype=torch.int8, device=dev),
+                               torch.empty((nl, W), dtype=torch.int32, device=dev),
+                               torch.empty((nl, W), dtype=torch.float64, device=dev),
+                               torch.empty((nl, W, 2), dtype=torch.int32, device=dev),
+                               torch.empty((nl, 3), dtype=torch.int32, device=dev), n16, n4)
+    args = KvqWindowArgs(_ptr(k), _TORCH_DT[k.dtype], nl, H, d, N, window, _ptr(text_query), int(pct_fp16),
+                         int(pct_int4), _ptr(out.bits), _ptr(out.order), _ptr(out.score), _ptr(out.groups),
+                         _ptr(out.class_tokens))
     _check(lib().kvq_assign_windows(ctypes.byref(args), _stream(stream)), "kvq_assign_windows")
-    return bits_out, order_out, score_out
+    return out
 
 
 def _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out, out_dtype, lse,
@@ -212,7 +262,12 @@ def _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out
     B, Hq, nq, d = q.shape
     segs = list(segments)
     if n_kv_heads is None:
-        n_kv_heads = segs[0].desc.n_kv_heads if segs else k_cur.shape[1]
+        if segs:
+            n_kv_heads = segs[0].desc.n_kv_heads
+        elif k_cur is not None:
+            n_kv_heads = k_cur.shape[1]
+        else:
+            raise ValueError("n_kv_heads is needed when there are neither segments nor a current chunk")
     arr = (KvqSegment * max(1, len(segs)))(*[s.desc for s in segs])
     n_cur = 0 if k_cur is None else k_cur.shape[2]
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
@@ -225,7 +280,6 @@ def _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out
 def attention_workspace_size(q: torch.Tensor, segments: Sequence[Segment], n_cur: int = 0,
                              n_kv_heads: Optional[int] = None, jensen: int = JENSEN_TAYLOR2,
                              out_dtype: int = F32) -> int:
-    k_cur = None
     a, arr = _attn_args(q, segments, None, None, n_kv_heads, 0.0, jensen, None, out_dtype, None, None)
     a.n_cur = int(n_cur)
     n = ctypes.c_size_t()
@@ -243,6 +297,8 @@ def chunk_attention(q: torch.Tensor, segments: Sequence[Segment], k_cur: Optiona
         _dev(k_cur, "k_cur"); _dev(v_cur, "v_cur")
     if out is None:
         out = torch.empty(q.shape, dtype=out_dtype, device=q.device)
+    if n_kv_heads is None and not segments and k_cur is not None:
+        n_kv_heads = k_cur.shape[1]
     if workspace is None:
         need = attention_workspace_size(q, segments, 0 if k_cur is None else k_cur.shape[2], n_kv_heads,
                                         jensen, _TORCH_DT[out.dtype])
@@ -254,25 +310,8 @@ def chunk_attention(q: torch.Tensor, segments: Sequence[Segment], k_cur: Optiona
     return out
 
 
-def window_budget(n_windows: int, pct_fp16: int, pct_int4: int):
-    """FP16 / INT4 window counts from percentages: floor over all windows, window 0 counted
-    inside the FP16 share, at least one FP16 window."""
-    n16 = n_windows * pct_fp16 // 100
-    n4 = n_windows * (pct_fp16 + pct_int4) // 100 - n16
-    n16 = max(n16, 1)
-    n4 = max(0, min(n4, n_windows - n16))
-    return n16, n4
-
-
-def window_groups(order: Sequence[int], bits: Sequence[int], n_tokens: int, window: int = 32):
-    """Host helper: per bit-width class, the {first token, length} gather list of its windows
-    in grouped storage order (an int32 [n][2] array, the layout kvq_quantize_append takes),
-    and the class's token count."""
-    order = np.asarray(order, dtype=np.int64).reshape(-1)
-    bits = np.asarray(bits).reshape(-1)
-    out = {}
-    for b in (16, 4, 2):
-        starts = order[bits[order] == b] * window
-        g = np.stack([starts, np.minimum(window, n_tokens - starts)], axis=1).astype(np.int32).reshape(-1, 2)
-        out[b] = (g, int(g[:, 1].sum()))
-    return out
+def probe_hbm_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueue one streaming read of ``buf`` (a measurement aid: kvq_probe_hbm_read)."""
+    _dev(buf, "buf"); _dev(sink, "sink")
+    nbytes = buf.numel() * buf.element_size()
+    _check(lib().kvq_probe_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_probe_hbm_read")

@@ -21,7 +21,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 OBJ_DIR = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["api.hip", "quant.hip", "attention.hip", "decode.hip", "windows.hip"]
+SOURCES = ["api.hip", "quant.hip", "attention.hip", "decode.hip", "windows.hip", "probe.hip"]
 PER_SOURCE = {"attention.hip": ["-fno-honor-nans"], "decode.hip": ["-fno-honor-nans"], "quant.hip": ["-fno-honor-nans"]}
 ARCH = os.environ.get("KVQ_OFFLOAD_ARCH", "gfx950")
 

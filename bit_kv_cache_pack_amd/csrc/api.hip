@@ -69,12 +69,13 @@ kvq_status check_attention_shape(const kvq_attn_args *a, long long *n_total) {
 }
 
 // Which attention kernel a call runs (the workspace size depends on it).
-bool use_decode(const kvq_attn_args *a) {
+bool use_decode(const kvq_attn_args *a, long long n_total) {
     int bits[KVQ_MAX_SEGMENTS];
     int n = 0;
     for (int i = 0; i < a->n_segs; ++i)
         if (a->segs[i].n_tokens > 0) bits[n++] = a->segs[i].bits;
-    return kvq::decode_eligible(a->dtype, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, bits, n);
+    return kvq::decode_eligible(a->dtype, a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, bits, n,
+                                a->n_cur, (int)n_total);
 }
 
 }  // namespace
@@ -144,30 +145,53 @@ kvq_status kvq_quantize_append(const kvq_append_args *a, void *stream) {
     return KVQ_OK;
 }
 
+kvq_status kvq_window_budget(int32_t n_windows, int32_t pct_fp16, int32_t pct_int4, int32_t *n_fp16,
+                             int32_t *n_int4) {
+    if (!n_fp16 || !n_int4 || n_windows < 1) return KVQ_ERR_ARG;
+    if (pct_fp16 < 0 || pct_int4 < 0 || pct_fp16 > 100 || pct_int4 > 100 || pct_fp16 + pct_int4 > 100)
+        return KVQ_ERR_ARG;
+    int a = 0, b = 0;
+    kvq::window_budget(n_windows, pct_fp16, pct_int4, &a, &b);
+    *n_fp16 = a;
+    *n_int4 = b;
+    return KVQ_OK;
+}
+
 kvq_status kvq_assign_windows(const kvq_window_args *a, void *stream) {
     if (!a) return KVQ_ERR_ARG;
     if (!any_dtype(a->k_dtype)) return KVQ_ERR_UNSUPPORTED;
     if (a->head_dim < 1 || a->head_dim > 256) return KVQ_ERR_UNSUPPORTED;
-    if (a->n_kv_heads < 1 || a->n_tokens < 1 || a->window < 1) return KVQ_ERR_ARG;
+    if (a->n_layers < 1 || a->n_kv_heads < 1 || a->n_tokens < 1 || a->window < 1) return KVQ_ERR_ARG;
+    if (a->n_layers > kvq::kMaxWindowLayers) return KVQ_ERR_UNSUPPORTED;
     if (!a->k || !a->text_query || !a->bits_out || !a->order_out || !a->score_out) return KVQ_ERR_ARG;
     const long long W = ((long long)a->n_tokens + a->window - 1) / a->window;
-    if (W > 16384) return KVQ_ERR_UNSUPPORTED;
-    if (a->n_fp16 < 1 || a->n_int4 < 0 || (long long)a->n_fp16 + a->n_int4 > W) return KVQ_ERR_ARG;
+    if (W > kvq::kMaxWindowsPerLayer) return KVQ_ERR_UNSUPPORTED;
+    int32_t n16 = 0, n4 = 0;
+    kvq_status st = kvq_window_budget((int32_t)W, a->pct_fp16, a->pct_int4, &n16, &n4);
+    if (st != KVQ_OK) return st;
     kvq::WindowParams p;
     p.k = a->k;
     p.k_dtype = a->k_dtype;
+    p.n_layers = a->n_layers;
     p.n_kv_heads = a->n_kv_heads;
     p.head_dim = a->head_dim;
     p.n_tokens = a->n_tokens;
     p.window = a->window;
     p.n_windows = (int32_t)W;
     p.text = a->text_query;
-    p.n_fp16 = a->n_fp16;
-    p.n_int4 = a->n_int4;
+    p.n_fp16 = n16;
+    p.n_int4 = n4;
     p.bits_out = a->bits_out;
     p.order_out = a->order_out;
     p.score = a->score_out;
+    p.groups_out = a->groups_out;
+    p.class_tokens_out = a->class_tokens_out;
     return kvq::launch_windows(p, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+}
+
+kvq_status kvq_probe_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream) {
+    if (!buf || !sink || !aligned16(buf) || bytes == 0 || bytes % 16 != 0) return KVQ_ERR_ARG;
+    return kvq::launch_hbm_read(buf, bytes, sink, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
 kvq_status kvq_attention_workspace_size(const kvq_attn_args *a, size_t *bytes) {
@@ -176,7 +200,7 @@ kvq_status kvq_attention_workspace_size(const kvq_attn_args *a, size_t *bytes) {
     kvq_status st = check_attention_shape(a, &n_total);
     if (st != KVQ_OK) return st;
     kvq::AttnPlan plan;
-    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, use_decode(a),
+    kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, use_decode(a, n_total),
                         &plan);
     *bytes = plan.workspace_bytes;
     return KVQ_OK;
@@ -191,7 +215,7 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
         return KVQ_ERR_ARG;
     for (int i = 0; i < a->n_segs; ++i)
         if (a->segs[i].n_tokens > 0 && (st = check_segment_ptrs(a->segs[i])) != KVQ_OK) return st;
-    const bool decode = use_decode(a);
+    const bool decode = use_decode(a, n_total);
     kvq::AttnPlan plan;
     kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, decode, &plan);
     const size_t need = plan.workspace_bytes;

@@ -9,6 +9,10 @@
 // Score of a window: for each KV head the window's mean key, cosine with the text vector,
 // averaged over heads. Everything in double, summed in index order (this file is built
 // with -ffp-contract=off), so the scores and therefore the ranking are reproducible.
+// Several independent caches (layers) are scored and assigned by the same two launches:
+// blockIdx.y is the layer. The selection also writes the grouped layout's gather lists
+// ({first token, length} of every window, FP16 windows first, then INT4, then INT2, each
+// ascending) and each class's token count, so that the appends can take them as they are.
 #include "kvq_device.cuh"
 #include "kvq_internal.h"
 
@@ -16,7 +20,6 @@ namespace kvq {
 namespace {
 
 constexpr int kSelectThreads = 1024;
-constexpr int kMaxWindows = 16384;
 
 constexpr int kScoreThreads = 256;
 constexpr int kScoreMeans = 2048;   // (head, channel) means held in LDS at once
@@ -28,8 +31,10 @@ constexpr int kScoreMeans = 2048;   // (head, channel) means held in LDS at once
 __global__ __launch_bounds__(kScoreThreads) void window_score_kernel(WindowParams p) {
     __shared__ double mean[kScoreMeans];
     __shared__ double cs[kScoreThreads];
-    const int w = blockIdx.x, tid = threadIdx.x;
+    const int w = blockIdx.x, tid = threadIdx.x, layer = blockIdx.y;
     const int d = p.head_dim, H = p.n_kv_heads;
+    const size_t kbase = (size_t)layer * H * p.n_tokens * d;
+    const float *text = p.text + (size_t)layer * d;
     const int t0 = w * p.window, t1 = min(p.n_tokens, t0 + p.window);
     const int hc = min(kScoreMeans / d, kScoreThreads);   // heads per chunk
     double acc = 0.0;
@@ -38,7 +43,7 @@ __global__ __launch_bounds__(kScoreThreads) void window_score_kernel(WindowParam
         __syncthreads();
         for (int idx = tid; idx < nh * d; idx += kScoreThreads) {
             const int h = h0 + idx / d, c = idx % d;
-            const size_t base = (size_t)h * p.n_tokens * d + c;
+            const size_t base = kbase + (size_t)h * p.n_tokens * d + c;
             double sum = 0.0;
             int t = t0;
             for (; t + 4 <= t1; t += 4) {
@@ -59,7 +64,7 @@ __global__ __launch_bounds__(kScoreThreads) void window_score_kernel(WindowParam
             const double *mh = mean + tid * d;
             double dot = 0.0, nm = 0.0, nt = 0.0;
             for (int i = 0; i < d; ++i) {
-                const double tv = (double)p.text[i];
+                const double tv = (double)text[i];
                 dot += mh[i] * tv;
                 nm += mh[i] * mh[i];
                 nt += tv * tv;
@@ -70,7 +75,7 @@ __global__ __launch_bounds__(kScoreThreads) void window_score_kernel(WindowParam
         if (tid == 0)
             for (int k = 0; k < nh; ++k) acc += cs[k];
     }
-    if (tid == 0) p.score[w] = acc / (double)H;
+    if (tid == 0) p.score[(size_t)layer * p.n_windows + w] = acc / (double)H;
 }
 
 constexpr int kSortMax = 8192;   // windows ranked by a sort in LDS; more are ranked by counting
@@ -86,19 +91,24 @@ __device__ __forceinline__ bool before(double sa, int ia, double sb, int ib) {
 // lists come from a block prefix sum, over the windows in index order, of three class
 // counters packed in one 64-bit word.
 __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowParams p) {
-    __shared__ int8_t cls[kMaxWindows];
+    __shared__ int8_t cls[kMaxWindowsPerLayer];
     __shared__ double key[kSortMax];
     __shared__ int idx[kSortMax];
     __shared__ unsigned long long wsum[kSelectThreads / kWave];
     const int W = p.n_windows, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int n16 = p.n_fp16, n4 = p.n_int4;
     const int M = W - 1;
+    const size_t lw = (size_t)blockIdx.y * W;   // this layer's windows
+    const double *score = p.score + lw;
+    int8_t *bits_out = p.bits_out + lw;
+    int32_t *order_out = p.order_out + lw;
+    int32_t *groups_out = p.groups_out != nullptr ? p.groups_out + 2 * lw : nullptr;
     auto class_of = [&](int rank) -> int8_t { return rank < n16 - 1 ? 16 : (rank < n16 - 1 + n4 ? 4 : 2); };
     if (M <= kSortMax) {
         int N = 1;
         while (N < M) N <<= 1;
         for (int i = tid; i < N; i += kSelectThreads) {
-            key[i] = i < M ? p.score[i + 1] : -__builtin_inf();
+            key[i] = i < M ? score[i + 1] : -__builtin_inf();
             idx[i] = i < M ? i + 1 : 0x7fffffff;   // pads sort last
         }
         __syncthreads();
@@ -125,10 +135,10 @@ __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowPar
     } else {
         for (int w = threadIdx.x; w < W; w += kSelectThreads) {
             if (w == 0) continue;
-            const double s = p.score[w];
+            const double s = score[w];
             int rank = 0;
             for (int v = 1; v < W; ++v) {
-                const double t = p.score[v];
+                const double t = score[v];
                 rank += before(t, v, s, w) ? 1 : 0;
             }
             cls[w] = class_of(rank);
@@ -141,7 +151,7 @@ __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowPar
     for (int w0 = 0; w0 < W; w0 += kSelectThreads) {
         const int w = w0 + tid;
         const int8_t b = w < W ? cls[w] : 0;
-        if (w < W) p.bits_out[w] = b;
+        if (w < W) bits_out[w] = b;
         const int sh = b == 16 ? 0 : (b == 4 ? 21 : 42);
         const unsigned long long v = w < W ? 1ull << sh : 0ull;
         unsigned long long x = v;
@@ -161,21 +171,51 @@ __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowPar
             const int before_w = (int)((pre >> sh) & 0x1fffff);
             const int base = b == 16 ? 0 : (b == 4 ? n16 : n16 + n4);
             // ranks form a permutation, so this stays inside the list; never write outside it
-            if (base + before_w < W) p.order_out[base + before_w] = w;
+            const int pos = base + before_w;
+            if (pos < W) {
+                order_out[pos] = w;
+                if (groups_out != nullptr) {
+                    const int t0 = w * p.window;
+                    groups_out[2 * pos] = t0;
+                    groups_out[2 * pos + 1] = min(p.window, p.n_tokens - t0);
+                }
+            }
         }
         carry = tot;
         __syncthreads();
+    }
+    // tokens per class: whole windows, less what the last window lacks in its own class
+    if (tid == 0 && p.class_tokens_out != nullptr) {
+        const int last = cls[W - 1];
+        const int short_by = W * p.window - p.n_tokens;
+        const int counts[3] = {n16, n4, W - n16 - n4};
+        const int which[3] = {16, 4, 2};
+        int32_t *ct = p.class_tokens_out + 3 * (size_t)blockIdx.y;
+        for (int k = 0; k < 3; ++k) ct[k] = counts[k] * p.window - (which[k] == last ? short_by : 0);
     }
 }
 
 }  // namespace
 
 hipError_t launch_windows(const WindowParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(window_score_kernel, dim3(p.n_windows), dim3(kScoreThreads), 0, s, p);
+    hipLaunchKernelGGL(window_score_kernel, dim3(p.n_windows, p.n_layers), dim3(kScoreThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(window_select_kernel, dim3(1), dim3(kSelectThreads), 0, s, p);
+    hipLaunchKernelGGL(window_select_kernel, dim3(1, p.n_layers), dim3(kSelectThreads), 0, s, p);
     return hipGetLastError();
+}
+
+void window_budget(int n_windows, int pct_fp16, int pct_int4, int *n_fp16, int *n_int4) {
+    // floor over all windows in integer arithmetic; window 0 counts inside the FP16 share,
+    // which keeps at least one window
+    const long long W = n_windows;
+    long long n16 = W * pct_fp16 / 100;
+    long long n4 = W * (pct_fp16 + pct_int4) / 100 - n16;
+    if (n16 < 1) n16 = 1;
+    if (n4 > W - n16) n4 = W - n16;
+    if (n4 < 0) n4 = 0;
+    *n_fp16 = (int)n16;
+    *n_int4 = (int)n4;
 }
 
 }  // namespace kvq

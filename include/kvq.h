@@ -46,7 +46,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 1
+#define KVQ_ABI_VERSION 2
 #define KVQ_MAX_SEGMENTS 8
 
 typedef enum kvq_status {
@@ -153,34 +153,61 @@ typedef struct kvq_append_args {
 kvq_status kvq_quantize_append(const kvq_append_args *args, void *stream);
 
 /*
- * kvq_assign_windows -- WindowQuant bit-widths for one sequence [WQ].
- *   k            device [n_kv_heads][n_tokens][head_dim] of k_dtype (F16, BF16 or F32).
+ * kvq_window_budget -- how many windows each bit-width class gets [WQ: high / middle / low
+ * relevance kept in FP16 / INT4 / INT2]. Host only, no device work.
+ *   n_fp16 = floor(n_windows * pct_fp16 / 100), at least 1 (window 0 is FP16 and counts
+ *   inside this share); n_int4 = floor(n_windows * (pct_fp16 + pct_int4) / 100) - the
+ *   unraised n_fp16, capped so the two fit in n_windows; the rest are INT2. Integer
+ *   arithmetic throughout. 613 windows at 10 % / 30 % give 61 FP16, 184 INT4, 368 INT2.
+ * Errors: KVQ_ERR_ARG (null outputs, n_windows < 1, a percentage outside [0, 100], or
+ * pct_fp16 + pct_int4 > 100).
+ */
+kvq_status kvq_window_budget(int32_t n_windows, int32_t pct_fp16, int32_t pct_int4, int32_t *n_fp16,
+                             int32_t *n_int4);
+
+/*
+ * kvq_assign_windows -- WindowQuant bit-widths and grouped layout for n_layers independent
+ * caches (e.g. the layers of a model) in one pair of launches [WQ].
+ *   k            device [n_layers][n_kv_heads][n_tokens][head_dim] of k_dtype (F16, BF16
+ *                or F32), head_dim 1..256.
+ *   text_query   device float32 [n_layers][head_dim]: each layer's text-query vector.
  *   Windows are [window*w, min(window*w + window, n_tokens)), w < n_windows =
- *   ceil(n_tokens / window).
+ *   ceil(n_tokens / window) <= 16384.
  *   Score: per KV head, the window's mean key (tokens summed in index order, in
- *   double, divided by the token count); cosine with text_query (device, float32
- *   [head_dim]) as dot / (sqrt(|mean|^2) * sqrt(|t|^2)), sums over channels in index
- *   order, 0 if either norm is zero; score = mean over KV heads (summed in order).
- *   Assignment: window 0 is FP16 whatever its score; windows 1.. are ranked by score,
- *   highest first, ties to the lower index; the first n_fp16 - 1 get FP16, the next
- *   n_int4 INT4, the rest INT2.
- *   bits_out     device int8 [n_windows]: 16, 4 or 2.
- *   order_out    device int32 [n_windows]: the FP16 windows ascending, then INT4
- *                ascending, then INT2 ascending (the grouped storage order).
- *   score_out    device double [n_windows] (required: also the scratch of the ranking).
- * Errors: KVQ_ERR_ARG (nulls, n_tokens < 1, window < 1, n_fp16 < 1, n_int4 < 0,
- * n_fp16 + n_int4 > n_windows), KVQ_ERR_UNSUPPORTED (head_dim not in {64, 128},
- * n_windows > 65536).
+ *   double, divided by the token count); cosine with the layer's text query as
+ *   dot / (sqrt(|mean|^2) * sqrt(|t|^2)), sums over channels in index order, 0 if either
+ *   norm is zero; score = mean over KV heads (summed in order).
+ *   Assignment (per layer): window 0 is FP16 whatever its score; windows 1.. are ranked
+ *   by score, highest first, ties to the lower index; with n_fp16 / n_int4 from
+ *   kvq_window_budget(n_windows, pct_fp16, pct_int4), the first n_fp16 - 1 get FP16, the
+ *   next n_int4 INT4, the rest INT2.
+ *   bits_out     device int8 [n_layers][n_windows]: 16, 4 or 2.
+ *   order_out    device int32 [n_layers][n_windows]: the FP16 windows ascending, then
+ *                INT4 ascending, then INT2 ascending (the grouped storage order).
+ *   score_out    device double [n_layers][n_windows] (required: also the ranking's input).
+ *   groups_out   device int32 [n_layers][n_windows][2], optional (NULL: not written):
+ *                {first token, length} of the windows in order_out's order. Rows
+ *                [0, n_fp16), [n_fp16, n_fp16 + n_int4) and [n_fp16 + n_int4, n_windows)
+ *                are the gather lists kvq_quantize_append takes for the FP16, INT4 and
+ *                INT2 segments.
+ *   class_tokens_out  device int32 [n_layers][3], optional: tokens of the FP16, INT4 and
+ *                INT2 classes (each class's n_new for those appends).
+ * Errors: KVQ_ERR_ARG (nulls, n_layers < 1, n_tokens < 1, window < 1, a bad budget as in
+ * kvq_window_budget), KVQ_ERR_UNSUPPORTED (k_dtype, head_dim outside 1..256, n_windows >
+ * 16384, n_layers > 65535).
  */
 typedef struct kvq_window_args {
     const void *k;
     int32_t k_dtype;
+    int32_t n_layers;
     int32_t n_kv_heads, head_dim, n_tokens, window;
     const float *text_query;
-    int32_t n_fp16, n_int4;
+    int32_t pct_fp16, pct_int4;
     int8_t *bits_out;
     int32_t *order_out;
     double *score_out;
+    int32_t *groups_out;
+    int32_t *class_tokens_out;
 } kvq_window_args;
 
 kvq_status kvq_assign_windows(const kvq_window_args *args, void *stream);
@@ -232,6 +259,18 @@ typedef struct kvq_attn_args {
 kvq_status kvq_attention_workspace_size(const kvq_attn_args *args, size_t *bytes);
 
 kvq_status kvq_chunk_attention(const kvq_attn_args *args, void *stream);
+
+/*
+ * kvq_probe_hbm_read -- a measurement aid, not a step of the method: reads the `bytes`
+ * bytes at device address `buf` once, as a plain coalesced stream of 16-byte loads, so
+ * that timing it on `stream` gives the HBM read bandwidth the device reaches (the
+ * attention and quantize-append kernels are rated against that as well as against the
+ * published peak). Use a buffer well above the last-level cache (256 MB on MI355X).
+ * `sink` (device uint32) is written only if an XOR of everything read equals a fixed
+ * constant; its contents do not matter.
+ * Errors: KVQ_ERR_ARG (null or misaligned buf, bytes 0 or not a multiple of 16, null sink).
+ */
+kvq_status kvq_probe_hbm_read(const void *buf, size_t bytes, uint32_t *sink, void *stream);
 
 /* Static, never-NULL description of a status code. */
 const char *kvq_status_string(kvq_status status);

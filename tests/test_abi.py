@@ -21,8 +21,7 @@ def _declared():
 
 
 def test_header_declares_the_entry_points():
-    assert _declared() == sorted(["kvq_quantize_append", "kvq_assign_windows", "kvq_attention_workspace_size",
-                                  "kvq_chunk_attention", "kvq_status_string", "kvq_abi_version"])
+    assert _declared() == sorted(kvq.SYMBOLS)
 
 
 def test_library_exports_every_declared_symbol():
@@ -32,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     assert set(_declared()) <= exported
-    assert L.kvq_abi_version() == 1
+    assert L.kvq_abi_version() == 2
 
 
 def test_header_compiles_as_c():
@@ -179,24 +178,60 @@ def test_workspace_size_and_check():
 
 def test_window_validation():
     def call(**kw):
-        d = dict(k=FAKE, k_dtype=kvq.F16, n_kv_heads=2, head_dim=64, n_tokens=19600, window=32, text_query=FAKE,
-                 n_fp16=61, n_int4=184, bits_out=FAKE, order_out=FAKE, score_out=FAKE)
+        d = dict(k=FAKE, k_dtype=kvq.F16, n_layers=1, n_kv_heads=2, head_dim=64, n_tokens=19600, window=32,
+                 text_query=FAKE, pct_fp16=10, pct_int4=30, bits_out=FAKE, order_out=FAKE, score_out=FAKE,
+                 groups_out=None, class_tokens_out=None)
         d.update(kw)
         a = kvq.KvqWindowArgs(**d)
         return kvq.lib().kvq_assign_windows(ctypes.byref(a), None)
-    assert call(n_fp16=0) == kvq.ERR_ARG
-    assert call(n_fp16=500, n_int4=200) == kvq.ERR_ARG
+    assert call(pct_fp16=70, pct_int4=40) == kvq.ERR_ARG   # shares above 100 %
+    assert call(pct_int4=-1) == kvq.ERR_ARG
     assert call(score_out=None) == kvq.ERR_ARG
+    assert call(bits_out=None) == kvq.ERR_ARG
     assert call(k_dtype=9) == kvq.ERR_UNSUPPORTED
-    assert call(head_dim=512) == kvq.ERR_UNSUPPORTED
-    assert call(n_tokens=16384 * 32 + 1) == kvq.ERR_UNSUPPORTED
+    assert call(head_dim=257) == kvq.ERR_UNSUPPORTED       # the header's limits: head_dim 1..256,
+    assert call(head_dim=0) == kvq.ERR_UNSUPPORTED
+    assert call(n_tokens=16384 * 32 + 1) == kvq.ERR_UNSUPPORTED   # at most 16384 windows per layer,
+    assert call(n_layers=65536) == kvq.ERR_UNSUPPORTED             # at most 65535 layers
+    assert call(n_layers=0) == kvq.ERR_ARG
     assert call(window=0) == kvq.ERR_ARG
+    assert call(n_tokens=0) == kvq.ERR_ARG
+    assert kvq.lib().kvq_assign_windows(None, None) == kvq.ERR_ARG
 
 
-def test_binding_window_budget():
+def test_window_budget_rule():
+    """kvq_window_budget: floor of the shares over all windows, window 0 inside the FP16
+    share, at least one FP16 window; the 100-frame workload's 613 windows give 61 / 184 / 368."""
     assert kvq.window_budget(613, 10, 30) == (61, 184)
-    g = kvq.window_groups([0, 2, 1, 3], [16, 4, 16, 2], n_tokens=100)
-    assert g[16][0].tolist() == [[0, 32], [64, 32]] and g[16][1] == 64
-    assert g[4][0].tolist() == [[32, 32]] and g[4][1] == 32
-    assert g[2][0].tolist() == [[96, 4]] and g[2][1] == 4
-    assert all(g[b][0].dtype == np.int32 and g[b][0].shape[1] == 2 for b in (16, 4, 2))
+    assert kvq.window_budget(5, 10, 30) == (1, 2)          # floor 0 FP16 raised to window 0
+    assert kvq.window_budget(1, 0, 0) == (1, 0)
+    assert kvq.window_budget(10, 0, 100) == (1, 9)         # INT4 capped to what is left
+    assert kvq.window_budget(100, 100, 0) == (100, 0)
+    for bad in ((0, 10, 30), (10, 101, 0), (10, -1, 0), (10, 60, 50)):
+        with pytest.raises(kvq.KvqError):
+            kvq.window_budget(*bad)
+    n = ctypes.c_int32()
+    assert kvq.lib().kvq_window_budget(10, 10, 30, None, ctypes.byref(n)) == kvq.ERR_ARG
+
+
+def test_binding_attention_without_segments_takes_heads_from_current_chunk():
+    """No segments: the KV head count comes from the current chunk; with neither, the
+    binding asks for it instead of failing inside."""
+    import torch
+    q = torch.zeros((1, 4, 33, 64), dtype=torch.float16)
+    kc = torch.zeros((1, 4, 77, 64), dtype=torch.float16)
+    a, arr = kvq._attn_args(q, [], kc, kc, None, 0.0, 1, None, kvq.F32, None, None)
+    assert a.n_kv_heads == 4 and a.n_cur == 77
+    assert kvq.attention_workspace_size(q, [], n_cur=77, n_kv_heads=4) >= 0
+    with pytest.raises(ValueError):
+        kvq.attention_workspace_size(q, [], n_cur=77)
+
+
+def test_probe_validation():
+    sink = FAKE
+    L = kvq.lib()
+    assert L.kvq_probe_hbm_read(None, 1 << 20, sink, None) == kvq.ERR_ARG
+    assert L.kvq_probe_hbm_read(FAKE, 0, sink, None) == kvq.ERR_ARG
+    assert L.kvq_probe_hbm_read(FAKE, 1000, sink, None) == kvq.ERR_ARG       # not a multiple of 16
+    assert L.kvq_probe_hbm_read(FAKE + 8, 1 << 20, sink, None) == kvq.ERR_ARG  # misaligned
+    assert L.kvq_probe_hbm_read(FAKE, 1 << 20, None, None) == kvq.ERR_ARG

@@ -120,7 +120,7 @@ def test_attention_chunk_small(bits, jensen):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("jensen", [1, 2])
+@pytest.mark.parametrize("jensen", [0, 1, 2])
 def test_attention_gqa_decode_splits(d, jensen):
     """GQA decode: one query per head, rows packed per KV head, token splits + combine."""
     go, gl, oo, ol = _attention_case(2, "bf16", 2, 8, 2, d, appends=(1500, 700), n_cur=0, n_q=1, jensen=jensen,
@@ -179,17 +179,81 @@ def test_tiny_workload(jensen):
     assert np.abs(gl - ol).max() <= TOL
 
 
+def _window_case(nl, H, N, d, seed, dtype=torch.float16):
+    rng = np.random.default_rng(seed)
+    k = torch.from_numpy(rng.standard_normal((nl, H, N, d)).astype(np.float32)).to(dtype)
+    t = torch.from_numpy(rng.standard_normal((nl, d)).astype(np.float32))
+    return k, t
+
+
+def _check_windows(asg, k, t, N, window=32, pct=(10, 30)):
+    """Every layer's scores (4 ulp), bits, order, gather lists and class token counts
+    (bit-exact) against the oracle run on that layer alone."""
+    W = -(-N // window)
+    n16, n4 = oracle.window_budget(W, *pct)
+    assert (asg.n_fp16, asg.n_int4) == (n16, n4)
+    score, bits, order = asg.score.cpu().numpy(), asg.bits.cpu().numpy(), asg.order.cpu().numpy()
+    groups, ct = asg.groups.cpu().numpy(), asg.class_tokens.cpu().numpy()
+    for layer in range(k.shape[0]):
+        osc = oracle.window_scores(f32(k[layer]), t[layer].numpy(), window)
+        ob, oo = oracle.assign_windows(osc, n16, n4)
+        og, oct_ = oracle.window_groups(ob, oo, N, window)
+        np.testing.assert_array_max_ulp(score[layer], osc, maxulp=4)
+        assert np.array_equal(bits[layer], ob), layer
+        assert np.array_equal(order[layer], oo), layer
+        assert np.array_equal(groups[layer], og), layer
+        assert np.array_equal(ct[layer], oct_), layer
+
+
 def test_windows_scores_and_assignment():
-    rng = np.random.default_rng(3)
-    H, N, d = 2, 1000, 64
-    k = torch.from_numpy(rng.standard_normal((H, N, d)).astype(np.float32)).half()
-    t = torch.from_numpy(rng.standard_normal(d).astype(np.float32))
-    W = -(-N // 32)
-    n16, n4 = kvq.window_budget(W, 10, 30)
-    bits, order, score = kvq.assign_windows(k.cuda(), t.cuda(), n16, n4)
+    k, t = _window_case(1, 2, 1000, 64, 3)
+    asg = kvq.assign_windows(k[0].cuda(), t[0].cuda(), 10, 30)
     torch.cuda.synchronize()
-    osc = oracle.window_scores(f32(k), t.numpy(), 32)
-    ob, oo = oracle.assign_windows(osc, n16, n4)
-    np.testing.assert_array_max_ulp(score.cpu().numpy(), osc, maxulp=4)
-    assert np.array_equal(bits.cpu().numpy(), ob)
-    assert np.array_equal(order.cpu().numpy(), oo)
+    _check_windows(asg, k, t, 1000)
+
+
+@pytest.mark.parametrize("N", [6272, 6256])
+def test_windows_many_layers_one_launch(N):
+    """Prefill scale: 12 independent caches (layers) scored and assigned by one pair of
+    launches, each layer with its own keys and text query; a short last window (6256)
+    lands in whatever class its score gives it."""
+    k, t = _window_case(12, 2, N, 64, 29)
+    asg = kvq.assign_windows(k.cuda(), t.cuda(), 10, 30)
+    torch.cuda.synchronize()
+    _check_windows(asg, k, t, N)
+
+
+@pytest.mark.parametrize("dtype,d,jensen", [("f16", 64, 1), ("bf16", 128, 1), ("bf16", 128, 2), ("f16", 128, 0)])
+def test_windowquant_segments_many_queries(dtype, d, jensen):
+    """Chunk-shaped attention over the WindowQuant layout: 300 query rows per query head
+    (GQA 4/2) over FP16 + INT4 + INT2 segments built from the device gather lists, plus an
+    unquantized current chunk; every row against the oracle."""
+    H, Hq, N, window = 2, 4, 3000 - 7, 32
+    rng = np.random.default_rng(41 + d)
+    scale = np.exp(rng.normal(0, 0.5, (H, 1, d))).astype(np.float32)
+    k = torch.from_numpy((rng.standard_normal((1, H, N, d)) * scale).astype(np.float32)).to(TORCH_DT[dtype])
+    v = torch.from_numpy(rng.standard_normal((1, H, N, d)).astype(np.float32)).to(TORCH_DT[dtype])
+    t = torch.from_numpy(rng.standard_normal(d).astype(np.float32))
+    asg = kvq.assign_windows(k.cuda(), t.cuda(), 10, 30, window=window)
+    torch.cuda.synchronize()
+    bits, order = asg.bits[0].cpu().numpy(), asg.order[0].cpu().numpy()
+    og, oct_ = oracle.window_groups(bits, order, N, window)
+    assert np.array_equal(asg.groups[0].cpu().numpy(), og)
+    rows = asg.class_rows()
+    gsegs, osegs = [], []
+    for ci, b in enumerate((16, 4, 2)):
+        a, e = rows[b]
+        n_tok = int(oct_[ci])
+        gseg, oseg = make_pair(b, dtype, 1, H, d, capacity=n_tok, Gk=window, kgroup_capacity=e - a)
+        kvq.quantize_append(gseg, k.cuda(), v.cuda(), n_new=n_tok, src_groups=asg.class_list(b))
+        oracle.append(oseg, f32(k), f32(v), groups=og[a:e])
+        assert_segments_equal(gseg, oseg)
+        gsegs.append(gseg)
+        osegs.append(oseg)
+    q = _rand((1, Hq, 300, d), dtype, 91)
+    kc = _rand((1, H, 150, d), dtype, 92, 2.0)
+    vc = _rand((1, H, 150, d), dtype, 93)
+    go, gl = gpu_attention(q, gsegs, kc, vc, n_kv_heads=H, jensen=jensen)
+    oo, ol = oracle_attention(q, osegs, kc, vc, n_kv_heads=H, jensen=jensen)
+    assert np.abs(go - oo).max() <= TOL
+    assert np.abs(gl - ol).max() <= TOL

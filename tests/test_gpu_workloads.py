@@ -41,8 +41,10 @@ def _rows(n_q, stride):
     return rows
 
 
-def _check_step(name, stride):
+def _check_step(name, stride, jensen=None):
     w = workloads.WORKLOADS[name]
+    if jensen is not None:
+        w = workloads.scaled(w, jensen=jensen)
     step = ChunkStep(w, n_copies=1)
     data = step.data
     oseg = _oracle_cache(w, data)
@@ -72,43 +74,56 @@ def test_video_chunk_int2_h12_d128():
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-def test_decode_gqa32x8_32k(bits):
-    """Decode, GQA 32/8, 8 sequences x 32,768 cached tokens: every query row."""
-    _check_step("decode_gqa32x8_int%d_32k" % bits, stride=1)
+@pytest.mark.parametrize("jensen", [0, 1])
+def test_decode_gqa32x8_32k(bits, jensen):
+    """Decode, GQA 32/8, 8 sequences x 32,768 cached tokens: every query row, with the
+    Jensen correction off and on."""
+    _check_step("decode_gqa32x8_int%d_32k" % bits, stride=1, jensen=jensen)
 
 
 @pytest.mark.timeout(600)
 def test_rollout_chunk_int2_h40_d128():
-    """Long rollout: 74,880 cached INT2 tokens + 4,680 current, 40 heads; sampled rows."""
-    _check_step("rollout_chunk_int2_h40_d128", stride=390)
+    """Long rollout: 74,880 cached INT2 tokens + 4,680 current, 40 heads; every 127th
+    query row and the last one, so every 256-row block of every head holds at least two
+    checked rows."""
+    w = workloads.WORKLOADS["rollout_chunk_int2_h40_d128"]
+    rows = _rows(w.n_q, 127)
+    assert {r // 256 for r in rows} == set(range(-(-w.n_q // 256)))
+    _check_step("rollout_chunk_int2_h40_d128", stride=127)
 
 
 @pytest.mark.parametrize("jensen", [0, 1])
 def test_windowquant_fp16_gqa14x2_d64(jensen):
-    """WindowQuant end to end: window scores and FP16/INT4/INT2 assignment (bit-exact), the
-    three grouped segments built by gathered appends (bit-exact), then one decode query of
-    14 heads over the mixed-precision cache."""
+    """WindowQuant end to end: window scores, FP16/INT4/INT2 assignment and the grouped
+    layout's gather lists (bit-exact), the three grouped segments built by gathered appends
+    from the device lists (bit-exact), then one decode query of 14 heads over the
+    mixed-precision cache."""
     w = workloads.WORKLOADS["windowquant_fp16_gqa14x2_d64"]
     data = workloads.generate(w)
     k, v = data["cache_k"], data["cache_v"]                 # [1][2][19600][64] fp16
     N, W = w.n_cache, w.n_windows
-    n16, n4 = kvq.window_budget(W, w.pct_fp16, w.pct_int4)
-    assert (n16, n4, W - n16 - n4) == (61, 184, 368)
-    bits, order, score = kvq.assign_windows(k[0].cuda(), data["text"].cuda(), n16, n4)
+    asg = kvq.assign_windows(k.cuda(), data["text"].cuda(), w.pct_fp16, w.pct_int4, window=w.window)
+    assert (asg.n_fp16, asg.n_int4, W - asg.n_fp16 - asg.n_int4) == (61, 184, 368)
     torch.cuda.synchronize()
     osc = oracle.window_scores(f32(k[0]), data["text"].numpy(), w.window)
-    ob, oo = oracle.assign_windows(osc, n16, n4)
-    np.testing.assert_array_max_ulp(score.cpu().numpy(), osc, maxulp=4)
-    bits_h, order_h = bits.cpu().numpy(), order.cpu().numpy()
-    assert np.array_equal(bits_h, ob) and np.array_equal(order_h, oo)
+    ob, oo = oracle.assign_windows(osc, asg.n_fp16, asg.n_int4)
+    og, oct_ = oracle.window_groups(ob, oo, N, w.window)
+    np.testing.assert_array_max_ulp(asg.score[0].cpu().numpy(), osc, maxulp=4)
+    assert np.array_equal(asg.bits[0].cpu().numpy(), ob) and np.array_equal(asg.order[0].cpu().numpy(), oo)
+    assert np.array_equal(asg.groups[0].cpu().numpy(), og)
+    class_tokens = asg.class_tokens[0].cpu().numpy()
+    assert np.array_equal(class_tokens, oct_)
 
-    classes = kvq.window_groups(order_h.tolist(), bits_h.tolist(), N, w.window)
+    rows = asg.class_rows()
+    kd, vd = k.cuda(), v.cuda()
     gsegs, osegs = [], []
-    for b in (16, 4, 2):
-        groups, n_tok = classes[b]
+    for ci, b in enumerate((16, 4, 2)):
+        a, e = rows[b]
+        n_tok = int(class_tokens[ci])
         gseg, oseg = make_pair(b, "f16", 1, w.n_kv_heads, w.head_dim, capacity=n_tok, Gk=w.window,
-                               kgroup_capacity=len(groups))
-        append_both(gseg, oseg, k, v, groups=groups)
+                               kgroup_capacity=e - a)
+        kvq.quantize_append(gseg, kd, vd, n_new=n_tok, src_groups=asg.class_list(b))
+        oracle.append(oseg, f32(k), f32(v), groups=og[a:e])
         assert_segments_equal(gseg, oseg)
         gsegs.append(gseg)
         osegs.append(oseg)
