@@ -67,7 +67,8 @@ class KvqAttnArgs(ctypes.Structure):
 
 
 SYMBOLS = ("kvq_quantize_append", "kvq_window_budget", "kvq_assign_windows", "kvq_attention_workspace_size",
-           "kvq_chunk_attention", "kvq_probe_hbm_read", "kvq_status_string", "kvq_abi_version")
+           "kvq_chunk_attention", "kvq_chunk_attention_noalloc", "kvq_probe_hbm_read", "kvq_status_string",
+           "kvq_abi_version")
 
 _lib = None
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
         L.kvq_attention_workspace_size.restype = ctypes.c_int
         L.kvq_chunk_attention.argtypes = [ctypes.POINTER(KvqAttnArgs), P]
         L.kvq_chunk_attention.restype = ctypes.c_int
+        L.kvq_chunk_attention_noalloc.argtypes = [ctypes.POINTER(KvqAttnArgs), P]
+        L.kvq_chunk_attention_noalloc.restype = ctypes.c_int
         L.kvq_probe_hbm_read.argtypes = [P, ctypes.c_size_t, P, P]
         L.kvq_probe_hbm_read.restype = ctypes.c_int
         L.kvq_status_string.argtypes = [ctypes.c_int]
@@ -307,6 +310,27 @@ def chunk_attention(q: torch.Tensor, segments: Sequence[Segment], k_cur: Optiona
     a, arr = _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out,
                         _TORCH_DT[out.dtype], lse, workspace)
     _check(lib().kvq_chunk_attention(ctypes.byref(a), _stream(stream)), "kvq_chunk_attention")
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 72 << 20   # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def chunk_attention_noalloc(q: torch.Tensor, segments: Sequence[Segment], out: torch.Tensor,
+                            k_cur: Optional[torch.Tensor] = None, v_cur: Optional[torch.Tensor] = None,
+                            n_kv_heads: Optional[int] = None, softmax_scale: float = 0.0,
+                            jensen: int = JENSEN_TAYLOR2, lse: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """kvq_chunk_attention_noalloc: chunk_attention with the partials in the library's static
+    per-GPU scratch; the caller passes the output, nothing is allocated here or in the call.
+    Calls that overlap on one GPU race on that scratch."""
+    _dev(q, "q"); _dev(out, "out")
+    if k_cur is not None:
+        _dev(k_cur, "k_cur"); _dev(v_cur, "v_cur")
+    if n_kv_heads is None and not segments and k_cur is not None:
+        n_kv_heads = k_cur.shape[1]
+    a, arr = _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out,
+                        _TORCH_DT[out.dtype], lse, None)
+    _check(lib().kvq_chunk_attention_noalloc(ctypes.byref(a), _stream(stream)), "kvq_chunk_attention_noalloc")
     return out
 
 

@@ -2,6 +2,10 @@
 // then kernel launches on the caller's stream. Nothing here allocates, frees or waits.
 #include <math.h>
 
+#include <mutex>
+
+#include <hip/hip_runtime.h>
+
 #include "kvq.h"
 #include "kvq_internal.h"
 
@@ -77,6 +81,39 @@ bool use_decode(const kvq_attn_args *a, long long n_total) {
     return kvq::decode_eligible(a->dtype, a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, bits, n,
                                 a->n_cur, (int)n_total);
 }
+
+// Scratch of kvq_chunk_attention_noalloc: the partial results that kvq_chunk_attention
+// keeps in the caller's workspace. Every GPU the library runs on holds its own copy of this
+// array until the process ends. In host code its name is only a stand-in for the symbol:
+// the device address comes from hipGetSymbolAddress, once per device (with that device
+// current), and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's address of the scratch array (looked up on its first use).
+kvq_status scratch_address(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return KVQ_ERR_HIP;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || ptr == nullptr) {
+            (void)hipGetLastError();
+            return KVQ_ERR_HIP;
+        }
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+
+kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static);
 
 }  // namespace
 
@@ -207,6 +244,20 @@ kvq_status kvq_attention_workspace_size(const kvq_attn_args *a, size_t *bytes) {
 }
 
 kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
+    return run_attention(a, stream, false);
+}
+
+kvq_status kvq_chunk_attention_noalloc(const kvq_attn_args *a, void *stream) {
+    return run_attention(a, stream, true);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Checks, plan, launches. With use_static the partials go to this device's static scratch
+// array instead of the caller's workspace (which is then ignored).
+kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) {
     long long n_total = 0;
     kvq_status st = check_attention_shape(a, &n_total);
     if (st != KVQ_OK) return st;
@@ -219,8 +270,14 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
     kvq::AttnPlan plan;
     kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, decode, &plan);
     const size_t need = plan.workspace_bytes;
-    if (need > 0 && (!a->workspace || a->workspace_bytes < need || !aligned16(a->workspace)))
+    void *workspace = a->workspace;
+    if (use_static) {
+        if (need > KVQ_NOALLOC_SCRATCH_BYTES) return KVQ_ERR_WORKSPACE;
+        workspace = nullptr;
+        if (need > 0 && (st = scratch_address(&workspace)) != KVQ_OK) return st;
+    } else if (need > 0 && (!workspace || a->workspace_bytes < need || !aligned16(workspace))) {
         return KVQ_ERR_WORKSPACE;
+    }
 
     kvq::AttnParams p;
     p.q = a->q;
@@ -269,9 +326,9 @@ kvq_status kvq_chunk_attention(const kvq_attn_args *a, void *stream) {
     p.tok_pad = plan.tok_pad;
     p.quota = plan.quota;
     p.work = plan.work;
-    p.partial = reinterpret_cast<float *>(a->workspace);
+    p.partial = reinterpret_cast<float *>(workspace);
     p.decode = decode ? 1 : 0;
     return kvq::launch_attention(p, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
 }
 
-}  // extern "C"
+}  // namespace

@@ -31,8 +31,9 @@
  *    nothing is enqueued and no output, buffer or descriptor is changed.
  *    KVQ_ERR_HIP reports a launch failure (hipGetLastError after the launch); device
  *    faults surface at the caller's next synchronization.
- *  - No global mutable state: calls are reentrant and may run on several streams
- *    at once if they touch disjoint buffers. No C++ exception crosses this ABI.
+ *  - No global mutable state (except the static scratch of kvq_chunk_attention_noalloc,
+ *    see there): calls are reentrant and may run on several streams at once if they
+ *    touch disjoint buffers. No C++ exception crosses this ABI.
  *  - Elements of fp16 / bf16 inputs must lie within fp16's finite range
  *    (|x| <= 65504); step and zero are stored in fp16.
  */
@@ -252,6 +253,26 @@ typedef struct kvq_attn_args {
     void *workspace;
     size_t workspace_bytes;
 } kvq_attn_args;
+
+/*
+ * kvq_chunk_attention_noalloc -- kvq_chunk_attention for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): the same checks, kernels and results, but the partial results go to a
+ * static device array of the library (KVQ_NOALLOC_SCRATCH_BYTES per GPU, held from the
+ * first use on that GPU until the process ends) instead of a caller workspace;
+ * workspace and workspace_bytes are ignored. The call allocates and frees nothing. Its
+ * first call on a device looks up the array's address there (with that device current).
+ * All calls on one GPU share that GPU's array: calls that overlap in time on one GPU (two
+ * streams, or two host threads) race on it and must be serialized by the caller. The
+ * array needs no clearing: every partial a call reads was written earlier in the same
+ * call.
+ * Errors: as kvq_chunk_attention; KVQ_ERR_WORKSPACE when the call needs more scratch than
+ * the array holds (kvq_attention_workspace_size > KVQ_NOALLOC_SCRATCH_BYTES; on MI355X the
+ * largest plan needs 69.2 MB, so no valid call is refused there); KVQ_ERR_HIP when the
+ * array's address cannot be looked up.
+ */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+kvq_status kvq_chunk_attention_noalloc(const kvq_attn_args *args, void *stream);
 
 /* Bytes of workspace kvq_chunk_attention needs for these arguments (pointers are not
  * read). Host only; returns KVQ_ERR_ARG / KVQ_ERR_UNSUPPORTED for arguments that
