@@ -487,8 +487,9 @@ def main():
     ap.add_argument("--no-probe-hbm", action="store_true",
                     help="skip the HBM read/copy probe (its copies would mix into a counter run's copy calibration)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
-    ap.add_argument("--jensen", type=int, choices=(0, 1, 2), default=None,
-                    help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic); default: the workload's")
+    ap.add_argument("--jensen", type=int, choices=(0, 1, 2, 3), default=None,
+                    help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic, 3 all orders); "
+                         "default: the workload's")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the reference dispatch "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")

@@ -29,7 +29,7 @@ LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(HERE, "libkvq.so")
 
 F32, F16, BF16 = 0, 1, 2
 OK, ERR_ARG, ERR_UNSUPPORTED, ERR_CAPACITY, ERR_WORKSPACE, ERR_HIP = 0, -1, -2, -3, -4, -5
-JENSEN_OFF, JENSEN_TAYLOR2, JENSEN_ISO = 0, 1, 2
+JENSEN_OFF, JENSEN_TAYLOR2, JENSEN_ISO, JENSEN_EXACT = 0, 1, 2, 3
 MAX_SEGMENTS = 8
 
 _TORCH_DT = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}

@@ -14,8 +14,9 @@ namespace {
 bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool half_dtype(int32_t d) { return d == KVQ_F16 || d == KVQ_BF16; }
 bool any_dtype(int32_t d) { return d == KVQ_F32 || d == KVQ_F16 || d == KVQ_BF16; }
-// the kernels compare the jensen field with this value (JENSEN_ISO)
+// the kernels compare the jensen field with these values (JENSEN_ISO, JENSEN_EXACT)
 static_assert(KVQ_JENSEN_ISO == 2, "isotropic Jensen form value");
+static_assert(KVQ_JENSEN_EXACT == 3, "all-orders Jensen form value");
 
 kvq_status check_segment_shape(const kvq_segment &s) {
     if (s.bits != 2 && s.bits != 4 && s.bits != 16) return KVQ_ERR_UNSUPPORTED;
@@ -51,7 +52,8 @@ kvq_status check_attention_shape(const kvq_attn_args *a, long long *n_total) {
     if (a->n_segs < 0) return KVQ_ERR_ARG;
     if (a->n_segs > KVQ_MAX_SEGMENTS) return KVQ_ERR_UNSUPPORTED;
     if (a->n_segs > 0 && !a->segs) return KVQ_ERR_ARG;
-    if (a->jensen != KVQ_JENSEN_OFF && a->jensen != KVQ_JENSEN_TAYLOR2 && a->jensen != KVQ_JENSEN_ISO)
+    if (a->jensen != KVQ_JENSEN_OFF && a->jensen != KVQ_JENSEN_TAYLOR2 && a->jensen != KVQ_JENSEN_ISO &&
+        a->jensen != KVQ_JENSEN_EXACT)
         return KVQ_ERR_UNSUPPORTED;
     if (!any_dtype(a->out_dtype)) return KVQ_ERR_UNSUPPORTED;
     if (!(a->softmax_scale >= 0.0f) || isinf(a->softmax_scale)) return KVQ_ERR_ARG;
@@ -315,7 +317,9 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
     const double scale = a->softmax_scale > 0.0f ? (double)a->softmax_scale : 1.0 / sqrt((double)a->head_dim);
     const double log2e = 1.4426950408889634074;
     p.scale_log2 = (float)(scale * log2e);
-    p.beta_log2 = a->jensen != KVQ_JENSEN_OFF ? (float)(scale * scale / 24.0 * log2e) : 0.0f;
+    p.beta_log2 = a->jensen == KVQ_JENSEN_OFF ? 0.0f
+                  : a->jensen == KVQ_JENSEN_EXACT ? 1.0f : (float)(scale * scale / 24.0 * log2e);
+    p.half_scale = (float)(scale / 2.0);
     p.jensen = a->jensen;
     p.out = a->out;
     p.out_dtype = a->out_dtype;

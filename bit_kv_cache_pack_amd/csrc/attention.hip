@@ -473,6 +473,40 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
     for (int j = 0; j < 16; ++j) cx.btab[(8 * (j / 4) + 4 * hh + (j % 4)) * 32 + r32] = acc[j];
 }
 
+// The all-orders Jensen terms of K-groups g0 .. g0+31 for the wave's 32 queries, log2
+// domain: sum over channels of log2(sinh(a) / a), a = (tau / 2) |q_c| step_c. Lane (r32, hh)
+// sums its query's channels of half hh (the positions it holds q at) for one group at a
+// time; the two halves meet through the lane L ^ 32 exchange.
+template <int HD, bool BF16>
+__device__ __forceinline__ void beta_block_exact(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0,
+                                                 float half_scale) {
+    typedef Ctx<HD, BF16> C;
+    const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
+    const int n = min(32, sg.n_kgroups - g0);
+    for (int gi = 0; gi < n; ++gi) {
+        const uint32_t *km = sg.k_meta + (bh * sg.kgroup_capacity + g0 + gi) * HD + 2 * hh;
+        float sum = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            // opaque: the query values are taken apart here, per group, not hoisted out of the
+            // group loop (64 more live registers)
+            u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+            asm volatile("" : "+v"(qw));
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                // channels 4k + 2hh (element k) and 4k + 2hh + 1 (element 4 + k) of block ks
+                const u32x2 v = *reinterpret_cast<const u32x2 *>(km + 16 * ks + 4 * k);
+                const float q0 = C::E::val((qw[k / 2] >> (16 * (k % 2))) & 0xffffu);
+                const float q1 = C::E::val((qw[(4 + k) / 2] >> (16 * (k % 2))) & 0xffffu);
+                sum += log2_sinhc(half_scale * __builtin_fabsf(q0) * f16_bits_to_f32(v.x & 0xffffu));
+                sum += log2_sinhc(half_scale * __builtin_fabsf(q1) * f16_bits_to_f32(v.y & 0xffffu));
+            }
+        }
+        sum += other_half(sum);
+        if (hh == 0) cx.btab[gi * 32 + r32] = sum;
+    }
+}
+
 // The Jensen sum of group row rr (0..31) of the current block for this lane's query.
 template <int HD, bool BF16>
 __device__ __forceinline__ float beta_of(const Ctx<HD, BF16> &cx, int rr) {
@@ -706,7 +740,9 @@ __device__ __forceinline__ void softmax_pv(Ctx<HD, BF16> &cx, const uint16_t *vl
     cx.l += ps;
 }
 
-template <int HD, bool BF16>
+// EXACT: the all-orders Jensen form (its direct per-channel evaluation in its own instance,
+// so the other forms keep their register allocation).
+template <int HD, bool BF16, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
@@ -812,7 +848,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
             if (wave_ok) {
                 if (cur.kind() == TILE_PACKED) {
-                    if (cur.batch()) beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, p.jensen == JENSEN_ISO);
+                    if (cur.batch()) {
+                        if constexpr (EXACT)
+                            beta_block_exact<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, p.half_scale);
+                        else
+                            beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, p.jensen == JENSEN_ISO);
+                    }
                     if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.jrow());
                 } else {
                     cx.beta = 0.f;
@@ -1020,7 +1061,10 @@ __global__ __launch_bounds__(HD) void combine_kernel(AttnParams p) {
 template <int HD, bool BF16>
 hipError_t launch_t(const AttnParams &p, hipStream_t s) {
     const unsigned n_wg = (unsigned)((p.work + p.quota - 1) / p.quota);
-    hipLaunchKernelGGL((attention_kernel<HD, BF16>), dim3(n_wg), dim3(kThreads), 0, s, p);
+    if (p.jensen == JENSEN_EXACT)
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, true>), dim3(n_wg), dim3(kThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, false>), dim3(n_wg), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.quota % p.tok_pad == 0) return e;   // no row block was split
     hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / (HD / 8))), dim3(256), 0, s, p);

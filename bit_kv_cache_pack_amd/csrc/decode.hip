@@ -296,6 +296,29 @@ __device__ __forceinline__ void kmeta_block(const u32x4 (&km)[4 * DGeo<HD>::NBL]
 
 // sum over the row's channels of (q_c step_c)^2, for the lane's row; in the isotropic
 // form |q|^2 * mean_c step_c^2 instead
+// The all-orders form: sum over the row's channels of log2(sinh(a) / a), a = (tau / 2)
+// |q_c| step_c (log2 domain already).
+template <int HD, bool BF16>
+__device__ __forceinline__ float jensen_sum_exact(const DCtx<HD, BF16> &cx, float half_scale) {
+    typedef DGeo<HD> G;
+    float acc = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < G::KS; ++ks) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, cx.qb[ks]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int pos = 8 * (ks & 1) + i;
+            const int ch = 16 * (ks >> 1) + swap_pos(pos);
+            const float qv = Elem<BF16>::val((qw[i / 2] >> (16 * (i % 2))) & 0xffffu);
+            const float st = mul_step(1.0f, cx.km[ch / 4][ch % 4]);
+            acc += log2_sinhc(half_scale * __builtin_fabsf(qv) * st);
+        }
+    }
+    acc += __shfl_xor(acc, 16);
+    acc += other_half(acc);
+    return acc;
+}
+
 template <int HD, bool BF16>
 __device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx, bool iso) {
     typedef DGeo<HD> G;
@@ -330,7 +353,7 @@ __device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx, bool iso) 
     return acc;
 }
 
-template <int HD, bool BF16>
+template <int HD, bool BF16, bool EXACT>
 __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const Step &st, const Step &nx,
                                              uint16_t *vt, const AttnParams &p, size_t bh) {
     typedef DGeo<HD> G;
@@ -343,8 +366,12 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     const int len = st.len;
     const bool nx_packed = nx.kind == ST_PACKED;
 
-    if (packed && st.new_group)
-        cx.beta = p.jensen ? p.beta_log2 * jensen_sum<HD, BF16>(cx, p.jensen == JENSEN_ISO) : 0.f;
+    if (packed && st.new_group) {
+        if constexpr (EXACT)
+            cx.beta = jensen_sum_exact<HD, BF16>(cx, p.half_scale);
+        else
+            cx.beta = p.jensen ? p.beta_log2 * jensen_sum<HD, BF16>(cx, p.jensen == JENSEN_ISO) : 0.f;
+    }
     if (!packed) cx.beta = 0.f;
 
     // ---- S^T = K^ Q^T: s[b][i] = logit of token 16 b + 4 j + i for row r16
@@ -540,7 +567,8 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     }
 }
 
-template <int HD, bool BF16>
+// EXACT: the all-orders Jensen form, in its own instance (as in the chunk kernel).
+template <int HD, bool BF16, bool EXACT>
 __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     typedef DGeo<HD> G;
     typedef typename DCtx<HD, BF16>::vec vec;
@@ -606,7 +634,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
         load_v<HD>(d, p, s0, bh);
     }
     while (s0.kind != ST_END) {
-        process_step<HD, BF16>(cx, d, s0, s1, vt, p, bh);
+        process_step<HD, BF16, EXACT>(cx, d, s0, s1, vt, p, bh);
         s0 = s1;
         s1 = uniform(wk.next(p, tb, te));
     }
@@ -663,7 +691,10 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
 template <int HD, bool BF16>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
     dim3 grid(p.n_split, p.batch * p.n_kv_heads);
-    hipLaunchKernelGGL((decode_kernel<HD, BF16>), grid, dim3(kDThreads), 0, s, p);
+    if (p.jensen == JENSEN_EXACT)
+        hipLaunchKernelGGL((decode_kernel<HD, BF16, true>), grid, dim3(kDThreads), 0, s, p);
+    else
+        hipLaunchKernelGGL((decode_kernel<HD, BF16, false>), grid, dim3(kDThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
     return launch_combine(p, s);

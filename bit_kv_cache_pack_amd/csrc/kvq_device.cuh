@@ -17,7 +17,7 @@ typedef __attribute__((ext_vector_type(2))) uint32_t u32x2;
 
 enum : int { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2 };
 // kvq_jensen values the kernels branch on
-enum : int { JENSEN_ISO = 2 };
+enum : int { JENSEN_ISO = 2, JENSEN_EXACT = 3 };
 
 constexpr int kWave = 64;
 

@@ -62,7 +62,9 @@ struct AttnParams {
     int32_t n_cur;
     int32_t n_total;               // history + current tokens
     float scale_log2;              // softmax scale * log2(e)
-    float beta_log2;               // scale^2 / 24 * log2(e) when Jensen is on, else 0
+    float beta_log2;               // scale^2 / 24 * log2(e) for the second-order forms, 1 for
+                                   // the all-orders one (computed in log2 units), else 0
+    float half_scale;              // scale / 2: a_c = half_scale |q_c| step_c (all-orders form)
     int32_t jensen;                // kvq_jensen
     void *out;
     int32_t out_dtype;

@@ -42,6 +42,30 @@ __device__ __forceinline__ int group_start(const int32_t *tab, int g) {
     typedef const __attribute__((address_space(1))) int32_t *gptr;
     return ((gptr)tab)[g];
 }
+// log2(sinh(a) / a) for a >= 0: the all-orders Jensen term of one key channel whose
+// logit noise is uniform on [-a, a] (E[exp(x)] = sinh(a) / a). Below a = 1 from the Taylor
+// series of ln(sinh a / a) in u = a^2 (six terms, the seventh below 1.6e-8); from 1 on as
+// a - ln(2a) + ln(1 - e^{-2a}), where nothing cancels. The second form is only evaluated
+// when some lane of the wave needs it.
+__device__ __forceinline__ float log2_sinhc(float a) {
+    constexpr float kLog2e = 1.4426950408889634f;
+    const float u = a * a;
+    float f = __builtin_fmaf(u, -1.80366e-7f, 2.1377799e-6f);   // -2^12 B12 / (12 * 12!), 1/467775
+    f = __builtin_fmaf(u, f, -2.6455026e-5f);                  // -1/37800
+    f = __builtin_fmaf(u, f, 3.5273369e-4f);                   // 1/2835
+    f = __builtin_fmaf(u, f, -5.5555556e-3f);                  // -1/180
+    f = __builtin_fmaf(u, f, 0.16666667f);                     // 1/6
+    f = f * u * kLog2e;
+    const bool big = a >= 1.0f;
+    if (__builtin_expect(__any(big), 0)) {
+        const float x = a * kLog2e;
+        const float t = __builtin_amdgcn_exp2f(-2.0f * x);     // e^{-2a}
+        const float g = x - 1.0f - __builtin_amdgcn_logf(a) + __builtin_amdgcn_logf(1.0f - t);
+        f = big ? g : f;
+    }
+    return f;
+}
+
 // value of lane L ^ 32
 __device__ __forceinline__ float other_half(float v) {
     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);

@@ -73,7 +73,12 @@ typedef enum kvq_jensen {
      * the query's norm, i.e. TAYLOR2 with every channel's step^2 replaced by its mean over
      * the group's channels (equal to TAYLOR2 when a group's steps are equal across
      * channels; the mean of TAYLOR2 over cyclic shifts of the step vector otherwise). */
-    KVQ_JENSEN_ISO = 2
+    KVQ_JENSEN_ISO = 2,
+    /* beta(i, g) = sum_c log(sinh(a_c) / a_c), a_c = tau * |q_ic| * step_gc / 2: the same
+     * uniform-noise model taken to all orders, log E[exp(tau q . e)] exactly (E[exp(x)] =
+     * sinh(a)/a for x uniform on [-a, a], channels independent); TAYLOR2 is its
+     * second-order term. */
+    KVQ_JENSEN_EXACT = 3
 } kvq_jensen;
 
 /*

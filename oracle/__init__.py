@@ -64,6 +64,7 @@ def _declare(L):
     L.orc_unpack_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P]; L.orc_unpack_row.restype = None
     L.orc_append.argtypes = [ctypes.c_int] * 11 + [P] * 7 + [P, P, I64, ctypes.c_int, P, ctypes.c_int]
     L.orc_append.restype = ctypes.c_int
+    L.orc_log_sinhc.argtypes = [F64]; L.orc_log_sinhc.restype = F64
     L.orc_attend_row.argtypes = [P, ctypes.c_int, P, P, P, I64, P, ctypes.c_int, F64, ctypes.c_int,
                                  P, P, P]
     L.orc_attend_row.restype = None
@@ -204,7 +205,8 @@ def attention(q: np.ndarray, segs: List[Dict], k_cur: Optional[np.ndarray] = Non
               scale: Optional[float] = None, jensen: int = 1, exact: bool = False,
               rows: Optional[Sequence[int]] = None, want_mass: bool = False):
     """A1-A3 in double. q float [B][Hq][nq][d]. jensen: 0 off, 1 the channel-weighted
-    second-order term, 2 its isotropic (query-norm) form. Returns (out [B][Hq][n_rows][d]
+    second-order term, 2 its isotropic (query-norm) form, 3 the same noise model to all
+    orders (sum over channels of log(sinh a / a)). Returns (out [B][Hq][n_rows][d]
     float64, lse [B][Hq][n_rows]) and, with want_mass, the softmax mass on cached tokens."""
     q = _c(q, np.float32)
     B, Hq, nq, d = q.shape
@@ -284,3 +286,8 @@ def window_groups(bits: np.ndarray, order: np.ndarray, n_tokens: int, window: in
     ct = np.zeros(3, np.int32)
     lib().orc_window_groups(_ptr(bits), _ptr(order), W, int(n_tokens), int(window), _ptr(groups), _ptr(ct))
     return groups, ct
+
+
+def log_sinhc(a: float) -> float:
+    """log(sinh(a) / a), a >= 0 (0 at a = 0)."""
+    return lib().orc_log_sinhc(float(a))

@@ -303,15 +303,32 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
  *   s_j = scale * q . k_j                            raw token (group < 0)
  *   beta(q, g) = scale^2 / 24 * sum_c q_c^2 * step_{g,c}^2    (jensen == 1)
  *   beta(q, g) = scale^2 / 24 * |q|^2 * mean_c step_{g,c}^2   (jensen == 2)
+ *   beta(q, g) = sum_c log(sinh(a_c) / a_c), a_c = scale |q_c| step_{g,c} / 2  (jensen == 3)
  * beta is half the variance of the logit noise scale * q . e when each key
  * channel's rounding error e_c is uniform on [-step/2, step/2] (variance step^2/12)
  * and independent: the second-order term of log E[exp(scale * q . e)], which is what
  * quantization noise adds to a cached key's logit on average [JB]. The second form
  * is the one [JB] states through the query's norm: each channel's step^2 replaced by
  * its mean over the group's channels (the two agree when the steps are equal across
- * channels).
+ * channels). The third is the same model taken to all orders: log E[exp(scale q . e)]
+ * itself, since E[exp(x)] = sinh(a)/a for x uniform on [-a, a] and the channels are
+ * independent; its second-order term is the first form.
  * out_c = sum_j softmax(s)_j v_jc; lse = log sum_j exp(s_j); mass = softmax mass
  * on tokens with group >= 0 (the quantized history). Everything in double. */
+/* log(sinh(a) / a) for a >= 0: the log of E[exp(x)] for x uniform on [-a, a]. Near 0
+ * it is taken from its Taylor series (u/6 - u^2/180 + u^3/2835, u = a^2), for large a
+ * from sinh(a) = e^a (1 - e^{-2a}) / 2, which keeps it finite. */
+double orc_log_sinhc(double a)
+{
+    if (a < 0.01) { /* sinh(a)/a - 1 would cancel: its series, next term a^8/37800 < 3e-21 */
+        const double u = a * a;
+        return u / 6.0 - u * u / 180.0 + u * u * u / 2835.0;
+    }
+    if (a > 20.0)
+        return a - log(2.0 * a) + log1p(-exp(-2.0 * a));
+    return log(sinh(a) / a);
+}
+
 void orc_attend_row(const double *q, int d, const double *K, const double *V,
                     const int32_t *tok_group, int64_t N, const double *step_sq, int n_groups,
                     double scale, int jensen, double *out, double *lse, double *mass)
@@ -319,16 +336,20 @@ void orc_attend_row(const double *q, int d, const double *K, const double *V,
     double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     double *beta = (double *)malloc(sizeof(double) * (size_t)(n_groups > 0 ? n_groups : 1));
     for (int g = 0; g < n_groups; ++g) {
-        double acc = 0.0, qq = 0.0, ss = 0.0;
+        double acc = 0.0, qq = 0.0, ss = 0.0, lg = 0.0;
         for (int c = 0; c < d; ++c) {
             acc += q[c] * q[c] * step_sq[(size_t)g * d + c];
             qq += q[c] * q[c];
             ss += step_sq[(size_t)g * d + c];
+            if (jensen == 3) /* a_c = scale |q_c| step_c / 2: half-width of scale q_c e_c */
+                lg += orc_log_sinhc(scale * fabs(q[c]) * sqrt(step_sq[(size_t)g * d + c]) / 2.0);
         }
         if (jensen == 1)
             beta[g] = scale * scale / 24.0 * acc;
         else if (jensen == 2)
             beta[g] = scale * scale / 24.0 * qq * (ss / d);
+        else if (jensen == 3)
+            beta[g] = lg;
         else
             beta[g] = 0.0;
     }

@@ -127,7 +127,7 @@ def _attn(segs=None, **kw):
     (dict(n_q_heads=3), kvq.ERR_ARG),
     (dict(n_segs=9), kvq.ERR_UNSUPPORTED),
     (dict(jensen=5), kvq.ERR_UNSUPPORTED),
-    (dict(jensen=3), kvq.ERR_UNSUPPORTED),
+    (dict(jensen=4), kvq.ERR_UNSUPPORTED),
     (dict(jensen=-1), kvq.ERR_UNSUPPORTED),
     (dict(out_dtype=9), kvq.ERR_UNSUPPORTED),
     (dict(q=None), kvq.ERR_ARG),

@@ -110,7 +110,7 @@ def _attention_case(bits, dtype, B, Hq, Hkv, d, appends, n_cur, n_q, jensen, see
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("jensen", [0, 1, 2])
+@pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_attention_chunk_small(bits, jensen):
     go, gl, oo, ol = _attention_case(bits, "bf16", 1, 2, 2, 128, appends=(200, 200), n_cur=100, n_q=150,
                                      jensen=jensen, seed=7)
@@ -120,7 +120,7 @@ def test_attention_chunk_small(bits, jensen):
 
 
 @pytest.mark.parametrize("d", [64, 128])
-@pytest.mark.parametrize("jensen", [0, 1, 2])
+@pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_attention_gqa_decode_splits(d, jensen):
     """GQA decode: one query per head, rows packed per KV head, token splits + combine."""
     go, gl, oo, ol = _attention_case(2, "bf16", 2, 8, 2, d, appends=(1500, 700), n_cur=0, n_q=1, jensen=jensen,
@@ -165,7 +165,7 @@ def test_attention_whole_row_blocks_half_outputs(out_dtype):
     assert np.abs(gl - ol).max() <= TOL
 
 
-@pytest.mark.parametrize("jensen", [0, 1, 2])
+@pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_tiny_workload(jensen):
     w = workloads.WORKLOADS["tiny_int2_h1_d64"]
     data = workloads.generate(w)
@@ -223,7 +223,8 @@ def test_windows_many_layers_one_launch(N):
     _check_windows(asg, k, t, N)
 
 
-@pytest.mark.parametrize("dtype,d,jensen", [("f16", 64, 1), ("bf16", 128, 1), ("bf16", 128, 2), ("f16", 128, 0)])
+@pytest.mark.parametrize("dtype,d,jensen", [("f16", 64, 1), ("bf16", 128, 1), ("bf16", 128, 2), ("f16", 128, 0),
+                                            ("bf16", 64, 3)])
 def test_windowquant_segments_many_queries(dtype, d, jensen):
     """Chunk-shaped attention over the WindowQuant layout: 300 query rows per query head
     (GQA 4/2) over FP16 + INT4 + INT2 segments built from the device gather lists, plus an

@@ -68,13 +68,15 @@ def _check_step(name, stride, jensen=None):
         assert_segments_equal(gseg, oseg)
 
 
-def test_video_chunk_int2_h12_d128():
-    """Video chunk step: 18,720 cached INT2 tokens + 4,680 current, 4,680 queries x 12 heads."""
-    _check_step("video_chunk_int2_h12_d128", stride=37)
+@pytest.mark.parametrize("jensen", [1, 3])
+def test_video_chunk_int2_h12_d128(jensen):
+    """Video chunk step: 18,720 cached INT2 tokens + 4,680 current, 4,680 queries x 12 heads
+    (the second-order and the all-orders Jensen forms)."""
+    _check_step("video_chunk_int2_h12_d128", stride=37, jensen=jensen)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("jensen", [0, 1])
+@pytest.mark.parametrize("jensen", [0, 1, 3])
 def test_decode_gqa32x8_32k(bits, jensen):
     """Decode, GQA 32/8, 8 sequences x 32,768 cached tokens: every query row, with the
     Jensen correction off and on."""
