@@ -48,8 +48,9 @@ def log(*a):
 class ChunkStep:
     """Attention of the current chunk over the packed cache + the chunk's quantize-append."""
 
-    def __init__(self, w: workloads.Workload, n_copies: int = 1):
+    def __init__(self, w: workloads.Workload, n_copies: int = 1, fused: bool = True):
         self.w = w
+        self.fused = fused   # the append in the attention's own call (append_dst) or after it
         t0 = time.time()
         data = workloads.generate(w)
         log("generated inputs in %.1fs" % (time.time() - t0))
@@ -113,11 +114,12 @@ class ChunkStep:
         seg.reset(*self.base)
         if events is not None:
             events[0].record()
+        fused = self.append and self.fused
         kvq.chunk_attention(self.q, [seg], self.k_cur, self.v_cur, jensen=self.w.jensen, out=self.out,
-                            workspace=self.ws)
+                            workspace=self.ws, append_to=seg if fused else None)
         if events is not None:
             events[1].record()
-        if self.append:
+        if self.append and not fused:
             kvq.quantize_append(seg, self.k_cur, self.v_cur)
         if events is not None:
             events[2].record()
@@ -386,27 +388,42 @@ def host_cpu():
     return {"cpu_model": model, "nproc": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
-def measure_chunk(args, w: workloads.Workload, copies: int = 0):
-    """Warm-ups, then exactly args.steps timed steps between device synchronizations; returns
-    the config's record (step time, value, roofline of the attention) and the step."""
-    # decode caches can sit in the 256 MB last-level cache: rotate copies > 2x that size
-    if copies == 0:
-        copies = 1 if w.n_cur else 4
-    step = ChunkStep(w, n_copies=copies)
-    log("%s: cache built, %d tokens, %d K-groups per head, %d copies" % (w.name, step.base[0], step.base[1], copies))
-    for _ in range(args.warmup):
+def time_steps(step: ChunkStep, steps: int, warmup: int):
+    """Warm-ups, then exactly ``steps`` timed steps between device synchronizations: wall ms
+    per step and, per step, the event times of the attention call and of the separate
+    append (0 when the append is in the attention's call)."""
+    for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(args.steps):
+    for i in range(steps):
         step.run(evs[i])
     torch.cuda.synchronize()
     t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    attn_ms = [e[0].elapsed_time(e[1]) for e in evs]
-    app_ms = [e[1].elapsed_time(e[2]) for e in evs]
+    return ((t1 - t0) * 1e3 / steps, [e[0].elapsed_time(e[1]) for e in evs],
+            [e[1].elapsed_time(e[2]) for e in evs])
+
+
+def measure_chunk(args, w: workloads.Workload, copies: int = 0):
+    """The config's record: step time, value, and the roofline of the attention call as the
+    step makes it; with a current chunk also the same step with the append as a launch of
+    its own (``separate``: the attention alone, and the append alone)."""
+    # decode caches can sit in the 256 MB last-level cache: rotate copies > 2x that size
+    if copies == 0:
+        copies = 1 if w.n_cur else 4
+    step = ChunkStep(w, n_copies=copies, fused=args.append == "fused")
+    log("%s: cache built, %d tokens, %d K-groups per head, %d copies" % (w.name, step.base[0], step.base[1], copies))
+    separate = None
+    if w.n_cur:
+        # the other way of running the append, first (its warm-ups also warm the fused step)
+        step.fused = args.append != "fused"
+        s_ms, s_attn, s_app = time_steps(step, args.steps, args.warmup)
+        separate = {"mode": "fused" if step.fused else "separate", "ms_per_step": round(s_ms, 4),
+                    "attention_ms": round(float(np.mean(s_attn)), 4), "append_ms": round(float(np.mean(s_app)), 4)}
+        step.fused = args.append == "fused"
+    ms_step, attn_ms, app_ms = time_steps(step, args.steps, args.warmup)
     attn_avg = float(np.mean(attn_ms))
     app_avg = float(np.mean(app_ms))
     default_mode = w.jensen == workloads.WORKLOADS[w.name].jensen   # stored counters: the workload's mode
@@ -441,12 +458,15 @@ def measure_chunk(args, w: workloads.Workload, copies: int = 0):
                       "ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
                       "ms_p90": round(float(np.percentile(attn_ms, 90)), 4), "tflops": round(attn_tflops, 2),
                       "kv_gbps": round(kvb / (attn_avg * 1e-3) / 1e9, 1), "kv_bytes": kvb, "flops": flops},
-        "append": {"ms": round(app_avg, 4), "ms_median": round(float(np.median(app_ms)), 4),
-                   "bytes": step.append_bytes(),
-                   "gbps": round(step.append_bytes() / (app_avg * 1e-3) / 1e9, 1) if step.append else None,
-                   "hbm_frac": round(step.append_bytes() / (app_avg * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
-                   if step.append else None},
+        "append": {"mode": args.append if step.append else None, "ms": round(app_avg, 4),
+                   "ms_median": round(float(np.median(app_ms)), 4), "bytes": step.append_bytes()},
     }
+    if separate is not None:
+        rec["other_append_mode"] = separate
+        app_sep = app_avg if args.append != "fused" else separate["append_ms"]
+        rec["append"]["separate_launch_ms"] = round(app_sep, 4)
+        rec["append"]["separate_launch_gbps"] = round(step.append_bytes() / (app_sep * 1e-3) / 1e9, 1)
+        rec["append"]["separate_launch_hbm_frac"] = round(step.append_bytes() / (app_sep * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)
     return rec, step
 
 
@@ -487,6 +507,9 @@ def main():
     ap.add_argument("--no-probe-hbm", action="store_true",
                     help="skip the HBM read/copy probe (its copies would mix into a counter run's copy calibration)")
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated per step (0: auto)")
+    ap.add_argument("--append", choices=("fused", "separate"), default="fused",
+                    help="the current chunk's quantize-append in the attention's own call (append_dst) or "
+                         "as a launch of its own after it")
     ap.add_argument("--jensen", type=int, choices=(0, 1, 2, 3), default=None,
                     help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic, 3 all orders); "
                          "default: the workload's")
@@ -519,6 +542,8 @@ def main():
            "warmup": args.warmup, "ms_per_step": rec["ms_per_step"], "higher_is_better": True,
            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic", "config": rec["config"],
            "roofline": rec["roofline"], "attention": rec["attention"], "append": rec["append"]}
+    if "other_append_mode" in rec:
+        res["other_append_mode"] = rec["other_append_mode"]
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample ...")
         res["cpu_baseline"] = cpu_baseline(step)
@@ -533,7 +558,7 @@ def main():
             del st
             torch.cuda.empty_cache()
             res["configs"][name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "roofline", "attention",
-                                                      "append")}
+                                                      "append", "other_append_mode") if k in r}
     if not args.no_probe_hbm:
         res["probe_hbm"] = probe_hbm()
     if args.probe_copy_mib:

@@ -63,7 +63,7 @@ class KvqAttnArgs(ctypes.Structure):
                 ("head_dim", I32), ("n_q", I32), ("segs", ctypes.POINTER(KvqSegment)), ("n_segs", I32),
                 ("k_cur", P), ("v_cur", P), ("n_cur", I32), ("softmax_scale", ctypes.c_float),
                 ("jensen", I32), ("out", P), ("out_dtype", I32), ("lse", P), ("workspace", P),
-                ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_bytes", ctypes.c_size_t), ("append_dst", ctypes.POINTER(KvqSegment))]
 
 
 SYMBOLS = ("kvq_quantize_append", "kvq_window_budget", "kvq_assign_windows", "kvq_attention_workspace_size",
@@ -261,7 +261,7 @@ def assign_windows(k: torch.Tensor, text_query: torch.Tensor, pct_fp16: int, pct
 
 
 def _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out, out_dtype, lse,
-               workspace):
+               workspace, append_to=None):
     B, Hq, nq, d = q.shape
     segs = list(segments)
     if n_kv_heads is None:
@@ -276,7 +276,8 @@ def _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     a = KvqAttnArgs(_ptr(q), _TORCH_DT[q.dtype], B, Hq, n_kv_heads, d, nq, arr, len(segs), _ptr(k_cur),
                     _ptr(v_cur), n_cur, float(softmax_scale), int(jensen), _ptr(out), out_dtype, _ptr(lse),
-                    _ptr(workspace), ws_bytes)
+                    _ptr(workspace), ws_bytes,
+                    None if append_to is None else ctypes.pointer(append_to.desc))
     return a, arr
 
 
@@ -294,7 +295,10 @@ def chunk_attention(q: torch.Tensor, segments: Sequence[Segment], k_cur: Optiona
                     v_cur: Optional[torch.Tensor] = None, n_kv_heads: Optional[int] = None,
                     softmax_scale: float = 0.0, jensen: int = JENSEN_TAYLOR2, out: Optional[torch.Tensor] = None,
                     out_dtype: torch.dtype = torch.float32, lse: Optional[torch.Tensor] = None,
-                    workspace: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+                    workspace: Optional[torch.Tensor] = None, append_to: Optional[Segment] = None,
+                    stream=None) -> torch.Tensor:
+    """``append_to``: also quantize k_cur / v_cur into this segment in the same call (the
+    attention reads the segments as they were before it)."""
     _dev(q, "q")
     if k_cur is not None:
         _dev(k_cur, "k_cur"); _dev(v_cur, "v_cur")
@@ -308,7 +312,7 @@ def chunk_attention(q: torch.Tensor, segments: Sequence[Segment], k_cur: Optiona
         if need:
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a, arr = _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out,
-                        _TORCH_DT[out.dtype], lse, workspace)
+                        _TORCH_DT[out.dtype], lse, workspace, append_to)
     _check(lib().kvq_chunk_attention(ctypes.byref(a), _stream(stream)), "kvq_chunk_attention")
     return out
 

@@ -268,6 +268,18 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
         return KVQ_ERR_ARG;
     for (int i = 0; i < a->n_segs; ++i)
         if (a->segs[i].n_tokens > 0 && (st = check_segment_ptrs(a->segs[i])) != KVQ_OK) return st;
+    // the optional quantize-append of the current chunk: checked as kvq_quantize_append would
+    kvq_segment *dst = a->n_cur > 0 ? a->append_dst : nullptr;
+    int app_groups = 0;
+    if (dst) {
+        if ((st = check_segment_shape(*dst)) != KVQ_OK) return st;
+        if ((st = check_segment_ptrs(*dst)) != KVQ_OK) return st;
+        if (dst->batch != a->batch || dst->n_kv_heads != a->n_kv_heads || dst->head_dim != a->head_dim)
+            return KVQ_ERR_ARG;
+        app_groups = (a->n_cur + dst->k_group_tokens - 1) / dst->k_group_tokens;
+        if ((long long)dst->n_tokens + a->n_cur > dst->capacity) return KVQ_ERR_CAPACITY;
+        if (dst->bits != 16 && (long long)dst->n_kgroups + app_groups > dst->kgroup_capacity) return KVQ_ERR_CAPACITY;
+    }
     const bool decode = use_decode(a, n_total);
     kvq::AttnPlan plan;
     kvq::attention_plan(a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, (int)n_total, decode, &plan);
@@ -332,7 +344,47 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
     p.work = plan.work;
     p.partial = reinterpret_cast<float *>(workspace);
     p.decode = decode ? 1 : 0;
-    return kvq::launch_attention(p, (hipStream_t)stream) == hipSuccess ? KVQ_OK : KVQ_ERR_HIP;
+    p.app_bits = p.app_groups = p.n_attn_wg = p.app_per_wg = 0;
+    bool append_after = false;
+    if (dst) {
+        kvq::QuantAppendParams &q = p.app;
+        q.k_src = a->k_cur;
+        q.v_src = a->v_cur;
+        q.src_dtype = a->dtype;
+        q.src_tokens = a->n_cur;
+        q.n_new = a->n_cur;
+        q.src_groups = nullptr;
+        q.k_group_tokens = dst->k_group_tokens;
+        q.batch = dst->batch;
+        q.n_kv_heads = dst->n_kv_heads;
+        q.head_dim = dst->head_dim;
+        q.capacity = dst->capacity;
+        q.kgroup_capacity = dst->kgroup_capacity;
+        q.n_tokens = dst->n_tokens;
+        q.n_kgroups = dst->n_kgroups;
+        q.elem_dtype = dst->elem_dtype;
+        q.k_dst = dst->k;
+        q.v_dst = dst->v;
+        q.k_meta = dst->k_meta;
+        q.v_meta = dst->v_meta;
+        q.kgroup_start = dst->kgroup_start;
+        // packed segments go into the chunk kernel's launch; the decode kernel and raw
+        // segments take the quantize-append kernel after the attention
+        if (!decode && dst->bits != 16) {
+            p.app_bits = dst->bits;
+            p.app_groups = app_groups;
+        } else {
+            append_after = true;
+        }
+    }
+    if (kvq::launch_attention(p, (hipStream_t)stream) != hipSuccess) return KVQ_ERR_HIP;
+    if (append_after && kvq::launch_quant_append(p.app, dst->bits, app_groups, (hipStream_t)stream) != hipSuccess)
+        return KVQ_ERR_HIP;
+    if (dst) {
+        dst->n_tokens += a->n_cur;
+        if (dst->bits != 16) dst->n_kgroups += app_groups;
+    }
+    return KVQ_OK;
 }
 
 }  // namespace

@@ -41,6 +41,7 @@
 // table in LDS as 16-byte row segments: the final output for a whole row block, otherwise
 // unnormalized partials in the workspace, which a combine kernel merges by log-sum-exp.
 #include "kvq_internal.h"
+#include "kvq_quant.cuh"
 #include "kvq_tile.cuh"
 
 namespace kvq {
@@ -142,7 +143,7 @@ __device__ __forceinline__ int find_group(const int32_t *tab, int ng, int a) {
 
 // Per piece [tb, te): the range and unit count of each segment, one wave per segment.
 // Ends with a barrier.
-__device__ void list_setup(const AttnParams &p, int tb, int te, TileList &L) {
+__device__ __forceinline__ void list_setup(const AttnParams &p, int tb, int te, TileList &L) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     for (int si = wave; si <= p.n_segs; si += kWaves) {
         SegInfo f{nullptr, 16, 0, 0, 0, 0, 0, 0};
@@ -178,7 +179,7 @@ __device__ void list_setup(const AttnParams &p, int tb, int te, TileList &L) {
 // Builds the list of the tiles of units u0, u0 + 1, ... (as many as fit) and returns how
 // many units it took; L.n_tiles is its length. All threads call it together; it begins
 // by overwriting the list (no wave may still read it) and ends with a barrier.
-__device__ int list_build(const AttnParams &p, TileList &L, int u0, int u_total) {
+__device__ __forceinline__ int list_build(const AttnParams &p, TileList &L, int u0, int u_total) {
     const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int u = u0 + tid;
     int n = 0, s = 0, g = 0, t0 = 0, t1 = 0, jrow = 0, kind = TILE_END, bits = 16;
@@ -740,10 +741,34 @@ __device__ __forceinline__ void softmax_pv(Ctx<HD, BF16> &cx, const uint16_t *vl
     cx.l += ps;
 }
 
+// The workgroups past the attention's: the quantize-append of the current chunk, units
+// (K-group fastest, then KV head, then batch) [u0, u0 + app_per_wg), one after another.
+template <int HD, bool BF16>
+__device__ __forceinline__ void append_units(const QuantAppendParams app, int bits, int n_groups, int n_heads,
+                                             int batch, int first_wg, int per_wg) {
+    typedef typename std::conditional<BF16, __bf16, _Float16>::type T;
+    const int64_t U = (int64_t)n_groups * n_heads * batch;
+    const int64_t u0 = (int64_t)(blockIdx.x - first_wg) * per_wg;
+    const int64_t u1 = min(u0 + (int64_t)per_wg, U);
+    for (int64_t u = u0; u < u1; ++u) {
+        const int g = (int)(u % n_groups);
+        const int64_t r = u / n_groups;
+        const int h = (int)(r % n_heads), b = (int)(r / n_heads);
+        if (bits == 2) qz::quant_group<T, HD, 2, kThreads>(app, g, h, b, n_groups);
+        else qz::quant_group<T, HD, 4, kThreads>(app, g, h, b, n_groups);
+        __syncthreads();   // the next unit reuses the group statistics in LDS
+    }
+}
+
 // EXACT: the all-orders Jensen form (its direct per-channel evaluation in its own instance,
 // so the other forms keep their register allocation).
 template <int HD, bool BF16, bool EXACT>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
+    if (blockIdx.x >= (unsigned)p.n_attn_wg) {
+        // a copy of the append's fields: the kernel argument itself is never addressed
+        append_units<HD, BF16>(p.app, p.app_bits, p.app_groups, p.n_kv_heads, p.batch, p.n_attn_wg, p.app_per_wg);
+        return;
+    }
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
     typedef Geo<HD> G;
@@ -1059,12 +1084,25 @@ __global__ __launch_bounds__(HD) void combine_kernel(AttnParams p) {
 }
 
 template <int HD, bool BF16>
-hipError_t launch_t(const AttnParams &p, hipStream_t s) {
+hipError_t launch_t(const AttnParams &p0, hipStream_t s) {
+    AttnParams p = p0;
     const unsigned n_wg = (unsigned)((p.work + p.quota - 1) / p.quota);
+    p.n_attn_wg = (int32_t)n_wg;
+    unsigned n_app = 0;
+    if (p.app_bits != 0) {
+        // append workgroups go after the attention's: on the CUs its last round leaves idle
+        // when there are a few, otherwise one per CU after it
+        const int64_t U = (int64_t)p.app_groups * p.n_kv_heads * p.batch;
+        const int G = device_cus();
+        const int idle = (int)(n_wg % (unsigned)G) == 0 ? 0 : G - (int)(n_wg % (unsigned)G);
+        const int64_t want = idle >= 4 ? idle : G;
+        p.app_per_wg = (int32_t)((U + want - 1) / want);
+        n_app = (unsigned)((U + p.app_per_wg - 1) / p.app_per_wg);
+    }
     if (p.jensen == JENSEN_EXACT)
-        hipLaunchKernelGGL((attention_kernel<HD, BF16, true>), dim3(n_wg), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, true>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((attention_kernel<HD, BF16, false>), dim3(n_wg), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, false>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.quota % p.tok_pad == 0) return e;   // no row block was split
     hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / (HD / 8))), dim3(256), 0, s, p);
@@ -1082,7 +1120,7 @@ hipError_t launch_combine(const AttnParams &p, hipStream_t s) {
 
 // Compute units of the current device (one chunk-attention workgroup runs per CU); 256,
 // the full gfx950 part, when there is no device to ask.
-static int device_cus() {
+int device_cus() {
     static int cached[64] = {0};
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
@@ -1139,7 +1177,7 @@ void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int 
 }
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {
-    if (p.decode) return launch_decode(p, s);
+    if (p.decode) return launch_decode(p, s);   // (the caller launches its append after it)
     const bool bf = p.dtype == DT_BF16;
     if (p.head_dim == 64) return bf ? launch_t<64, true>(p, s) : launch_t<64, false>(p, s);
     return bf ? launch_t<128, true>(p, s) : launch_t<128, false>(p, s);

@@ -80,6 +80,12 @@ struct AttnParams {
     float *partial;                // decode: [n_split][rows][head_dim + 2];
                                    // chunk: [workgroup][2][row in block][head_dim + 4]
     int32_t decode;                // run the decode-shaped kernel (decided by decode_eligible)
+    // quantize-append of the current chunk in the same call (app_bits 0: none). The chunk
+    // kernel runs it in workgroups after its own (blocks past n_attn_wg, app_per_wg units
+    // of (K-group, KV head, batch) each, on the CUs the attention leaves idle in its last
+    // round); other paths launch the quantize-append kernel after the attention.
+    QuantAppendParams app;
+    int32_t app_bits, app_groups, n_attn_wg, app_per_wg;
 };
 struct AttnPlan {
     int32_t n_split, split_tokens;   // decode kernel
@@ -87,6 +93,8 @@ struct AttnPlan {
     int64_t quota, work;
     size_t workspace_bytes;
 };
+// Compute units of the current device (256 when there is none to ask).
+int device_cus();
 // How either kernel divides the work (decode selects the decode-shaped one), and the
 // workspace its partials need.
 void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q, int n_total, bool decode,

@@ -238,6 +238,18 @@ kvq_status kvq_assign_windows(const kvq_window_args *args, void *stream);
  *   lse      device float32 [batch][n_q_heads][n_q], optional: log sum_j exp(s_j).
  *   workspace  device scratch of at least kvq_attention_workspace_size bytes (may be
  *            NULL when that size is 0). Contents on entry do not matter.
+ *   append_dst  optional host descriptor (NULL: none): the current chunk is also
+ *            quantized and appended to this segment in the same call, as
+ *            kvq_quantize_append with k_src = k_cur, v_src = v_cur, src_tokens = n_new =
+ *            n_cur would do it [JB: the finished chunk joins the cache of earlier chunks],
+ *            and the descriptor is advanced on KVQ_OK. The attention reads every segment
+ *            as it was before the call, so append_dst may be one of segs (the new tokens
+ *            land past its n_tokens). For packed segments on the chunk-shaped path the
+ *            append runs in extra workgroups of the attention's own launch, placed after
+ *            the attention's so that they fill the CUs its last round leaves idle; the
+ *            decode-shaped path and raw segments launch the quantize-append kernel right
+ *            after the attention. Capacity and shape errors are those of
+ *            kvq_quantize_append, reported before anything is enqueued.
  * Errors: KVQ_ERR_ARG (nulls, shape mismatch, no tokens at all, n_q_heads not a
  * multiple of n_kv_heads), KVQ_ERR_UNSUPPORTED (dtypes, head_dim, bits, too many
  * segments, jensen not a kvq_jensen value), KVQ_ERR_WORKSPACE.
@@ -257,6 +269,7 @@ typedef struct kvq_attn_args {
     float *lse;
     void *workspace;
     size_t workspace_bytes;
+    kvq_segment *append_dst;   /* host, optional (see above) */
 } kvq_attn_args;
 
 /*

@@ -235,3 +235,22 @@ def test_probe_validation():
     assert L.kvq_probe_hbm_read(FAKE, 1000, sink, None) == kvq.ERR_ARG       # not a multiple of 16
     assert L.kvq_probe_hbm_read(FAKE + 8, 1 << 20, sink, None) == kvq.ERR_ARG  # misaligned
     assert L.kvq_probe_hbm_read(FAKE, 1 << 20, None, None) == kvq.ERR_ARG
+
+
+def test_fused_append_validation():
+    """append_dst is checked like kvq_quantize_append before anything is enqueued; on error
+    neither descriptor changes."""
+    dst = _seg(capacity=1000, n_tokens=995, n_kgroups=8)            # 995 + 10 current > 1000
+    a, arr = _attn(append_dst=ctypes.pointer(dst))
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_CAPACITY
+    assert (dst.n_tokens, dst.n_kgroups) == (995, 8)
+    dst = _seg(n_tokens=100, n_kgroups=16, kgroup_capacity=16)       # no room for a new K-group
+    a, arr = _attn(append_dst=ctypes.pointer(dst))
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_CAPACITY
+    dst = _seg(n_kv_heads=4)                                         # not the attention's heads
+    a, arr = _attn(append_dst=ctypes.pointer(dst))
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_ARG
+    dst = _seg(k_meta=None)
+    a, arr = _attn(append_dst=ctypes.pointer(dst))
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_ARG
+    assert (dst.n_tokens, dst.n_kgroups) == (0, 0)

@@ -258,3 +258,41 @@ def test_windowquant_segments_many_queries(dtype, d, jensen):
     oo, ol = oracle_attention(q, osegs, kc, vc, n_kv_heads=H, jensen=jensen)
     assert np.abs(go - oo).max() <= TOL
     assert np.abs(gl - ol).max() <= TOL
+
+
+@pytest.mark.parametrize("case", ["whole_row_blocks", "shares", "decode_path", "raw_segment", "int4_d64"])
+def test_attention_with_fused_append(case):
+    """kvq_chunk_attention with append_dst: the attention reads the cache as it was before
+    the call (against the oracle), and the current chunk lands in the segment bit-exactly
+    as a separate kvq_quantize_append would put it (against the oracle's append)."""
+    cfg = {
+        # 250 row blocks of 256 queries on a 256-CU part: one round of whole row blocks, six
+        # CUs left idle for the append workgroups
+        "whole_row_blocks": dict(bits=2, dtype="bf16", B=1, Hq=10, Hkv=10, d=128, n_q=6400, n_cache=700, n_cur=300),
+        # 24 row blocks: equal shares on every CU, the append after them
+        "shares": dict(bits=2, dtype="bf16", B=1, Hq=2, Hkv=2, d=128, n_q=3000, n_cache=900, n_cur=500),
+        # few rows per KV head: the decode kernel, then the quantize-append kernel
+        "decode_path": dict(bits=2, dtype="bf16", B=2, Hq=8, Hkv=2, d=128, n_q=1, n_cache=400, n_cur=40),
+        "raw_segment": dict(bits=16, dtype="f16", B=1, Hq=4, Hkv=2, d=64, n_q=300, n_cache=200, n_cur=77),
+        "int4_d64": dict(bits=4, dtype="f16", B=1, Hq=4, Hkv=4, d=64, n_q=600, n_cache=500, n_cur=130),
+    }[case]
+    bits, dtype, B, Hq, Hkv, d = (cfg[k] for k in ("bits", "dtype", "B", "Hq", "Hkv", "d"))
+    n_q, n_cache, n_cur = cfg["n_q"], cfg["n_cache"], cfg["n_cur"]
+    Gk = 128 if d == 128 else 32
+    cap = n_cache + n_cur
+    kgc = -(-n_cache // Gk) + -(-n_cur // Gk)
+    gseg, oseg = make_pair(bits, dtype, B, Hkv, d, capacity=cap, Gk=Gk, kgroup_capacity=kgc)
+    append_both(gseg, oseg, _rand((B, Hkv, n_cache, d), dtype, 61, 2.0), _rand((B, Hkv, n_cache, d), dtype, 62))
+    q = _rand((B, Hq, n_q, d), dtype, 63)
+    kc = _rand((B, Hkv, n_cur, d), dtype, 64, 2.0)
+    vc = _rand((B, Hkv, n_cur, d), dtype, 65)
+    oo, ol = oracle_attention(q, [oseg], kc, vc, n_kv_heads=Hkv, jensen=1)   # before the append
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    out = kvq.chunk_attention(q.cuda(), [gseg], kc.cuda(), vc.cuda(), n_kv_heads=Hkv, jensen=1, lse=lse,
+                              append_to=gseg)
+    torch.cuda.synchronize()
+    assert gseg.n_tokens == cap
+    assert np.abs(out.cpu().numpy() - oo).max() <= TOL
+    assert np.abs(lse.cpu().numpy() - ol).max() <= TOL
+    oracle.append(oseg, f32(kc), f32(vc))
+    assert_segments_equal(gseg, oseg)
