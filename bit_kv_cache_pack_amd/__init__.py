@@ -43,7 +43,8 @@ class KvqSegment(ctypes.Structure):
     _fields_ = [("bits", I32), ("elem_dtype", I32), ("batch", I32), ("n_kv_heads", I32),
                 ("head_dim", I32), ("capacity", I32), ("n_tokens", I32), ("k_group_tokens", I32),
                 ("v_group_channels", I32), ("kgroup_capacity", I32), ("n_kgroups", I32),
-                ("k", P), ("v", P), ("k_meta", P), ("v_meta", P), ("kgroup_start", P)]
+                ("k", P), ("v", P), ("k_meta", P), ("v_meta", P), ("kgroup_start", P),
+                ("k_group_channels", I32), ("comp_rank", I32), ("comp_basis", P), ("k_comp", P)]
 
 
 class KvqAppendArgs(ctypes.Structure):
@@ -141,7 +142,10 @@ class Segment:
 
     def __init__(self, bits: int, elem_dtype: torch.dtype, batch: int, n_kv_heads: int, head_dim: int,
                  capacity: int, k_group_tokens: int = 128, kgroup_capacity: Optional[int] = None,
-                 v_group_channels: int = 32, device=None):
+                 v_group_channels: int = 32, device=None, k_group_channels: int = 0,
+                 comp_basis: Optional[torch.Tensor] = None):
+        """k_group_channels > 0: per-token K groups of that many channels. comp_basis: device
+        float32 [n_kv_heads][head_dim][r] (r <= 8), the low-rank compensation's basis."""
         device = device or torch.device("cuda")
         self.bits = bits
         if kgroup_capacity is None:
@@ -155,13 +159,21 @@ class Segment:
             wpr = d * bits // 32
             self.k = torch.zeros((B, H, capacity, wpr), dtype=torch.int32, device=device)
             self.v = torch.zeros((B, H, capacity, wpr), dtype=torch.int32, device=device)
-            self.k_meta = torch.zeros((B, H, kgroup_capacity, d, 2), dtype=torch.int16, device=device)
+            if k_group_channels:
+                self.k_meta = torch.zeros((B, H, capacity, d // k_group_channels, 2), dtype=torch.int16,
+                                          device=device)
+            else:
+                self.k_meta = torch.zeros((B, H, kgroup_capacity, d, 2), dtype=torch.int16, device=device)
             self.v_meta = torch.zeros((B, H, capacity, d // v_group_channels, 2), dtype=torch.int16,
                                       device=device)
             self.kgroup_start = torch.zeros(kgroup_capacity + 1, dtype=torch.int32, device=device)
+        self.comp_basis = comp_basis
+        r = 0 if comp_basis is None else comp_basis.shape[2]
+        self.k_comp = torch.zeros((B, H, capacity, 8), dtype=torch.int16, device=device) if r else None
         self.desc = KvqSegment(bits, _TORCH_DT[elem_dtype], B, H, d, capacity, 0, k_group_tokens,
                                v_group_channels, kgroup_capacity, 0, _ptr(self.k), _ptr(self.v),
-                               _ptr(self.k_meta), _ptr(self.v_meta), _ptr(self.kgroup_start))
+                               _ptr(self.k_meta), _ptr(self.v_meta), _ptr(self.kgroup_start),
+                               k_group_channels, r, _ptr(comp_basis), _ptr(self.k_comp))
 
     @property
     def n_tokens(self) -> int:
@@ -177,7 +189,7 @@ class Segment:
         self.desc.n_kgroups = n_kgroups
 
     def nbytes(self) -> int:
-        return sum(t.numel() * t.element_size() for t in (self.k, self.v, self.k_meta, self.v_meta)
+        return sum(t.numel() * t.element_size() for t in (self.k, self.v, self.k_meta, self.v_meta, self.k_comp)
                    if t is not None)
 
 

@@ -28,6 +28,14 @@ kvq_status check_segment_shape(const kvq_segment &s) {
     if (s.bits != 16) {
         if (s.v_group_channels != 32) return KVQ_ERR_UNSUPPORTED;
         if (s.kgroup_capacity < 0 || s.n_kgroups < 0 || s.n_kgroups > s.kgroup_capacity) return KVQ_ERR_ARG;
+        if (s.k_group_channels != 0 && s.k_group_channels != 32 && s.k_group_channels != 64 &&
+            s.k_group_channels != 128)
+            return KVQ_ERR_UNSUPPORTED;
+        if (s.k_group_channels > s.head_dim) return KVQ_ERR_UNSUPPORTED;
+        if (s.comp_rank < 0 || s.comp_rank > 8) return KVQ_ERR_UNSUPPORTED;
+        if (s.comp_rank > 0 && s.k_group_channels != 0) return KVQ_ERR_UNSUPPORTED;
+    } else if (s.k_group_channels != 0 || s.comp_rank != 0) {
+        return KVQ_ERR_UNSUPPORTED;
     }
     return KVQ_OK;
 }
@@ -35,8 +43,10 @@ kvq_status check_segment_shape(const kvq_segment &s) {
 kvq_status check_segment_ptrs(const kvq_segment &s) {
     if (!s.k || !s.v || !aligned16(s.k) || !aligned16(s.v)) return KVQ_ERR_ARG;
     if (s.bits != 16) {
-        if (!s.k_meta || !s.v_meta || !s.kgroup_start) return KVQ_ERR_ARG;
+        if (!s.k_meta || !s.v_meta || (s.k_group_channels == 0 && !s.kgroup_start)) return KVQ_ERR_ARG;
         if (!aligned16(s.k_meta) || !aligned16(s.v_meta)) return KVQ_ERR_ARG;
+        if (s.comp_rank > 0 && (!s.comp_basis || !s.k_comp || !aligned16(s.k_comp) || !aligned16(s.comp_basis)))
+            return KVQ_ERR_ARG;
     }
     return KVQ_OK;
 }
@@ -58,6 +68,7 @@ kvq_status check_attention_shape(const kvq_attn_args *a, long long *n_total) {
     if (!any_dtype(a->out_dtype)) return KVQ_ERR_UNSUPPORTED;
     if (!(a->softmax_scale >= 0.0f) || isinf(a->softmax_scale)) return KVQ_ERR_ARG;
     long long n = a->n_cur;
+    const kvq_segment *aug = nullptr;   // the first segment with per-token K groups or compensation
     for (int i = 0; i < a->n_segs; ++i) {
         const kvq_segment &s = a->segs[i];
         kvq_status st = check_segment_shape(s);
@@ -65,6 +76,15 @@ kvq_status check_attention_shape(const kvq_attn_args *a, long long *n_total) {
         if (s.elem_dtype != a->dtype) return KVQ_ERR_UNSUPPORTED;
         if (s.batch != a->batch || s.n_kv_heads != a->n_kv_heads || s.head_dim != a->head_dim)
             return KVQ_ERR_ARG;
+        if (s.bits != 16 && s.n_tokens > 0 && (s.k_group_channels > 0 || s.comp_rank > 0)) {
+            // per-token K groups take the all-orders Jensen form nowhere; segments with extra
+            // per-token K columns in one call all use the same kind (and basis)
+            if (a->jensen == KVQ_JENSEN_EXACT) return KVQ_ERR_UNSUPPORTED;
+            if (aug && (aug->k_group_channels != s.k_group_channels || aug->comp_rank != s.comp_rank ||
+                        aug->comp_basis != s.comp_basis))
+                return KVQ_ERR_UNSUPPORTED;
+            aug = &s;
+        }
         n += s.n_tokens;
     }
     if (n < 1 || n > (1ll << 30)) return KVQ_ERR_ARG;
@@ -78,8 +98,13 @@ kvq_status check_attention_shape(const kvq_attn_args *a, long long *n_total) {
 bool use_decode(const kvq_attn_args *a, long long n_total) {
     int bits[KVQ_MAX_SEGMENTS];
     int n = 0;
-    for (int i = 0; i < a->n_segs; ++i)
-        if (a->segs[i].n_tokens > 0) bits[n++] = a->segs[i].bits;
+    for (int i = 0; i < a->n_segs; ++i) {
+        const kvq_segment &s = a->segs[i];
+        if (s.n_tokens == 0) continue;
+        // per-token K groups and the compensation are chunk-kernel features
+        if (s.bits != 16 && (s.k_group_channels > 0 || s.comp_rank > 0)) return false;
+        bits[n++] = s.bits;
+    }
     return kvq::decode_eligible(a->dtype, a->batch, a->n_q_heads, a->n_kv_heads, a->head_dim, a->n_q, bits, n,
                                 a->n_cur, (int)n_total);
 }
@@ -155,7 +180,8 @@ kvq_status kvq_quantize_append(const kvq_append_args *a, void *stream) {
         n_groups = (a->n_new + s.k_group_tokens - 1) / s.k_group_tokens;
     }
     if ((long long)s.n_tokens + a->n_new > s.capacity) return KVQ_ERR_CAPACITY;
-    if (s.bits != 16 && (long long)s.n_kgroups + n_groups > s.kgroup_capacity) return KVQ_ERR_CAPACITY;
+    const bool table = s.bits != 16 && s.k_group_channels == 0;   // the segment keeps a K-group table
+    if (table && (long long)s.n_kgroups + n_groups > s.kgroup_capacity) return KVQ_ERR_CAPACITY;
 
     kvq::QuantAppendParams p;
     p.k_src = a->k_src;
@@ -178,9 +204,13 @@ kvq_status kvq_quantize_append(const kvq_append_args *a, void *stream) {
     p.k_meta = s.k_meta;
     p.v_meta = s.v_meta;
     p.kgroup_start = s.kgroup_start;
+    p.k_group_channels = s.bits != 16 ? s.k_group_channels : 0;
+    p.comp_rank = s.bits != 16 ? s.comp_rank : 0;
+    p.comp_basis = s.comp_basis;
+    p.k_comp = s.k_comp;
     if (kvq::launch_quant_append(p, s.bits, n_groups, (hipStream_t)stream) != hipSuccess) return KVQ_ERR_HIP;
     s.n_tokens += a->n_new;
-    if (s.bits != 16) s.n_kgroups += n_groups;
+    if (table) s.n_kgroups += n_groups;
     return KVQ_OK;
 }
 
@@ -278,7 +308,9 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
             return KVQ_ERR_ARG;
         app_groups = (a->n_cur + dst->k_group_tokens - 1) / dst->k_group_tokens;
         if ((long long)dst->n_tokens + a->n_cur > dst->capacity) return KVQ_ERR_CAPACITY;
-        if (dst->bits != 16 && (long long)dst->n_kgroups + app_groups > dst->kgroup_capacity) return KVQ_ERR_CAPACITY;
+        if (dst->bits != 16 && dst->k_group_channels == 0 &&
+            (long long)dst->n_kgroups + app_groups > dst->kgroup_capacity)
+            return KVQ_ERR_CAPACITY;
     }
     const bool decode = use_decode(a, n_total);
     kvq::AttnPlan plan;
@@ -309,12 +341,13 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
         kvq::SegmentView &v = p.segs[p.n_segs++];
         v.bits = s.bits;
         v.n_tokens = s.n_tokens;
-        v.n_kgroups = s.bits == 16 ? 0 : s.n_kgroups;
+        v.n_kgroups = s.bits == 16 || s.k_group_channels > 0 ? 0 : s.n_kgroups;
+        v.k_group_channels = s.bits == 16 ? 0 : s.k_group_channels;
+        v.k_comp = s.bits != 16 && s.comp_rank > 0 ? reinterpret_cast<const uint16_t *>(s.k_comp) : nullptr;
         v.capacity = s.capacity;
         v.kgroup_capacity = s.kgroup_capacity;
         v.v_group_channels = s.v_group_channels;
         v.token_begin = begin;
-        v.pad_ = 0;
         v.k = s.k;
         v.v = s.v;
         v.k_meta = reinterpret_cast<const uint32_t *>(s.k_meta);
@@ -333,6 +366,20 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
                   : a->jensen == KVQ_JENSEN_EXACT ? 1.0f : (float)(scale * scale / 24.0 * log2e);
     p.half_scale = (float)(scale / 2.0);
     p.jensen = a->jensen;
+    p.aug = p.aug_kgc = p.aug_rank = 0;
+    p.aug_basis = nullptr;
+    for (int i = 0; i < a->n_segs; ++i) {
+        const kvq_segment &s = a->segs[i];
+        if (s.n_tokens == 0 || s.bits == 16) continue;
+        if (s.k_group_channels > 0) {
+            p.aug = 1;
+            p.aug_kgc = s.k_group_channels;
+        } else if (s.comp_rank > 0) {
+            p.aug = 2;
+            p.aug_rank = s.comp_rank;
+            p.aug_basis = s.comp_basis;
+        }
+    }
     p.out = a->out;
     p.out_dtype = a->out_dtype;
     p.lse = a->lse;
@@ -368,9 +415,14 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
         q.k_meta = dst->k_meta;
         q.v_meta = dst->v_meta;
         q.kgroup_start = dst->kgroup_start;
-        // packed segments go into the chunk kernel's launch; the decode kernel and raw
-        // segments take the quantize-append kernel after the attention
-        if (!decode && dst->bits != 16) {
+        q.k_group_channels = dst->bits != 16 ? dst->k_group_channels : 0;
+        q.comp_rank = dst->bits != 16 ? dst->comp_rank : 0;
+        q.comp_basis = dst->comp_basis;
+        q.k_comp = dst->k_comp;
+        // packed segments of the plain layout go into the chunk kernel's launch; the decode
+        // kernel, raw segments, per-token K groups and the compensation take the
+        // quantize-append kernel after the attention
+        if (!decode && dst->bits != 16 && dst->k_group_channels == 0 && dst->comp_rank == 0) {
             p.app_bits = dst->bits;
             p.app_groups = app_groups;
         } else {
@@ -382,7 +434,7 @@ kvq_status run_attention(const kvq_attn_args *a, void *stream, bool use_static) 
         return KVQ_ERR_HIP;
     if (dst) {
         dst->n_tokens += a->n_cur;
-        if (dst->bits != 16) dst->n_kgroups += app_groups;
+        if (dst->bits != 16 && dst->k_group_channels == 0) dst->n_kgroups += app_groups;
     }
     return KVQ_OK;
 }

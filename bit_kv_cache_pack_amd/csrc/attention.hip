@@ -69,7 +69,9 @@ template <int HD> struct Geo {
 };
 
 // ---------------------------------------------------------------- tile list
-enum : int { TILE_END = 0, TILE_PACKED = 1, TILE_RAW = 2, TILE_CUR = 3 };
+enum : int { TILE_END = 0, TILE_PACKED = 1, TILE_RAW = 2, TILE_CUR = 3, TILE_PTOK = 4 };
+// TILE_PTOK: a packed segment with per-token K groups (no K-group table: taken in TT-token
+// tiles like raw segments, its keys' step/zero read per token)
 
 // A tile descriptor in four words: kind, segment, flags, Jensen row and bit-width in one.
 struct Tile {
@@ -85,6 +87,8 @@ struct Tile {
     __device__ __forceinline__ int jrow() const { return (info >> 10) & 31; }
     // the segment's bit-width (16: raw elements)
     __device__ __forceinline__ int bits() const { return info >> 16; }
+    // the segment stores the low-rank compensation of its keys
+    __device__ __forceinline__ bool comp() const { return (info >> 15) & 1; }
     static __device__ __forceinline__ Tile make(int kind, int seg, int g, int t, int len, int new_group, int jrow,
                                                 int bits) {
         return Tile{kind | seg << 4 | new_group << 8 | (new_group && jrow == 0) << 9 | jrow << 10 | bits << 16, g,
@@ -114,6 +118,7 @@ struct SegInfo {
     int a, e;             // tokens of the piece inside the segment, [a, e)
     int g_lo;             // K-group of token a (packed segments)
     int units;            // units of the segment in the piece
+    int ptok, comp;       // per-token K groups; stores the compensation
 };
 
 struct TileList {
@@ -146,7 +151,7 @@ __device__ __forceinline__ int find_group(const int32_t *tab, int ng, int a) {
 __device__ __forceinline__ void list_setup(const AttnParams &p, int tb, int te, TileList &L) {
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave), lane = threadIdx.x % kWave;
     for (int si = wave; si <= p.n_segs; si += kWaves) {
-        SegInfo f{nullptr, 16, 0, 0, 0, 0, 0, 0};
+        SegInfo f{nullptr, 16, 0, 0, 0, 0, 0, 0, 0, 0};
         if (si == p.n_segs) {
             const int cb = p.n_total - p.n_cur;
             f.n = p.n_cur;
@@ -161,8 +166,10 @@ __device__ __forceinline__ void list_setup(const AttnParams &p, int tb, int te, 
             f.ng = sg.bits == 16 ? 0 : sg.n_kgroups;
             f.a = max(tb, sg.token_begin) - sg.token_begin;
             f.e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
+            f.ptok = sg.bits != 16 && sg.k_group_channels > 0;
+            f.comp = sg.k_comp != nullptr;
             if (f.e > f.a) {
-                if (f.bits == 16) {
+                if (f.bits == 16 || f.ptok) {
                     f.units = (f.e - f.a + TT - 1) / TT;
                 } else if (f.ng > 0) {
                     f.g_lo = f.a == 0 ? 0 : find_group(f.tab, f.ng, f.a);
@@ -194,8 +201,9 @@ __device__ __forceinline__ int list_build(const AttnParams &p, TileList &L, int 
             base += nu;
         }
         const SegInfo &f = L.seg[s];
-        if (s == p.n_segs || f.bits == 16) {
-            kind = s == p.n_segs ? TILE_CUR : TILE_RAW;
+        if (s == p.n_segs || f.bits == 16 || f.ptok) {
+            kind = s == p.n_segs ? TILE_CUR : (f.bits == 16 ? TILE_RAW : TILE_PTOK);
+            if (kind == TILE_PTOK) bits = f.bits;
             t0 = f.a + TT * i;
             t1 = min(t0 + TT, f.e);
             n = 1;
@@ -227,9 +235,13 @@ __device__ __forceinline__ int list_build(const AttnParams &p, TileList &L, int 
     for (int w = 0; w < wave; ++w) off += L.wsum[w];
     // the units that fit are a prefix of the batch
     const bool inc = u < u_total && off + n <= kListCap;
-    for (int k = 0; inc && k < n; ++k)
-        L.t[off + k] = Tile::make(kind, s, g, t0 + TT * k, min(TT, t1 - t0 - TT * k), kind == TILE_PACKED && k == 0,
-                                  jrow, bits);
+    const int comp_flag = kind == TILE_PACKED && s < p.n_segs && L.seg[s].comp ? 1 << 15 : 0;
+    for (int k = 0; inc && k < n; ++k) {
+        Tile t = Tile::make(kind, s, g, t0 + TT * k, min(TT, t1 - t0 - TT * k), kind == TILE_PACKED && k == 0,
+                            jrow, bits);
+        t.info |= comp_flag;
+        L.t[off + k] = t;
+    }
     const int taken = __syncthreads_count(inc);
     if (taken == 0) {
         if (tid == 0) L.n_tiles = 0;
@@ -245,9 +257,12 @@ __device__ __forceinline__ int list_build(const AttnParams &p, TileList &L, int 
 // Raw tiles: w[0..1] = 16 key elements, w[2..3] = 16 value elements. Packed tiles:
 // w[0..3] = {step, zero} of the block's 16 key channels, w[4] = a key word pair (x, y) and
 // a value word pair (z, w), w[5].x = the token's value {step, zero} for the block.
-struct Prefetch {
-    u32x4 w[6];
+// With the per-token K columns (AUG), w[6] is the token's source of them: its K step/zero
+// row (per-token K groups) or its stored compensation (8 bf16).
+template <bool AUG> struct PrefetchT {
+    u32x4 w[AUG ? 7 : 6];
 };
+typedef PrefetchT<false> Prefetch;
 
 // Loads are unconditional, from rows clamped into the tile (staging zeroes rows past it):
 // a load under a per-lane condition would have to land before its registers are merged
@@ -260,8 +275,8 @@ __device__ __forceinline__ int fresh_tid() {
     return t;
 }
 
-template <int HD>
-__device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p, const Tile &tl, size_t bh) {
+template <int HD, bool AUG>
+__device__ __forceinline__ void prefetch_tile(PrefetchT<AUG> &pf, const AttnParams &p, const Tile &tl, size_t bh) {
     typedef Geo<HD> G;
     const int tid = fresh_tid();
     const int r = min(tid / G::NBLK, tl.len - 1), b = tid % G::NBLK;
@@ -270,11 +285,11 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
     // on it. w[0..3]: four 16-byte loads (raw keys and values, or the K-group's
     // {step, zero} when it changes). w[4], w[5].x: the packed word pairs and value meta
     // (raw tiles read a harmless copy of their own row).
-    const u32x4 *ka, *va;
+    const u32x4 *ka = nullptr, *va = nullptr;
     const u32x2 *kp, *vp;
     const uint32_t *vmp;
     bool load4;
-    if (tl.kind() == TILE_PACKED) {
+    if (tl.kind() == TILE_PACKED || (AUG && tl.kind() == TILE_PTOK)) {
         const SegmentView &sg = p.segs[tl.seg()];
         const int bits = tl.bits();
         const int wpr = HD * bits / 32;   // words per token row
@@ -287,11 +302,36 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
         kp = reinterpret_cast<const u32x2 *>(kc + widx);
         vp = reinterpret_cast<const u32x2 *>(vc + widx);
         vmp = sg.v_meta + row0 * (HD / 32) + (uint32_t)(r * (HD / 32) + b / 2);
-        // the {step, zero} of the thread's 16 channels change only with the K-group (a thread
-        // keeps its channel block from tile to tile; raw tiles are followed by a new group)
-        ka = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
-        va = ka + 2;
-        load4 = tl.new_group();
+        if constexpr (AUG) {
+            if (tl.kind() == TILE_PTOK) {
+                // per-token K groups: the {step, zero} of the thread's block (one group: the
+                // group width is at least 32 channels), and the token's whole row of them for
+                // the Jensen columns
+                const int ng = HD / sg.k_group_channels;
+                const uint32_t *krow = sg.k_meta + (row0 + r) * ng;
+                pf.w[0].x = krow[(16 * b) / sg.k_group_channels];
+                if (ng == 4) {
+                    pf.w[6] = *reinterpret_cast<const u32x4 *>(krow);
+                } else if (ng == 2) {
+                    const u32x2 m = *reinterpret_cast<const u32x2 *>(krow);
+                    pf.w[6] = u32x4{m.x, m.y, 0u, 0u};
+                } else {
+                    pf.w[6] = u32x4{krow[0], 0u, 0u, 0u};
+                }
+                load4 = false;
+            } else {
+                if (tl.comp()) pf.w[6] = *reinterpret_cast<const u32x4 *>(sg.k_comp + (row0 + r) * 8);
+                ka = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
+                va = ka + 2;
+                load4 = tl.new_group();
+            }
+        } else {
+            // the {step, zero} of the thread's 16 channels change only with the K-group (a thread
+            // keeps its channel block from tile to tile; raw tiles are followed by a new group)
+            ka = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + tl.g) * HD) + 4 * b;
+            va = ka + 2;
+            load4 = tl.new_group();
+        }
     } else {
         const uint16_t *kb, *vb;
         if (tl.kind() == TILE_RAW) {
@@ -323,10 +363,11 @@ __device__ __forceinline__ void prefetch_tile(Prefetch &pf, const AttnParams &p,
 }
 
 // ---------------------------------------------------------------- staging (registers -> LDS)
-enum : int { STAGE_NONE = 0, STAGE_INT2 = 1, STAGE_INT4 = 2, STAGE_RAW = 3 };
+enum : int { STAGE_NONE = 0, STAGE_INT2 = 1, STAGE_INT4 = 2, STAGE_RAW = 3, STAGE_INT2T = 4, STAGE_INT4T = 5 };
 
 __device__ __forceinline__ int stage_kind(const Tile &tl) {
     if (tl.kind() == TILE_END) return STAGE_NONE;
+    if (tl.kind() == TILE_PTOK) return tl.bits() == 2 ? STAGE_INT2T : STAGE_INT4T;
     if (tl.kind() != TILE_PACKED) return STAGE_RAW;
     return tl.bits() == 2 ? STAGE_INT2 : STAGE_INT4;
 }
@@ -334,8 +375,8 @@ __device__ __forceinline__ int stage_kind(const Tile &tl) {
 // The thread's unit of a prefetched tile, dequantized: 16 keys (element dtype) and 16
 // values (fp16), position order. Rows past the tile's end hold a copy of its last row
 // (the loads are clamped); their scores are masked, so they add nothing.
-template <int SK, bool BF16>
-__device__ __forceinline__ void dequant_unit(const Prefetch &pf, int b, uint32_t (&ko)[8], uint32_t (&vo)[8]) {
+template <int SK, bool BF16, bool AUG>
+__device__ __forceinline__ void dequant_unit(const PrefetchT<AUG> &pf, int b, uint32_t (&ko)[8], uint32_t (&vo)[8]) {
     typedef Elem<BF16> E;
     if constexpr (SK == STAGE_RAW) {
         const uint32_t kd8[8] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w, pf.w[1].x, pf.w[1].y, pf.w[1].z, pf.w[1].w};
@@ -346,13 +387,18 @@ __device__ __forceinline__ void dequant_unit(const Prefetch &pf, int b, uint32_t
         to_positions(vd8, vo);
     } else {
         uint32_t km[16];  // {step, zero} of the block's channels, channel order
+        if constexpr (SK == STAGE_INT2T || SK == STAGE_INT4T) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            km[4 * i] = pf.w[i].x; km[4 * i + 1] = pf.w[i].y; km[4 * i + 2] = pf.w[i].z; km[4 * i + 3] = pf.w[i].w;
+            for (int i = 0; i < 16; ++i) km[i] = pf.w[0].x;   // per-token K group: one for the block
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                km[4 * i] = pf.w[i].x; km[4 * i + 1] = pf.w[i].y; km[4 * i + 2] = pf.w[i].z; km[4 * i + 3] = pf.w[i].w;
+            }
         }
         const u32x4 c = pf.w[4];   // key word pair, value word pair
         const uint32_t vmeta = pf.w[5].x;
-        if constexpr (SK == STAGE_INT2) {
+        if constexpr (SK == STAGE_INT2 || SK == STAGE_INT2T) {
             const bool odd = b & 1;
             k2_block<BF16>(odd ? c.y : c.x, km, ko);
             uint32_t tlo, thi;
@@ -380,18 +426,64 @@ __device__ __forceinline__ void write_unit(uint16_t *buf, const uint32_t (&ko)[8
     }
 }
 
-template <int HD, bool BF16, int SK>
-__device__ __forceinline__ void stage_only(uint16_t *buf, const Prefetch &pf) {
-    uint32_t ko[8], vo[8];
-    dequant_unit<SK, BF16>(pf, threadIdx.x % Geo<HD>::NBLK, ko, vo);
-    write_unit<HD>(buf, ko, vo);
+// Per-token K columns (AUG): 16 bf16 per token, row stride AROW halves. Per-token K groups
+// put the squares of the token's group steps there, split into high and low bf16 parts:
+// [hi_0..3 | lo_0..3 | hi_0..3 | 0], against the query's [k q2hi_0..3 | k q2hi_0..3 |
+// k q2lo_0..3 | 0] (k = -tau / 24), so that one more MFMA k-step adds -beta_t / tau to each
+// score; the compensation puts the token's stored c there twice, [c_0..7 | c_0..7], against
+// [(U^T q)hi_0..7 | (U^T q)lo_0..7]. Other tiles write zeros. Mode 0 zeros, 1 per-token K
+// groups, 2 compensation.
+constexpr int AROW = 24;
+enum : int { AUG_ZERO = 0, AUG_TOKEN = 1, AUG_COMP = 2 };
+
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) { return pack_bf16x2(lo, hi); }
+
+template <int HD, bool AUG>
+__device__ __forceinline__ void write_aug(uint16_t *abuf, const PrefetchT<AUG> &pf, int mode) {
+    if constexpr (AUG) {
+        typedef Geo<HD> G;
+        const int tid = threadIdx.x;
+        if (tid % G::NBLK != 0 || tid / G::NBLK >= TT) return;
+        u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
+        if (mode == AUG_TOKEN) {
+            float d[4], dh[4], dl[4];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const float st = f16_bits_to_f32(pf.w[6][g] & 0xffffu);
+                d[g] = st * st;
+                dh[g] = (float)(__bf16)d[g];
+                dl[g] = d[g] - dh[g];
+            }
+            lo = u32x4{bf16_pair(dh[0], dh[1]), bf16_pair(dh[2], dh[3]), bf16_pair(dl[0], dl[1]), bf16_pair(dl[2], dl[3])};
+            hi = u32x4{lo.x, lo.y, 0u, 0u};
+        } else if (mode == AUG_COMP) {
+            lo = pf.w[6];
+            hi = pf.w[6];
+        }
+        u32x4 *dst = reinterpret_cast<u32x4 *>(abuf + (tid / G::NBLK) * AROW);
+        dst[0] = lo;
+        dst[1] = hi;
+    }
 }
 
-template <int HD, bool BF16>
-__device__ __forceinline__ void stage_tile(uint16_t *buf, const Prefetch &pf, int sk) {
-    if (sk == STAGE_INT2) stage_only<HD, BF16, STAGE_INT2>(buf, pf);
-    else if (sk == STAGE_INT4) stage_only<HD, BF16, STAGE_INT4>(buf, pf);
-    else if (sk == STAGE_RAW) stage_only<HD, BF16, STAGE_RAW>(buf, pf);
+template <int HD, bool BF16, int SK, bool AUG>
+__device__ __forceinline__ void stage_only(uint16_t *buf, uint16_t *abuf, const PrefetchT<AUG> &pf, int amode) {
+    uint32_t ko[8], vo[8];
+    dequant_unit<SK, BF16, AUG>(pf, threadIdx.x % Geo<HD>::NBLK, ko, vo);
+    write_unit<HD>(buf, ko, vo);
+    write_aug<HD, AUG>(abuf, pf, amode);
+}
+
+template <int HD, bool BF16, bool AUG>
+__device__ __forceinline__ void stage_tile(uint16_t *buf, uint16_t *abuf, const PrefetchT<AUG> &pf, int sk,
+                                           int amode) {
+    if (sk == STAGE_INT2) stage_only<HD, BF16, STAGE_INT2, AUG>(buf, abuf, pf, amode);
+    else if (sk == STAGE_INT4) stage_only<HD, BF16, STAGE_INT4, AUG>(buf, abuf, pf, amode);
+    else if (sk == STAGE_RAW) stage_only<HD, BF16, STAGE_RAW, AUG>(buf, abuf, pf, amode);
+    else if constexpr (AUG) {
+        if (sk == STAGE_INT2T) stage_only<HD, BF16, STAGE_INT2T, AUG>(buf, abuf, pf, amode);
+        else if (sk == STAGE_INT4T) stage_only<HD, BF16, STAGE_INT4T, AUG>(buf, abuf, pf, amode);
+    }
 }
 
 // ---------------------------------------------------------------- per-wave state and compute
@@ -405,6 +497,7 @@ template <int HD, bool BF16> struct Ctx {
     float *btab;      // LDS [32 K-groups][32 queries]: Jensen sums of the current block of groups
     float m, l;       // running max (log2 domain) and this lane's partial row sum
     float beta;       // Jensen term of the current group, log2 domain
+    bf16x8 qa;        // B operand of the per-token K columns (k-slots 8 hh .. 8 hh + 7), AUG only
 };
 
 // Jensen sums of K-groups g0 .. g0+31 of a segment for the wave's 32 queries:
@@ -520,8 +613,8 @@ constexpr int kSchedValu = 0x002, kSchedMfma = 0x008, kSchedDsRead = 0x100, kSch
 // One of 8 slices of the dequantization of the thread's unit (k = 0..7: keys in 0..3,
 // values in 4..7), so that it can be spread between matrix products. ko / vo complete after
 // slices 3 / 7; tab carries the INT2 value table from slice 4 on.
-template <int SK, bool BF16>
-__device__ __forceinline__ void dequant_slice(const Prefetch &pf, int b, int k, uint32_t (&ko)[8],
+template <int SK, bool BF16, bool AUG>
+__device__ __forceinline__ void dequant_slice(const PrefetchT<AUG> &pf, int b, int k, uint32_t (&ko)[8],
                                               uint32_t (&vo)[8], uint32_t (&tab)[2]) {
     typedef Elem<BF16> E;
     if constexpr (SK == STAGE_RAW) {
@@ -536,12 +629,16 @@ __device__ __forceinline__ void dequant_slice(const Prefetch &pf, int b, int k, 
                                      E::raw_to_f16(pf.w[3].z), E::raw_to_f16(pf.w[3].w)};
             to_positions(vd8, vo);
         }
-    } else if constexpr (SK == STAGE_INT2 || SK == STAGE_INT4) {
-        const uint32_t km[16] = {pf.w[0].x, pf.w[0].y, pf.w[0].z, pf.w[0].w, pf.w[1].x, pf.w[1].y,
-                                 pf.w[1].z, pf.w[1].w, pf.w[2].x, pf.w[2].y, pf.w[2].z, pf.w[2].w,
-                                 pf.w[3].x, pf.w[3].y, pf.w[3].z, pf.w[3].w};
+    } else if constexpr (SK == STAGE_INT2 || SK == STAGE_INT4 || SK == STAGE_INT2T || SK == STAGE_INT4T) {
+        constexpr bool TOK = SK == STAGE_INT2T || SK == STAGE_INT4T;   // per-token K group: one step/zero
+        const uint32_t km[16] = {pf.w[0].x, TOK ? pf.w[0].x : pf.w[0].y, TOK ? pf.w[0].x : pf.w[0].z,
+                                 TOK ? pf.w[0].x : pf.w[0].w, TOK ? pf.w[0].x : pf.w[1].x, TOK ? pf.w[0].x : pf.w[1].y,
+                                 TOK ? pf.w[0].x : pf.w[1].z, TOK ? pf.w[0].x : pf.w[1].w, TOK ? pf.w[0].x : pf.w[2].x,
+                                 TOK ? pf.w[0].x : pf.w[2].y, TOK ? pf.w[0].x : pf.w[2].z, TOK ? pf.w[0].x : pf.w[2].w,
+                                 TOK ? pf.w[0].x : pf.w[3].x, TOK ? pf.w[0].x : pf.w[3].y, TOK ? pf.w[0].x : pf.w[3].z,
+                                 TOK ? pf.w[0].x : pf.w[3].w};
         const u32x4 c = pf.w[4];   // key word pair, value word pair
-        if constexpr (SK == STAGE_INT2) {
+        if constexpr (SK == STAGE_INT2 || SK == STAGE_INT2T) {
             const bool odd = b & 1;
             if (k < 4) {
                 k2_step<BF16>(odd ? c.y : c.x, km, k, ko);
@@ -582,9 +679,10 @@ __device__ __forceinline__ void write_values(uint16_t *buf, const uint32_t (&vo)
 // order, so the dequantization is written between the products: the matrix core works
 // through each product while the vector unit converts. Operand reads run LEAD products
 // ahead through a ring of registers.
-template <int HD, bool BF16, int SK>
+template <int HD, bool BF16, int SK, bool AUG>
 __device__ __forceinline__ void qk_stage(const Ctx<HD, BF16> &cx, const uint16_t *kl, uint16_t *nbuf,
-                                         const Prefetch &pf, f32x16 (&s)[2]) {
+                                         const uint16_t *acur, uint16_t *anext, const PrefetchT<AUG> &pf,
+                                         f32x16 (&s)[2], int amode) {
     typedef Ctx<HD, BF16> C;
     typedef typename C::vec vec;
     typedef Geo<HD> G;
@@ -610,7 +708,7 @@ __device__ __forceinline__ void qk_stage(const Ctx<HD, BF16> &cx, const uint16_t
         s[i / C::KS] = C::E::mma(ka[i % (LEAD + 1)], cx.q[i % C::KS], s[i / C::KS]);
         if (i % EVERY == 0) {
             const int k = i / EVERY;
-            dequant_slice<SK, BF16>(pf, b, k, ko, vo, tab);
+            dequant_slice<SK, BF16, AUG>(pf, b, k, ko, vo, tab);
             if (SK != STAGE_NONE && k == 3) write_keys<HD>(nbuf, ko);
             if (SK != STAGE_NONE && k == 7) write_values<HD>(nbuf, vo);
         }
@@ -625,6 +723,16 @@ __device__ __forceinline__ void qk_stage(const Ctx<HD, BF16> &cx, const uint16_t
         if (i == NP / 2 - 1 || i == NP - 1) __builtin_amdgcn_sched_group_barrier(kSchedDsWrite, 2, 0);
     }
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (AUG) {
+        // the per-token K columns: one more k-step per 32-token half, bf16 whatever the
+        // element dtype; and the next tile's columns into the other buffer
+        if (SK != STAGE_NONE) write_aug<HD, AUG>(anext, pf, amode);
+        const uint16_t *ar = acur + r32 * AROW + 8 * hh;
+        const bf16x8 a0 = *reinterpret_cast<const bf16x8 *>(ar);
+        const bf16x8 a1 = *reinterpret_cast<const bf16x8 *>(ar + 32 * AROW);
+        s[0] = mfma32_bf16(a0, cx.qa, s[0]);
+        s[1] = mfma32_bf16(a1, cx.qa, s[1]);
+    }
 }
 
 // Two of the 8 probabilities of the 16 tokens 16 st .. 16 st + 15 (scores
@@ -754,15 +862,88 @@ __device__ __forceinline__ void append_units(const QuantAppendParams app, int bi
         const int g = (int)(u % n_groups);
         const int64_t r = u / n_groups;
         const int h = (int)(r % n_heads), b = (int)(r / n_heads);
-        if (bits == 2) qz::quant_group<T, HD, 2, kThreads>(app, g, h, b, n_groups);
-        else qz::quant_group<T, HD, 4, kThreads>(app, g, h, b, n_groups);
+        if (bits == 2) qz::quant_group<T, HD, 2, kThreads, false>(app, g, h, b, n_groups);
+        else qz::quant_group<T, HD, 4, kThreads, false>(app, g, h, b, n_groups);
         __syncthreads();   // the next unit reuses the group statistics in LDS
     }
 }
 
+// B operand of the per-token K columns for the lane's query: per-token K groups take
+// k q2_g (k = -tau/24, q2_g the sum of the query's squares over group g's channels, or
+// |q|^2 times the group's share of the channels in the isotropic form) as bf16 high and
+// low parts; the compensation takes U_h^T q, the same way. Lanes of half hh hold k-slots
+// 8 hh .. 8 hh + 7.
+template <int HD, bool BF16>
+__device__ __forceinline__ void aug_operand(Ctx<HD, BF16> &cx, const AttnParams &p, int h) {
+    typedef Ctx<HD, BF16> C;
+    const int hh = (threadIdx.x % kWave) / 32;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (p.aug == AUG_TOKEN) {
+        float q2[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int ks = 0; ks < C::KS; ++ks) {
+            const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+            float part = 0.f;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float qv = C::E::val((qw[i / 2] >> (16 * (i % 2))) & 0xffffu);
+                part = __builtin_fmaf(qv, qv, part);
+            }
+            const int g = (16 * ks) / p.aug_kgc;
+#pragma unroll
+            for (int gg = 0; gg < 4; ++gg) q2[gg] += gg == g ? part : 0.f;
+        }
+        float tot = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            q2[g] += other_half(q2[g]);
+            tot += q2[g];
+        }
+        const int ng = HD / p.aug_kgc;
+        const float kap = p.jensen == 0 ? 0.f : -p.beta_log2 / p.scale_log2;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+            const float v = g < ng ? kap * (p.jensen == JENSEN_ISO ? tot / ng : q2[g]) : 0.f;
+            const float vh = (float)(__bf16)v;
+            const float vl = v - vh;
+            x[g] = hh == 0 ? vh : vl;
+            x[4 + g] = hh == 0 ? vh : 0.f;
+        }
+    } else if (p.aug == AUG_COMP) {
+        const float *U = p.aug_basis + (size_t)h * HD * p.aug_rank;
+        for (int j = 0; j < p.aug_rank; ++j) {
+            float acc = 0.f;
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks) {
+                const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const int ch = 16 * ks + 4 * (i % 4) + 2 * hh + i / 4;
+                    const float qv = C::E::val((qw[i / 2] >> (16 * (i % 2))) & 0xffffu);
+                    acc = __builtin_fmaf(U[(size_t)ch * p.aug_rank + j], qv, acc);
+                }
+            }
+            acc += other_half(acc);
+            const float vh = (float)(__bf16)acc;
+            const float vl = acc - vh;
+#pragma unroll
+            for (int jj = 0; jj < 8; ++jj) x[jj] = jj == j ? (hh == 0 ? vh : vl) : x[jj];
+        }
+    }
+    bf16x8 qa;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) qa[i] = (__bf16)x[i];
+    cx.qa = qa;
+}
+
+__device__ __forceinline__ int aug_mode(const Tile &t) {
+    return t.kind() == TILE_PTOK ? AUG_TOKEN : (t.kind() == TILE_PACKED && t.comp() ? AUG_COMP : AUG_ZERO);
+}
+
 // EXACT: the all-orders Jensen form (its direct per-channel evaluation in its own instance,
-// so the other forms keep their register allocation).
-template <int HD, bool BF16, bool EXACT>
+// so the other forms keep their register allocation). AUG: segments with per-token K
+// columns (per-token K groups, or the low-rank compensation), in an instance of their own.
+template <int HD, bool BF16, bool EXACT, bool AUG>
 __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     if (blockIdx.x >= (unsigned)p.n_attn_wg) {
         // a copy of the append's fields: the kernel argument itself is never addressed
@@ -773,6 +954,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     typedef typename C::vec vec;
     typedef Geo<HD> G;
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G::BUF];
+    __shared__ __attribute__((aligned(16))) uint16_t augs[AUG ? 2 * TT * AROW : 8];
     __shared__ float btab_all[kWaves][32 * 32];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: wave_ok branches on scalars
@@ -830,6 +1012,7 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
                 cx.q[ks] = __builtin_bit_cast(vec, o);
             }
         }
+        if constexpr (AUG) aug_operand<HD, BF16>(cx, p, h);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) cx.o[db] = f32x16{};
         cx.btab = btab_all[wave];
@@ -859,18 +1042,21 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         // Pipeline per tile i (one barrier per tile): tile i is computed out of LDS buffer i%2
         // while tile i+1, loaded into registers during tile i-1, is dequantized into buffer
         // (i+1)%2; then tile i+2 is loaded into the registers.
-        Prefetch pf;
+        PrefetchT<AUG> pf;
         if (cur.kind() != TILE_END) {
-            prefetch_tile<HD>(pf, p, cur, bh);
-            stage_tile<HD, BF16>(smem, pf, stage_kind(cur));
+            prefetch_tile<HD, AUG>(pf, p, cur, bh);
+            stage_tile<HD, BF16, AUG>(smem, augs, pf, stage_kind(cur), aug_mode(cur));
         }
-        if (nxt.kind() != TILE_END) prefetch_tile<HD>(pf, p, nxt, bh);
+        if (nxt.kind() != TILE_END) prefetch_tile<HD, AUG>(pf, p, nxt, bh);
         __syncthreads();
         int buf = 0, it = 0;  // cur is tile it of the piece
         while (cur.kind() != TILE_END) {
             const int sk = stage_kind(nxt);
             const uint16_t *cbuf = smem + buf * G::BUF;
             uint16_t *nbuf = smem + (buf ^ 1) * G::BUF;
+            const uint16_t *acur = augs + (AUG ? buf * TT * AROW : 0);
+            uint16_t *anext = augs + (AUG ? (buf ^ 1) * TT * AROW : 0);
+            const int amode = aug_mode(nxt);
             if (wave_ok) {
                 if (cur.kind() == TILE_PACKED) {
                     if (cur.batch()) {
@@ -884,15 +1070,19 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
                     cx.beta = 0.f;
                 }
                 f32x16 s[2];
-                if (sk == STAGE_INT2) qk_stage<HD, BF16, STAGE_INT2>(cx, cbuf, nbuf, pf, s);
-                else if (sk == STAGE_INT4) qk_stage<HD, BF16, STAGE_INT4>(cx, cbuf, nbuf, pf, s);
-                else if (sk == STAGE_RAW) qk_stage<HD, BF16, STAGE_RAW>(cx, cbuf, nbuf, pf, s);
-                else qk_stage<HD, BF16, STAGE_NONE>(cx, cbuf, nbuf, pf, s);
+                if (sk == STAGE_INT2) qk_stage<HD, BF16, STAGE_INT2, AUG>(cx, cbuf, nbuf, acur, anext, pf, s, amode);
+                else if (sk == STAGE_INT4) qk_stage<HD, BF16, STAGE_INT4, AUG>(cx, cbuf, nbuf, acur, anext, pf, s, amode);
+                else if (sk == STAGE_RAW) qk_stage<HD, BF16, STAGE_RAW, AUG>(cx, cbuf, nbuf, acur, anext, pf, s, amode);
+                else if (AUG && sk == STAGE_INT2T)
+                    qk_stage<HD, BF16, STAGE_INT2T, AUG>(cx, cbuf, nbuf, acur, anext, pf, s, amode);
+                else if (AUG && sk == STAGE_INT4T)
+                    qk_stage<HD, BF16, STAGE_INT4T, AUG>(cx, cbuf, nbuf, acur, anext, pf, s, amode);
+                else qk_stage<HD, BF16, STAGE_NONE, AUG>(cx, cbuf, nbuf, acur, anext, pf, s, amode);
                 softmax_pv<HD, BF16>(cx, cbuf + G::KBUF, s, cur.len, p.scale_log2);
-                if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
+                if (far.kind() != TILE_END) prefetch_tile<HD, AUG>(pf, p, far, bh);
             } else {
-                stage_tile<HD, BF16>(nbuf, pf, sk);
-                if (far.kind() != TILE_END) prefetch_tile<HD>(pf, p, far, bh);
+                stage_tile<HD, BF16, AUG>(nbuf, anext, pf, sk, amode);
+                if (far.kind() != TILE_END) prefetch_tile<HD, AUG>(pf, p, far, bh);
             }
             if (nxt.kind() == TILE_END) break;
             __syncthreads();
@@ -1100,9 +1290,11 @@ hipError_t launch_t(const AttnParams &p0, hipStream_t s) {
         n_app = (unsigned)((U + p.app_per_wg - 1) / p.app_per_wg);
     }
     if (p.jensen == JENSEN_EXACT)
-        hipLaunchKernelGGL((attention_kernel<HD, BF16, true>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, true, false>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
+    else if (p.aug != 0)
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, false, true>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((attention_kernel<HD, BF16, false>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
+        hipLaunchKernelGGL((attention_kernel<HD, BF16, false, false>), dim3(n_wg + n_app), dim3(kThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.quota % p.tok_pad == 0) return e;   // no row block was split
     hipLaunchKernelGGL((piece_combine_kernel<HD>), dim3(n_wg, BM / (256 / (HD / 8))), dim3(256), 0, s, p);

@@ -22,6 +22,10 @@ struct QuantAppendParams {
     void *k_dst, *v_dst;
     void *k_meta, *v_meta;
     int32_t *kgroup_start;
+    int32_t k_group_channels;    // > 0: per-token K groups of that many channels
+    int32_t comp_rank;           // > 0: write the compensation c_t (rank <= 8)
+    const float *comp_basis;     // [n_kv_heads][head_dim][comp_rank]
+    void *k_comp;                // bf16 [batch][n_kv_heads][capacity][8]
 };
 hipError_t launch_quant_append(const QuantAppendParams &p, int bits, int n_groups, hipStream_t s);
 
@@ -46,10 +50,12 @@ void window_budget(int n_windows, int pct_fp16, int pct_int4, int *n_fp16, int *
 constexpr int kMaxSegments = 8;
 
 struct SegmentView {
-    int32_t bits, n_tokens, n_kgroups, capacity, kgroup_capacity, v_group_channels, token_begin, pad_;
+    int32_t bits, n_tokens, n_kgroups, capacity, kgroup_capacity, v_group_channels, token_begin;
+    int32_t k_group_channels;      // > 0: per-token K groups (k_meta [cap][head_dim / k_group_channels])
     const void *k, *v;
     const uint32_t *k_meta, *v_meta;
     const int32_t *kgroup_start;
+    const uint16_t *k_comp;        // compensation c_t, bf16 [cap][8] per (b, h); nullptr: none
 };
 
 struct AttnParams {
@@ -66,6 +72,10 @@ struct AttnParams {
                                    // the all-orders one (computed in log2 units), else 0
     float half_scale;              // scale / 2: a_c = half_scale |q_c| step_c (all-orders form)
     int32_t jensen;                // kvq_jensen
+    // per-token K columns: 0 none, 1 per-token K groups of aug_kgc channels, 2 the low-rank
+    // compensation of rank aug_rank with basis aug_basis [n_kv_heads][head_dim][aug_rank]
+    int32_t aug, aug_kgc, aug_rank;
+    const float *aug_basis;
     void *out;
     int32_t out_dtype;
     float *lse;

@@ -19,6 +19,8 @@
 // each token's 32-channel runs.
 #pragma once
 
+#include <type_traits>
+
 #include "kvq_device.cuh"
 #include "kvq_internal.h"
 
@@ -200,11 +202,89 @@ __device__ __forceinline__ void v_row(const float (&y)[8], int r, int len, int c
     }
 }
 
+// value of the lane whose index differs in bit 2 or bit 3 (the 8-channel chunks of a row
+// are consecutive lanes)
+__device__ __forceinline__ float lane_xor(float v, int m) { return __shfl_xor(v, m); }
+
+// Codes of one row's 8 channels of K with per-token groups of GW channels (GW / 8 lanes of
+// the row share a group), their step/zero, and the store. As v_row, for any group width.
+template <int HD, int BITS, int GW>
+__device__ __forceinline__ void k_token_row(const float (&x)[8], int r, int len, int cc, uint32_t *kcodes,
+                                            uint32_t *km_base) {
+    constexpr int L = (1 << BITS) - 1;
+    constexpr int WPR = HD * BITS / 32;
+    constexpr int LPG = GW / 8;   // lanes per group
+    float a = x[0], z = x[0];
+#pragma unroll
+    for (int i = 1; i < 8; ++i) { a = fminf(a, x[i]); z = fmaxf(z, x[i]); }
+    a = fminf(a, quad_xor1(a)); z = fmaxf(z, quad_xor1(z));
+    a = fminf(a, quad_xor2(a)); z = fmaxf(z, quad_xor2(z));
+    if (LPG >= 8) { a = fminf(a, lane_xor(a, 4)); z = fmaxf(z, lane_xor(z, 4)); }
+    if (LPG >= 16) { a = fminf(a, lane_xor(a, 8)); z = fmaxf(z, lane_xor(z, 8)); }
+    Quant kq;
+    kq.set(a, z, L);
+    const float kinv = kq.inv();
+    bool near = false;
+    float kc[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kc[i] = fast_code(x[i], kq.zero, kinv, L, near);
+    uint32_t kbits = pack_codes<BITS>(kc);
+    if (__builtin_expect(__any(near), 0)) {
+        kbits = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kbits |= kq.code(x[i], L) << (BITS * i);
+    }
+    const uint32_t kn = quad_xor1(kbits);
+    if (r < len) {
+        if (cc % LPG == 0) km_base[(size_t)r * (HD / GW) + cc / LPG] = kq.meta;
+        if (BITS == 4) kcodes[(size_t)r * WPR + cc] = kbits;
+        else if ((cc & 1) == 0) kcodes[(size_t)r * WPR + cc / 2] = kbits | (kn << 16);
+    }
+}
+
+// The compensation of one row: c_j = sum over the row's channels of U[c][j] (x_c - khat_c),
+// khat the dequantized key (the element dtype's rounding of code * step + zero), each of
+// the row's lanes taking its 8 channels, the sum completed across the row's CC lanes in
+// fp32, then one rounding to bf16. U is staged in LDS as [j][channel]. The row's first lane
+// stores the 8 bf16 entries (zeros past the rank).
+template <int HD, int BITS, bool BF16>
+__device__ __forceinline__ void comp_row(const float (&x)[8], const uint32_t kbits, int r, int len, int cc,
+                                         const Quant (&kq)[8], const float *u_lds, int rank, uint16_t *comp) {
+    constexpr int CC = HD / 8;
+    constexpr uint32_t M = (1u << BITS) - 1;
+    float e[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float y = __builtin_fmaf((float)((kbits >> (BITS * i)) & M), kq[i].step, kq[i].zero);
+        const float yh = BF16 ? (float)(__bf16)y : (float)(_Float16)y;
+        e[i] = x[i] - yh;
+    }
+    uint32_t packed[4] = {0u, 0u, 0u, 0u};
+    for (int j = 0; j < rank; ++j) {
+        const f32x4 u0 = *reinterpret_cast<const f32x4 *>(u_lds + j * HD + cc * 8);
+        const f32x4 u1 = *reinterpret_cast<const f32x4 *>(u_lds + j * HD + cc * 8 + 4);
+        float acc = u0.x * e[0];
+        acc = __builtin_fmaf(u0.y, e[1], acc);
+        acc = __builtin_fmaf(u0.z, e[2], acc);
+        acc = __builtin_fmaf(u0.w, e[3], acc);
+        acc = __builtin_fmaf(u1.x, e[4], acc);
+        acc = __builtin_fmaf(u1.y, e[5], acc);
+        acc = __builtin_fmaf(u1.z, e[6], acc);
+        acc = __builtin_fmaf(u1.w, e[7], acc);
+#pragma unroll
+        for (int o = 1; o < CC; o <<= 1) acc += __shfl_xor(acc, o);
+        const uint32_t hb = f32_to_bf16_bits(acc);
+        packed[j / 2] |= hb << (16 * (j % 2));
+    }
+    if (r < len && cc == 0)
+        *reinterpret_cast<u32x4 *>(comp + (size_t)r * 8) = u32x4{packed[0], packed[1], packed[2], packed[3]};
+}
+
 // Codes of one row's 8 channels of K against the group's per-channel step/zero, and
 // their store (as v_row).
 template <int HD, int BITS>
-__device__ __forceinline__ void k_row(const float (&x)[8], int r, int len, int cc, const Quant (&kq)[8],
-                                      const float (&kinv)[8], uint32_t *kcodes) {
+__device__ __forceinline__ uint32_t k_row(const float (&x)[8], int r, int len, int cc, const Quant (&kq)[8],
+                                          const float (&kinv)[8], uint32_t *kcodes) {
     constexpr int L = (1 << BITS) - 1;
     constexpr int WPR = HD * BITS / 32;
     bool near = false;
@@ -222,6 +302,35 @@ __device__ __forceinline__ void k_row(const float (&x)[8], int r, int len, int c
         if (BITS == 4) kcodes[(size_t)r * WPR + cc] = kbits;
         else if ((cc & 1) == 0) kcodes[(size_t)r * WPR + cc / 2] = kbits | (kn << 16);
     }
+    return kbits;
+}
+
+// Per-token K groups: no K-group statistics; rows are coded one after another, keys as
+// values are, with the group width of the segment.
+template <typename T, int HD, int BITS, int NT, int GW>
+__device__ __forceinline__ void token_group_rows(const T *ks, const T *vs, int len, uint32_t *kcodes,
+                                                 uint32_t *vcodes, uint32_t *km_base, uint32_t *vm_base) {
+    constexpr int CC = HD / 8;
+    constexpr int RP = NT / CC;
+    typedef typename Src<T>::Raw Raw;
+    const int tid = threadIdx.x, cc = tid % CC, rp = tid / CC;
+    for (int b0 = 0; b0 < len; b0 += kBatch2 * RP) {
+        Raw kraw[kBatch2], vraw[kBatch2];
+#pragma unroll
+        for (int u = 0; u < kBatch2; ++u) {
+            const int rr = min(b0 + u * RP + rp, len - 1);
+            kraw[u] = Src<T>::load(ks + (size_t)rr * HD);
+            vraw[u] = Src<T>::load(vs + (size_t)rr * HD);
+        }
+#pragma unroll
+        for (int u = 0; u < kBatch2; ++u) {
+            float x[8], y[8];
+            Src<T>::unpack(kraw[u], x);
+            Src<T>::unpack(vraw[u], y);
+            v_row<HD, BITS>(y, b0 + u * RP + rp, len, cc, vcodes, vm_base);
+            k_token_row<HD, BITS, GW>(x, b0 + u * RP + rp, len, cc, kcodes, km_base);
+        }
+    }
 }
 
 // One K-group g (of n_groups appended) of one (batch b, KV head h) by a workgroup of NT
@@ -229,7 +338,9 @@ __device__ __forceinline__ void k_row(const float (&x)[8], int r, int len, int c
 // Every thread of the workgroup calls it, in uniform control flow; it holds barriers, and
 // a caller that runs it again must pass a barrier in between (the LDS statistics are
 // reused).
-template <typename T, int HD, int BITS, int NT>
+// EXT: also the per-token K groups and the compensation (off where only the plain layout
+// can occur, so that those paths take no code or registers there).
+template <typename T, int HD, int BITS, int NT, bool EXT = true>
 __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, int h, int b, int n_groups) {
     constexpr int L = (1 << BITS) - 1;
     constexpr int CC = HD / 8;            // 8-channel chunks per token row
@@ -256,6 +367,28 @@ __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, i
     uint32_t *kcodes = reinterpret_cast<uint32_t *>(p.k_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
     uint32_t *vcodes = reinterpret_cast<uint32_t *>(p.v_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
     uint32_t *vm_base = reinterpret_cast<uint32_t *>(p.v_meta) + (bh * p.capacity + p.n_tokens + dst0) * (HD / VG);
+
+    if (EXT && p.k_group_channels > 0) {
+        uint32_t *km_base = reinterpret_cast<uint32_t *>(p.k_meta) +
+                            (bh * p.capacity + p.n_tokens + dst0) * (HD / p.k_group_channels);
+        if (p.k_group_channels == 32)
+            token_group_rows<T, HD, BITS, NT, 32>(ks, vs, len, kcodes, vcodes, km_base, vm_base);
+        else if (p.k_group_channels == 64)
+            token_group_rows<T, HD, BITS, NT, 64>(ks, vs, len, kcodes, vcodes, km_base, vm_base);
+        else
+            token_group_rows<T, HD, BITS, NT, HD>(ks, vs, len, kcodes, vcodes, km_base, vm_base);
+        return;
+    }
+    // the compensation basis of head h, as [j][channel], for comp_row
+    __shared__ float u_lds[EXT ? 8 * HD : 1];
+    const int rank = EXT ? p.comp_rank : 0;
+    if (rank > 0) {
+        const float *U = p.comp_basis + (size_t)h * HD * rank;
+        for (int i = tid; i < HD * rank; i += NT) u_lds[(i % rank) * HD + i / rank] = U[i];
+    }
+    uint16_t *comp = rank > 0 ? reinterpret_cast<uint16_t *>(p.k_comp) + (bh * p.capacity + p.n_tokens + dst0) * 8
+                              : nullptr;
+    constexpr bool kBf16Elem = std::is_same<T, __bf16>::value;
 
     // ---- K: per-channel extremes over the group's tokens ----
     // Rows are read in batches whose loads are all in flight together; a thread's rows
@@ -367,7 +500,8 @@ __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, i
             if (u * RP < len) {
                 float x[8];
                 Src<T>::unpack(kres[u], x);
-                k_row<HD, BITS>(x, u * RP + rp, len, cc, kq, kinv, kcodes);
+                const uint32_t kb = k_row<HD, BITS>(x, u * RP + rp, len, cc, kq, kinv, kcodes);
+                if (rank > 0) comp_row<HD, BITS, kBf16Elem>(x, kb, u * RP + rp, len, cc, kq, u_lds, rank, comp);
             }
         }
     } else {
@@ -385,7 +519,9 @@ __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, i
                 Src<T>::unpack(kraw[u], x);
                 Src<T>::unpack(vraw[u], y);
                 v_row<HD, BITS>(y, b0 + u * RP + rp, len, cc, vcodes, vm_base);
-                k_row<HD, BITS>(x, b0 + u * RP + rp, len, cc, kq, kinv, kcodes);
+                const uint32_t kb = k_row<HD, BITS>(x, b0 + u * RP + rp, len, cc, kq, kinv, kcodes);
+                if (rank > 0)
+                    comp_row<HD, BITS, kBf16Elem>(x, kb, b0 + u * RP + rp, len, cc, kq, u_lds, rank, comp);
             }
         }
     }

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define KVQ_ABI_VERSION 2
+#define KVQ_ABI_VERSION 3
 #define KVQ_MAX_SEGMENTS 8
 
 typedef enum kvq_status {
@@ -105,8 +105,33 @@ typedef enum kvq_jensen {
  *   kgroup_start  bits 2|4: int32 [kgroup_capacity + 1]; K-group g holds tokens
  *            [kgroup_start[g], kgroup_start[g+1]), the same for every (b, h).
  *   For bits 16 k_meta, v_meta and kgroup_start are unused and may be NULL.
- * The descriptor lives in host memory; n_tokens and n_kgroups mirror the device state
- * and are advanced by kvq_quantize_append.
+ *
+ * Per-token K groups (k_group_channels > 0; 0 is the per-channel layout above): keys are
+ * grouped like values, one group per (token, run of k_group_channels channels), the
+ * geometry in which the Jensen term's query-norm form is exact [JB: "computed ... from the
+ * quantization step sizes of the cached keys and the query norm"]: with k_group_channels
+ * == head_dim every channel of a token has the same step, and the channel-weighted term
+ * is tau^2/24 * |q|^2 * step_t^2.
+ *   k_meta   {fp16 step, fp16 zero} [batch][n_kv_heads][capacity][head_dim/k_group_channels];
+ *            kgroup_start, kgroup_capacity and n_kgroups are unused (kgroup_start may be
+ *            NULL; n_kgroups stays 0), and k_group_tokens only sets how many tokens one
+ *            append workgroup takes.
+ *
+ * Low-rank logit compensation (comp_rank r > 0, PSAC-style ["QuantWM Preserves Attention
+ * in 2-Bit KV Cache Quantization for Video World Models": compensating key error along
+ * the dominant query subspace]): each appended token stores the projection of its key's
+ * rounding error onto an r-dimensional query subspace, and attention adds it back for the
+ * part of the query inside that subspace. For queries in the subspace the logits are those
+ * of the unquantized keys (up to the bf16 rounding of the stored projection); the part of
+ * the query orthogonal to it sees the quantized keys alone.
+ *   comp_basis  device float32 [n_kv_heads][head_dim][r]: U_h, orthonormal columns (the
+ *            caller's estimate of the dominant subspace of the queries that read KV head h).
+ *   k_comp   device bf16 [batch][n_kv_heads][capacity][8]: c_t = bf16(U_h^T (k_t - khat_t))
+ *            in the first r entries of token t's row, zeros after, khat_t the dequantized
+ *            key (written by kvq_quantize_append; the difference is exact, the projection
+ *            summed in fp32).
+ *   Attention adds tau * (U_h^T q) . c_t to the logit of token t. 1 <= r <= 8.
+ * A segment uses per-token K groups or the compensation, not both.
  */
 typedef struct kvq_segment {
     int32_t bits;              /* 2, 4 (packed codes) or 16 (raw elements) */
@@ -121,6 +146,10 @@ typedef struct kvq_segment {
     void *k, *v;               /* device */
     void *k_meta, *v_meta;     /* device */
     int32_t *kgroup_start;     /* device */
+    int32_t k_group_channels;  /* 0: per-channel K groups; 32, 64 or 128 (<= head_dim): per-token */
+    int32_t comp_rank;         /* 0: no compensation; 1..8: rank r */
+    const float *comp_basis;   /* device, comp_rank > 0 */
+    void *k_comp;              /* device, comp_rank > 0 */
 } kvq_segment;
 
 /*

@@ -47,7 +47,8 @@ class OrcSegment(ctypes.Structure):
     _fields_ = [("bits", I32), ("elem_dtype", I32), ("capacity", I32), ("n_tokens", I32),
                 ("n_kgroups", I32), ("kgroup_capacity", I32), ("v_group_channels", I32),
                 ("k_codes", P), ("v_codes", P), ("k_meta", P), ("v_meta", P),
-                ("kgroup_start", P), ("k_raw", P), ("v_raw", P)]
+                ("kgroup_start", P), ("k_raw", P), ("v_raw", P),
+                ("k_group_channels", I32), ("comp_rank", I32), ("comp_basis", P), ("k_comp", P)]
 
 
 def _declare(L):
@@ -62,11 +63,13 @@ def _declare(L):
     L.orc_dequant.restype = F64
     L.orc_pack_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P]; L.orc_pack_row.restype = None
     L.orc_unpack_row.argtypes = [P, ctypes.c_int, ctypes.c_int, P]; L.orc_unpack_row.restype = None
-    L.orc_append.argtypes = [ctypes.c_int] * 11 + [P] * 7 + [P, P, I64, ctypes.c_int, P, ctypes.c_int]
+    L.orc_append.argtypes = ([ctypes.c_int] * 11 + [P] * 7 + [P, P, I64, ctypes.c_int, P, ctypes.c_int]
+                             + [ctypes.c_int, ctypes.c_int, P, P])
+    L.orc_f64_to_bf16.argtypes = [F64]; L.orc_f64_to_bf16.restype = U16
     L.orc_append.restype = ctypes.c_int
     L.orc_log_sinhc.argtypes = [F64]; L.orc_log_sinhc.restype = F64
     L.orc_attend_row.argtypes = [P, ctypes.c_int, P, P, P, I64, P, ctypes.c_int, F64, ctypes.c_int,
-                                 P, P, P]
+                                 P, P, P, P]
     L.orc_attend_row.restype = None
     L.orc_attention.argtypes = [P] + [ctypes.c_int] * 5 + [P, ctypes.c_int, P, P, ctypes.c_int,
                                                            F64, ctypes.c_int, ctypes.c_int, P,
@@ -147,9 +150,15 @@ def unpack_row(words: np.ndarray, d: int, bits: int) -> np.ndarray:
 
 # -------------------------------------------------------------------- segments
 def new_segment(bits: int, elem: str, B: int, H: int, d: int, capacity: int,
-                k_group_tokens: int, kgroup_capacity: int, v_group_channels: int = 32) -> Dict:
+                k_group_tokens: int, kgroup_capacity: int, v_group_channels: int = 32,
+                k_group_channels: int = 0, comp_basis: Optional[np.ndarray] = None) -> Dict:
+    """k_group_channels > 0: per-token K groups of that many channels (k_meta [B][H][cap]
+    [d/kgc][2]). comp_basis float32 [H][d][r]: the low-rank compensation, c stored as bf16
+    bits in k_comp [B][H][cap][8] (the first r entries)."""
+    r = 0 if comp_basis is None else comp_basis.shape[2]
     seg = dict(bits=bits, elem=elem, B=B, H=H, d=d, capacity=capacity, n_tokens=0, n_kgroups=0,
-               Gk=k_group_tokens, Gv=v_group_channels, kgroup_capacity=kgroup_capacity)
+               Gk=k_group_tokens, Gv=v_group_channels, kgroup_capacity=kgroup_capacity,
+               kgc=k_group_channels, comp_rank=r)
     if bits == 16:
         seg["k_raw"] = np.zeros((B, H, capacity, d), np.uint16)
         seg["v_raw"] = np.zeros((B, H, capacity, d), np.uint16)
@@ -157,9 +166,15 @@ def new_segment(bits: int, elem: str, B: int, H: int, d: int, capacity: int,
         wpr = d * bits // 32
         seg["k_codes"] = np.zeros((B, H, capacity, wpr), np.uint32)
         seg["v_codes"] = np.zeros((B, H, capacity, wpr), np.uint32)
-        seg["k_meta"] = np.zeros((B, H, kgroup_capacity, d, 2), np.uint16)
+        if k_group_channels:
+            seg["k_meta"] = np.zeros((B, H, capacity, d // k_group_channels, 2), np.uint16)
+        else:
+            seg["k_meta"] = np.zeros((B, H, kgroup_capacity, d, 2), np.uint16)
         seg["v_meta"] = np.zeros((B, H, capacity, d // v_group_channels, 2), np.uint16)
         seg["kgroup_start"] = np.zeros(kgroup_capacity + 1, np.int32)
+        if r:
+            seg["comp_basis"] = np.ascontiguousarray(comp_basis, np.float32)
+            seg["k_comp"] = np.zeros((B, H, capacity, 8), np.uint16)
     return seg
 
 
@@ -181,7 +196,8 @@ def append(seg: Dict, k_src: np.ndarray, v_src: np.ndarray, n_new: Optional[int]
                          _ptr(seg.get("k_meta")), _ptr(seg.get("v_meta")),
                          _ptr(seg.get("kgroup_start")), _ptr(seg.get("k_raw")),
                          _ptr(seg.get("v_raw")), _ptr(k_src), _ptr(v_src), src_tokens, n_new,
-                         _ptr(g), n_groups_in)
+                         _ptr(g), n_groups_in, seg.get("kgc", 0), seg.get("comp_rank", 0),
+                         _ptr(seg.get("comp_basis")), _ptr(seg.get("k_comp")))
     if r < 0:
         raise ValueError("oracle append rejected the request")
     seg["n_tokens"] += n_new
@@ -196,7 +212,8 @@ def _orc_seg(seg: Dict) -> OrcSegment:
                       _ptr(seg.get("k_codes")), _ptr(seg.get("v_codes")),
                       _ptr(seg.get("k_meta")), _ptr(seg.get("v_meta")),
                       _ptr(seg.get("kgroup_start")), _ptr(seg.get("k_raw")),
-                      _ptr(seg.get("v_raw")))
+                      _ptr(seg.get("v_raw")), seg.get("kgc", 0), seg.get("comp_rank", 0),
+                      _ptr(seg.get("comp_basis")), _ptr(seg.get("k_comp")))
 
 
 # -------------------------------------------------------------------- attention
@@ -235,7 +252,7 @@ def attention(q: np.ndarray, segs: List[Dict], k_cur: Optional[np.ndarray] = Non
 
 
 def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, tok_group: np.ndarray,
-               step_sq: np.ndarray, scale: float, jensen: int):
+               step_sq: np.ndarray, scale: float, jensen: int, logit_add: Optional[np.ndarray] = None):
     """One query over a dense key/value list (real-valued keys, e.g. keys plus sampled
     rounding noise); jensen as in attention(). Returns (out [d], lse, mass on grouped
     tokens)."""
@@ -244,8 +261,9 @@ def attend_row(q: np.ndarray, K: np.ndarray, V: np.ndarray, tok_group: np.ndarra
     d = q.size
     out = np.zeros(d, np.float64)
     lse, mass = F64(), F64()
+    la = None if logit_add is None else _c(logit_add, np.float64)
     lib().orc_attend_row(_ptr(q), d, _ptr(K), _ptr(V), _ptr(tg), K.shape[0], _ptr(ssq),
-                         ssq.shape[0] if ssq.ndim == 2 else 0, float(scale), int(jensen),
+                         ssq.shape[0] if ssq.ndim == 2 else 0, float(scale), int(jensen), _ptr(la),
                          _ptr(out), ctypes.byref(lse), ctypes.byref(mass))
     return out, lse.value, mass.value
 
@@ -291,3 +309,7 @@ def window_groups(bits: np.ndarray, order: np.ndarray, n_tokens: int, window: in
 def log_sinhc(a: float) -> float:
     """log(sinh(a) / a), a >= 0 (0 at a = 0)."""
     return lib().orc_log_sinhc(float(a))
+
+
+def f64_to_bf16_bits(x: float) -> int:
+    return lib().orc_f64_to_bf16(float(x))

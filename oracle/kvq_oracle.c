@@ -100,6 +100,28 @@ uint16_t orc_f32_to_bf16(float x)
     return (uint16_t)(u >> 16);
 }
 
+/* value -> nearest bfloat16, ties to even (x exactly representable as a double): 8
+ * significant bits, float's exponent range; below 2^-126 in units of 2^-133. */
+uint16_t orc_f64_to_bf16(double x)
+{
+    if (isnan(x))
+        return 0x7fc0;
+    uint16_t sign = signbit(x) ? 0x8000 : 0;
+    double a = fabs(x);
+    if (a >= ldexp(255.0 / 128.0 + 1.0 / 256.0, 127)) /* half-way past the largest bf16: to infinity */
+        return sign | 0x7f80;
+    if (a < ldexp(1.0, -126)) {
+        double q = nearbyint(ldexp(a, 133));
+        return sign | (uint16_t)q;
+    }
+    int E;
+    frexp(a, &E);
+    int e = E - 1;                                     /* a in [2^e, 2^(e+1)) */
+    double q = nearbyint(ldexp(a, 7 - e));             /* in [128, 256] */
+    uint32_t bits = (uint32_t)((e + 127) << 7) + (uint32_t)q - 128u;
+    return sign | (uint16_t)bits;
+}
+
 /* Round a float to an element dtype and return the rounded value as a double. */
 static double round_elem(float y, int elem_dtype)
 {
@@ -202,7 +224,8 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
                uint32_t *k_codes, uint32_t *v_codes, uint16_t *k_meta, uint16_t *v_meta,
                int32_t *kgroup_start, uint16_t *k_raw, uint16_t *v_raw,
                const float *k_src, const float *v_src, int64_t src_tokens, int n_new,
-               const int32_t *groups, int n_groups_in)
+               const int32_t *groups, int n_groups_in,
+               int kgc, int comp_rank, const float *comp_basis, uint16_t *k_comp)
 {
     int n_groups;
     if (groups) {
@@ -223,7 +246,9 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
     }
     if (n_tokens + n_new > cap)
         return -1;
-    if (bits != 16 && n_kgroups + n_groups > kgroup_cap)
+    if (bits != 16 && kgc == 0 && n_kgroups + n_groups > kgroup_cap)
+        return -1;
+    if (kgc < 0 || (kgc > 0 && d % kgc != 0) || (kgc > 0 && comp_rank > 0) || comp_rank < 0 || comp_rank > 8)
         return -1;
 
     /* source token of the i-th appended token, and its K-group */
@@ -259,21 +284,53 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
                 continue;
             }
             uint8_t *codes = (uint8_t *)malloc((size_t)(n_new > 0 ? n_new : 1) * d);
-            /* K: per (K-group, channel) over the group's tokens */
-            for (int g = 0; g < n_groups; ++g) {
-                float *col = (float *)malloc(sizeof(float) * (size_t)glen[g]);
-                for (int c = 0; c < d; ++c) {
-                    for (int t = 0; t < glen[g]; ++t)
-                        col[t] = ks[(size_t)src_of[gstart[g] + t] * d + c];
-                    uint16_t *m = k_meta + ((bh * kgroup_cap + (size_t)(n_kgroups + g)) * d + c) * 2;
-                    orc_quantize_group(col, glen[g], 1, bits, &m[0], &m[1],
-                                       codes + (size_t)gstart[g] * d + c, d);
+            if (kgc > 0) {
+                /* K: per (token, run of kgc channels), as V */
+                for (int i = 0; i < n_new; ++i)
+                    for (int gk = 0; gk < d / kgc; ++gk) {
+                        uint16_t *m = k_meta + ((bh * cap + (size_t)(n_tokens + i)) * (d / kgc) + gk) * 2;
+                        orc_quantize_group(ks + (size_t)src_of[i] * d + (size_t)gk * kgc, kgc, 1, bits,
+                                           &m[0], &m[1], codes + (size_t)i * d + (size_t)gk * kgc, 1);
+                    }
+            } else {
+                /* K: per (K-group, channel) over the group's tokens */
+                for (int g = 0; g < n_groups; ++g) {
+                    float *col = (float *)malloc(sizeof(float) * (size_t)glen[g]);
+                    for (int c = 0; c < d; ++c) {
+                        for (int t = 0; t < glen[g]; ++t)
+                            col[t] = ks[(size_t)src_of[gstart[g] + t] * d + c];
+                        uint16_t *m = k_meta + ((bh * kgroup_cap + (size_t)(n_kgroups + g)) * d + c) * 2;
+                        orc_quantize_group(col, glen[g], 1, bits, &m[0], &m[1],
+                                           codes + (size_t)gstart[g] * d + c, d);
+                    }
+                    free(col);
                 }
-                free(col);
             }
             for (int i = 0; i < n_new; ++i)
                 orc_pack_row(codes + (size_t)i * d, d, bits,
                              k_codes + (bh * cap + (size_t)(n_tokens + i)) * wpr);
+            /* compensation: the key's rounding error (source minus dequantized key, exact)
+             * projected on the basis of head h, rounded once to bf16 */
+            if (comp_rank > 0) {
+                const float *U = comp_basis + (size_t)h * d * comp_rank;
+                for (int i = 0; i < n_new; ++i) {
+                    int gi = 0; /* K-group of appended token i */
+                    while (gi + 1 < n_groups && gstart[gi + 1] <= i)
+                        ++gi;
+                    for (int j = 0; j < comp_rank; ++j) {
+                        double acc = 0.0;
+                        for (int c = 0; c < d; ++c) {
+                            const uint16_t *m = k_meta + ((bh * kgroup_cap + (size_t)(n_kgroups + gi)) * d + c) * 2;
+                            const double x = ks[(size_t)src_of[i] * d + c];
+                            const double xh = orc_dequant(codes[(size_t)i * d + c], m[0], m[1], elem_dtype, 0);
+                            acc += (double)U[(size_t)c * comp_rank + j] * (x - xh);
+                        }
+                        k_comp[(bh * cap + (size_t)(n_tokens + i)) * 8 + j] = orc_f64_to_bf16(acc);
+                    }
+                    for (int j = comp_rank; j < 8; ++j)
+                        k_comp[(bh * cap + (size_t)(n_tokens + i)) * 8 + j] = 0;
+                }
+            }
             /* V: per (token, run of Gv channels) */
             for (int i = 0; i < n_new; ++i) {
                 for (int gv = 0; gv < d / Gv; ++gv) {
@@ -286,7 +343,7 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
             }
             free(codes);
         }
-    if (bits != 16 && kgroup_start) {
+    if (bits != 16 && kgc == 0 && kgroup_start) {
         for (int g = 0; g < n_groups; ++g)
             kgroup_start[n_kgroups + g] = n_tokens + gstart[g];
         kgroup_start[n_kgroups + n_groups] = n_tokens + n_new;
@@ -294,13 +351,15 @@ int orc_append(int bits, int elem_dtype, int B, int H, int d, int cap, int n_tok
     free(src_of);
     free(gstart);
     free(glen);
-    return n_groups;
+    return kgc > 0 ? 0 : n_groups;
 }
 
 /* ------------------------------------------------------------------------ */
 /* Attention of one query row over a dense key/value list (A2, A3).
- *   s_j = scale * q . k_j - beta(q, group(j))        token j in a quantized K-group
- *   s_j = scale * q . k_j                            raw token (group < 0)
+ *   s_j = scale * (q . k_j + add_j) - beta(q, group(j))   token j in a quantized K-group
+ *   s_j = scale * (q . k_j + add_j)                      raw token (group < 0)
+ * (add_j = logit_add[j], 0 when logit_add is NULL: the compensation term of a segment
+ * that stores one)
  *   beta(q, g) = scale^2 / 24 * sum_c q_c^2 * step_{g,c}^2    (jensen == 1)
  *   beta(q, g) = scale^2 / 24 * |q|^2 * mean_c step_{g,c}^2   (jensen == 2)
  *   beta(q, g) = sum_c log(sinh(a_c) / a_c), a_c = scale |q_c| step_{g,c} / 2  (jensen == 3)
@@ -331,7 +390,8 @@ double orc_log_sinhc(double a)
 
 void orc_attend_row(const double *q, int d, const double *K, const double *V,
                     const int32_t *tok_group, int64_t N, const double *step_sq, int n_groups,
-                    double scale, int jensen, double *out, double *lse, double *mass)
+                    double scale, int jensen, const double *logit_add, double *out, double *lse,
+                    double *mass)
 {
     double *s = (double *)malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
     double *beta = (double *)malloc(sizeof(double) * (size_t)(n_groups > 0 ? n_groups : 1));
@@ -358,6 +418,8 @@ void orc_attend_row(const double *q, int d, const double *K, const double *V,
         double dot = 0.0;
         for (int c = 0; c < d; ++c)
             dot += q[c] * K[(size_t)j * d + c];
+        if (logit_add)
+            dot += logit_add[j];
         s[j] = scale * dot - (tok_group[j] >= 0 ? beta[tok_group[j]] : 0.0);
         if (s[j] > m) m = s[j];
     }
@@ -387,6 +449,9 @@ typedef struct orc_segment {
     const uint16_t *k_meta, *v_meta;
     const int32_t *kgroup_start;
     const uint16_t *k_raw, *v_raw;
+    int32_t k_group_channels, comp_rank;
+    const float *comp_basis;    /* [H][d][comp_rank] */
+    const uint16_t *k_comp;     /* bf16 bits [B][H][cap][8], the first comp_rank used */
 } orc_segment;
 
 /* Chunk attention: queries q [B][Hq][nq][d] (float values of the query dtype), the
@@ -406,11 +471,13 @@ int orc_attention(const float *q, int B, int Hq, int Hkv, int d, int nq,
     if (!rows)
         n_rows = nq;
     int64_t N = n_cur;
-    int G = 0;
+    int G = 0, any_comp = 0;
     for (int s = 0; s < n_segs; ++s) {
         N += segs[s].n_tokens;
         if (segs[s].bits != 16)
-            G += segs[s].n_kgroups;
+            G += segs[s].k_group_channels > 0 ? segs[s].n_tokens : segs[s].n_kgroups;
+        if (segs[s].bits != 16 && segs[s].comp_rank > 0)
+            any_comp = 1;
     }
     const int gqa = Hq / Hkv;
     for (int b = 0; b < B; ++b)
@@ -438,6 +505,27 @@ int orc_attention(const float *q, int B, int Hq, int Hkv, int d, int nq,
                 }
                 const int wpr = d * sg->bits / 32, Gv = sg->v_group_channels;
                 uint8_t *kc = (uint8_t *)malloc((size_t)d), *vc = (uint8_t *)malloc((size_t)d);
+                if (sg->k_group_channels > 0) {
+                    /* per-token K groups: every token is its own group of step sizes */
+                    const int kgc = sg->k_group_channels;
+                    for (int t = 0; t < sg->n_tokens; ++t, ++j) {
+                        orc_unpack_row(sg->k_codes + (row0 + t) * wpr, d, sg->bits, kc);
+                        orc_unpack_row(sg->v_codes + (row0 + t) * wpr, d, sg->bits, vc);
+                        for (int c = 0; c < d; ++c) {
+                            const uint16_t *km = sg->k_meta + ((row0 + t) * (d / kgc) + c / kgc) * 2;
+                            const uint16_t *vm = sg->v_meta + ((row0 + t) * (d / Gv) + c / Gv) * 2;
+                            double st = orc_f16_to_f64(km[0]);
+                            ssq[(size_t)(gbase + t) * d + c] = st * st;
+                            K[j * d + c] = orc_dequant(kc[c], km[0], km[1], sg->elem_dtype, exact);
+                            V[j * d + c] = orc_dequant(vc[c], vm[0], vm[1], sg->elem_dtype, exact);
+                        }
+                        tg[j] = gbase + t;
+                    }
+                    free(kc);
+                    free(vc);
+                    gbase += sg->n_tokens;
+                    continue;
+                }
                 for (int g = 0; g < sg->n_kgroups; ++g) {
                     const uint16_t *km = sg->k_meta + (bh * sg->kgroup_capacity + (size_t)g) * d * 2;
                     for (int c = 0; c < d; ++c) {
@@ -475,9 +563,37 @@ int orc_attention(const float *q, int B, int Hq, int Hkv, int d, int nq,
                     const float *qr = q + (((size_t)b * Hq + hq) * nq + i) * d;
                     for (int c = 0; c < d; ++c)
                         qd[c] = qr[c];
+                    /* compensation: (U_h^T q) . c_t for the tokens of segments that store c */
+                    double *add = NULL;
+                    if (any_comp) {
+                        add = (double *)calloc((size_t)(j > 0 ? j : 1), sizeof(double));
+                        int64_t t0 = 0;
+                        for (int s = 0; s < n_segs; ++s) {
+                            const orc_segment *sg = &segs[s];
+                            if (sg->bits != 16 && sg->comp_rank > 0) {
+                                const int r_ = sg->comp_rank;
+                                const float *U = sg->comp_basis + (size_t)h * d * r_;
+                                double uq[8];
+                                for (int jj = 0; jj < r_; ++jj) {
+                                    uq[jj] = 0.0;
+                                    for (int c = 0; c < d; ++c)
+                                        uq[jj] += (double)U[(size_t)c * r_ + jj] * qd[c];
+                                }
+                                for (int t = 0; t < sg->n_tokens; ++t) {
+                                    const uint16_t *ct = sg->k_comp + (bh * (size_t)sg->capacity + t) * 8;
+                                    double acc = 0.0;
+                                    for (int jj = 0; jj < r_; ++jj)
+                                        acc += uq[jj] * (double)orc_bf16_to_f32(ct[jj]);
+                                    add[t0 + t] = acc;
+                                }
+                            }
+                            t0 += sg->n_tokens;
+                        }
+                    }
                     const size_t o = ((size_t)b * Hq + hq) * n_rows + ri;
-                    orc_attend_row(qd, d, K, V, tg, j, ssq, gbase, scale, jensen, out + o * d,
+                    orc_attend_row(qd, d, K, V, tg, j, ssq, gbase, scale, jensen, add, out + o * d,
                                    lse ? lse + o : NULL, mass ? mass + o : NULL);
+                    free(add);
                 }
             free(K);
             free(V);

@@ -14,10 +14,14 @@ def f32(t: torch.Tensor) -> np.ndarray:
     return t.float().numpy()
 
 
-def make_pair(bits, elem, B, H, d, capacity, Gk, kgroup_capacity):
-    g = kvq.Segment(bits, TORCH_DT[elem], B, H, d, capacity, k_group_tokens=Gk, kgroup_capacity=kgroup_capacity)
+def make_pair(bits, elem, B, H, d, capacity, Gk, kgroup_capacity, k_group_channels=0, comp_basis=None):
+    """comp_basis: numpy float32 [H][d][r] (the low-rank compensation's basis)."""
+    gb = None if comp_basis is None else torch.from_numpy(np.ascontiguousarray(comp_basis, np.float32)).cuda()
+    g = kvq.Segment(bits, TORCH_DT[elem], B, H, d, capacity, k_group_tokens=Gk, kgroup_capacity=kgroup_capacity,
+                    k_group_channels=k_group_channels, comp_basis=gb)
     o = oracle.new_segment(bits, elem, B, H, d, capacity=capacity, k_group_tokens=Gk,
-                           kgroup_capacity=kgroup_capacity)
+                           kgroup_capacity=kgroup_capacity, k_group_channels=k_group_channels,
+                           comp_basis=comp_basis)
     return g, o
 
 
@@ -46,6 +50,8 @@ def host_view(gseg):
         out["k_meta"] = gseg.k_meta.cpu().numpy().view(np.uint16)
         out["v_meta"] = gseg.v_meta.cpu().numpy().view(np.uint16)
         out["kgroup_start"] = gseg.kgroup_start.cpu().numpy()
+        if gseg.k_comp is not None:
+            out["k_comp"] = gseg.k_comp.cpu().numpy().view(np.uint16)
     return out
 
 
@@ -59,8 +65,21 @@ def assert_segments_equal(gseg, oseg):
         return
     G = oseg["n_kgroups"]
     assert h["n_kgroups"] == G
-    assert np.array_equal(h["kgroup_start"][:G + 1], oseg["kgroup_start"][:G + 1])
-    for name, sl in (("k_codes", np.s_[:, :, :n]), ("v_codes", np.s_[:, :, :n]), ("k_meta", np.s_[:, :, :G]),
+    token_groups = oseg.get("kgc", 0) > 0
+    if not token_groups:
+        assert np.array_equal(h["kgroup_start"][:G + 1], oseg["kgroup_start"][:G + 1])
+    if "k_comp" in h:
+        # the compensation is a float sum (fp32 on the device, double in the oracle) rounded
+        # to bf16: within one bf16 step of the oracle's plus the fp32 sum's own error (head_dim
+        # terms |U e| <= |e| <= a few units: below 2^-15 absolute), and mostly equal
+        a = h["k_comp"][:, :, :n].astype(np.uint32) << 16
+        b = oseg["k_comp"][:, :, :n].astype(np.uint32) << 16
+        fa, fb = a.view(np.float32).astype(np.float64), b.view(np.float32).astype(np.float64)
+        step = np.abs(fb) * 2.0 ** -7 + 2.0 ** -15
+        assert np.all(np.abs(fa - fb) <= step), np.abs(fa - fb).max()
+        assert (a == b).mean() >= 0.98, (a == b).mean()
+    for name, sl in (("k_codes", np.s_[:, :, :n]), ("v_codes", np.s_[:, :, :n]),
+                     ("k_meta", np.s_[:, :, :n] if token_groups else np.s_[:, :, :G]),
                      ("v_meta", np.s_[:, :, :n])):
         a, b = h[name][sl], oseg[name][sl]
         bad = np.argwhere(a != b)

@@ -31,7 +31,7 @@ def test_library_exports_every_declared_symbol():
     out = subprocess.run(["nm", "-D", "--defined-only", kvq.LIB_PATH], capture_output=True, text=True).stdout
     exported = set(re.findall(r" T (kvq_\w+)", out))
     assert set(_declared()) <= exported
-    assert L.kvq_abi_version() == 2
+    assert L.kvq_abi_version() == 3
 
 
 def test_header_compiles_as_c():

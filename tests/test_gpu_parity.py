@@ -296,3 +296,66 @@ def test_attention_with_fused_append(case):
     assert np.abs(lse.cpu().numpy() - ol).max() <= TOL
     oracle.append(oseg, f32(kc), f32(vc))
     assert_segments_equal(gseg, oseg)
+
+
+@pytest.mark.parametrize("bits,d,kgc,dtype", [(2, 128, 32, "bf16"), (4, 128, 128, "bf16"), (2, 64, 64, "f16"),
+                                              (2, 128, 64, "bf16")])
+@pytest.mark.parametrize("jensen", [0, 1, 2])
+def test_token_groups_attention(bits, d, kgc, dtype, jensen):
+    """Per-token K groups: codes and step/zero bit-exact; chunk attention (GQA, a current
+    chunk, a second plain segment) with the Jensen term carried by the extra K columns."""
+    B, Hq, Hkv, n1, n2, n_cur, n_q = 1, 4, 2, 700, 300, 90, 260
+    Gk = 128 if d == 128 else 32
+    tseg, toseg = make_pair(bits, dtype, B, Hkv, d, capacity=n1, Gk=Gk, kgroup_capacity=1, k_group_channels=kgc)
+    append_both(tseg, toseg, _rand((B, Hkv, n1, d), dtype, 71, 2.0), _rand((B, Hkv, n1, d), dtype, 72))
+    assert tseg.n_kgroups == 0
+    assert_segments_equal(tseg, toseg)
+    pseg, poseg = make_pair(bits, dtype, B, Hkv, d, capacity=n2, Gk=Gk, kgroup_capacity=-(-n2 // Gk))
+    append_both(pseg, poseg, _rand((B, Hkv, n2, d), dtype, 73, 2.0), _rand((B, Hkv, n2, d), dtype, 74))
+    q = _rand((B, Hq, n_q, d), dtype, 75)
+    kc = _rand((B, Hkv, n_cur, d), dtype, 76, 2.0)
+    vc = _rand((B, Hkv, n_cur, d), dtype, 77)
+    go, gl = gpu_attention(q, [tseg, pseg], kc, vc, n_kv_heads=Hkv, jensen=jensen)
+    oo, ol = oracle_attention(q, [toseg, poseg], kc, vc, n_kv_heads=Hkv, jensen=jensen)
+    assert np.abs(go - oo).max() <= TOL
+    assert np.abs(gl - ol).max() <= TOL
+
+
+def _basis(rng, H, d, r):
+    U = np.zeros((H, d, r), np.float32)
+    for h in range(H):
+        U[h] = np.linalg.qr(rng.standard_normal((d, r)))[0].astype(np.float32)
+    return U
+
+
+@pytest.mark.parametrize("bits,d,r,dtype", [(2, 128, 8, "bf16"), (4, 64, 4, "f16"), (2, 64, 3, "bf16")])
+@pytest.mark.parametrize("jensen", [0, 1])
+def test_compensation_attention(bits, d, r, dtype, jensen):
+    """The low-rank compensation: stored c within one bf16 step of the oracle's; attention
+    (queries half inside span(U), a current chunk, a fused append into the segment) against
+    the oracle."""
+    B, Hq, Hkv, n, n_cur, n_q = 1, 4, 2, 900, 120, 300
+    Gk = 128 if d == 128 else 32
+    rng = np.random.default_rng(81 + r)
+    U = _basis(rng, Hkv, d, r)
+    gseg, oseg = make_pair(bits, dtype, B, Hkv, d, capacity=n + n_cur, Gk=Gk,
+                           kgroup_capacity=-(-n // Gk) + -(-n_cur // Gk), comp_basis=U)
+    append_both(gseg, oseg, _rand((B, Hkv, n, d), dtype, 82, 2.0), _rand((B, Hkv, n, d), dtype, 83))
+    assert_segments_equal(gseg, oseg)
+    q = _rand((B, Hq, n_q, d), dtype, 84).float().numpy()
+    # half of every query inside the subspace of its KV head
+    for hq in range(Hq):
+        Uh = U[hq * Hkv // Hq].astype(np.float64)
+        q[0, hq] = (0.5 * q[0, hq] + 2.0 * (q[0, hq] @ Uh) @ Uh.T).astype(np.float32)
+    q = torch.from_numpy(q).to(TORCH_DT[dtype])
+    kc = _rand((B, Hkv, n_cur, d), dtype, 85, 2.0)
+    vc = _rand((B, Hkv, n_cur, d), dtype, 86)
+    oo, ol = oracle_attention(q, [oseg], kc, vc, n_kv_heads=Hkv, jensen=jensen)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    out = kvq.chunk_attention(q.cuda(), [gseg], kc.cuda(), vc.cuda(), n_kv_heads=Hkv, jensen=jensen, lse=lse,
+                              append_to=gseg)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy() - oo).max() <= TOL
+    assert np.abs(lse.cpu().numpy() - ol).max() <= TOL
+    oracle.append(oseg, f32(kc), f32(vc))
+    assert_segments_equal(gseg, oseg)
