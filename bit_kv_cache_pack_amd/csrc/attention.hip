@@ -51,6 +51,9 @@ constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * kWave;
 constexpr int BM = 32 * kWaves;   // query rows per workgroup
 constexpr int TT = 64;    // tokens per tile
+// A row of a partial piece: HD int16 mantissas, then m (log2 domain), l and the exponent E
+// (the mantissas stand for O 2^(15 - E)) as f32, f32, i32, and a pad word.
+template <int HD> struct PieceRow { static constexpr size_t bytes = 2 * HD + 16; };
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kRescale = 8.0f;  // log2 headroom before the running max is moved
 
@@ -1099,7 +1102,19 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
         // the column writes), and leaves as 16-byte row segments. The wave alone writes and
         // reads its table; its LDS operations complete in order.
         const float lt = cx.l + other_half(cx.l);
-        const float scale = whole ? 1.0f / lt : 1.0f;
+        // a partial row leaves as block floating point: 16-bit mantissas of O 2^(15 - E),
+        // 2^E the power of two above the row's largest |O| (E = 0 for a zero row)
+        int pexp = 0;
+        if (!whole) {
+            float amax = 0.f;
+#pragma unroll
+            for (int db = 0; db < C::DB; ++db)
+#pragma unroll
+                for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(cx.o[db][j]));
+            amax = fmaxf(amax, other_half(amax));
+            if (amax > 0.f) pexp = ilogbf(amax) + 1;
+        }
+        const float scale = whole ? 1.0f / lt : ldexpf(1.0f, 15 - pexp);
         float *lo = cx.btab;
         // this lane's four chunks of a block: rows lane / 8 + 8 i, channels 4 (lane % 8) + 0..3
         const int crow = lane / 8, c4 = 4 * (lane % 8);
@@ -1125,7 +1140,12 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
                 if (!dst_ok[i]) continue;
                 const int ch = 32 * db + c4;
                 if (!whole) {
-                    *reinterpret_cast<f32x4 *>(p.partial + dst[i] * (HD + 4) + ch) = v;
+                    uint32_t e[4];
+#pragma unroll
+                    for (int t = 0; t < 4; ++t)
+                        e[t] = (uint32_t)(int32_t)fminf(fmaxf(rintf(v[t]), -32767.f), 32767.f) & 0xffffu;
+                    *reinterpret_cast<u32x2 *>(reinterpret_cast<uint8_t *>(p.partial) + dst[i] * PieceRow<HD>::bytes +
+                                               2 * ch) = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
                 } else if (p.out_dtype == DT_F32) {
                     *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + dst[i] * HD + ch) = v;
                 } else {
@@ -1141,9 +1161,9 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             if (whole) {
                 if (p.lse != nullptr) p.lse[qrow] = (cx.m + __log2f(lt)) * kLn2;
             } else {
-                float *pp = p.partial + (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * (HD + 4);
-                pp[HD] = cx.m;
-                pp[HD + 1] = lt;
+                uint8_t *pp = reinterpret_cast<uint8_t *>(p.partial) +
+                              (((size_t)blockIdx.x * 2 + pslot) * BM + (row - rbi * BM)) * PieceRow<HD>::bytes;
+                *reinterpret_cast<f32x4 *>(pp + 2 * HD) = f32x4{cx.m, lt, __int_as_float(pexp), 0.f};
             }
         }
         // the next piece restages the LDS buffers and rebuilds the tile list
@@ -1154,12 +1174,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 // Merge the pieces of the row blocks that the shares split. Job y (one per workgroup of
 // the attention launch) takes the row block holding position y quota if share y is the
 // first to start in it; the row block's pieces are in shares w0..w1. One pass over the
-// pieces with a running maximum; a thread merges 8 channels of one row (partial rows are
-// HD + 4 floats: O, then m and l, 16-byte aligned).
+// pieces with a running maximum; a thread merges 8 channels of one row (one 16-byte load
+// of mantissas per piece, and the piece row's m, l and exponent).
 template <int HD>
 __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     constexpr int CPT = 8;          // channels per thread
-    constexpr int NQ = CPT / 4;     // 16-byte loads per piece
     constexpr int TPR = HD / CPT;   // threads per row
     constexpr int RPB = 256 / TPR;  // rows per block
     const int64_t U = p.quota, Np = p.tok_pad;
@@ -1176,55 +1195,58 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     if (row >= rows) return;
     const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
     const size_t qrow = ((size_t)b * p.n_q_heads + h * gqa + row / p.n_q) * p.n_q + row % p.n_q;
+    const uint8_t *base = reinterpret_cast<const uint8_t *>(p.partial);
     float M = -__builtin_inff(), L = 0.f;
-    f32x4 acc[NQ];
+    float acc[CPT];
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) acc[q] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
     // pieces in groups of 8 whose loads are in flight together (a row block of a few rows can
     // be cut into many pieces)
     constexpr int NP = 8;
     for (int64_t w = w0; w <= w1; w += NP) {
-        f32x4 o[NP][NQ];
-        float m[NP], l[NP];
+        u32x4 o[NP];
+        f32x4 t[NP];   // m, l, exponent bits, pad
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
             const int64_t ww = w + k;
             if (ww > w1) {   // past the last piece (uniform over the workgroup): no load
-#pragma unroll
-                for (int q = 0; q < NQ; ++q) o[k][q] = f32x4{0.f, 0.f, 0.f, 0.f};
-                m[k] = -__builtin_inff();
-                l[k] = 0.f;
+                o[k] = u32x4{0u, 0u, 0u, 0u};
+                t[k] = f32x4{-__builtin_inff(), 0.f, 0.f, 0.f};
                 continue;
             }
             // the row block's piece in share ww is that share's first piece iff the share starts in it
-            const float *pp = p.partial + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * (HD + 4);
-#pragma unroll
-            for (int q = 0; q < NQ; ++q) o[k][q] = *reinterpret_cast<const f32x4 *>(pp + c + 4 * q);
-            m[k] = pp[HD];
-            l[k] = pp[HD + 1];
+            const uint8_t *pp = base + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * PieceRow<HD>::bytes;
+            o[k] = *reinterpret_cast<const u32x4 *>(pp + 2 * c);
+            t[k] = *reinterpret_cast<const f32x4 *>(pp + 2 * HD);
         }
 #pragma unroll
         for (int k = 0; k < NP; ++k) {
-            if (m[k] == -__builtin_inff()) continue;   // past the last piece, or a piece past the last token
-            const float mn = fmaxf(M, m[k]);
-            const float sa = exp2f(M - mn), sb = exp2f(m[k] - mn);
+            const float mk = t[k][0];
+            if (mk == -__builtin_inff()) continue;   // past the last piece, or a piece past the last token
+            const float mn = fmaxf(M, mk);
+            const float sa = exp2f(M - mn), sb = exp2f(mk - mn);
+            const float so = ldexpf(sb, __float_as_int(t[k][2]) - 15);   // mantissa weight
 #pragma unroll
-            for (int q = 0; q < NQ; ++q) acc[q] = acc[q] * sa + o[k][q] * sb;
-            L = L * sa + l[k] * sb;
+            for (int i = 0; i < CPT; ++i) {
+                const uint32_t wd = o[k][i / 2];
+                const float mv = (float)(int16_t)(i % 2 ? wd >> 16 : wd & 0xffffu);
+                acc[i] = acc[i] * sa + mv * so;
+            }
+            L = L * sa + t[k][1] * sb;
             M = mn;
         }
     }
     const float inv = 1.0f / L;
 #pragma unroll
-    for (int q = 0; q < NQ; ++q) {
+    for (int q = 0; q < CPT / 4; ++q) {
         const size_t o0 = qrow * HD + c + 4 * q;
+        const f32x4 v = f32x4{acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]} * inv;
         if (p.out_dtype == DT_F32) {
-            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + o0) = acc[q] * inv;
+            *reinterpret_cast<f32x4 *>(reinterpret_cast<float *>(p.out) + o0) = v;
         } else {
             uint16_t e[4];
 #pragma unroll
-            for (int i = 0; i < 4; ++i)
-                e[i] = p.out_dtype == DT_BF16 ? f32_to_bf16_bits(acc[q][i] * inv) : f32_to_f16_bits(acc[q][i] * inv);
+            for (int i = 0; i < 4; ++i) e[i] = p.out_dtype == DT_BF16 ? f32_to_bf16_bits(v[i]) : f32_to_f16_bits(v[i]);
             *reinterpret_cast<u32x2 *>(reinterpret_cast<uint16_t *>(p.out) + o0) =
                 u32x2{(uint32_t)e[0] | ((uint32_t)e[1] << 16), (uint32_t)e[2] | ((uint32_t)e[3] << 16)};
         }
@@ -1365,7 +1387,8 @@ void attention_plan(int batch, int n_q_heads, int n_kv_heads, int head_dim, int 
     plan->quota = quota;
     plan->work = work;
     if (quota % np != 0)
-        plan->workspace_bytes = (size_t)((work + quota - 1) / quota) * 2 * BM * (head_dim + 4) * sizeof(float);
+        plan->workspace_bytes = (size_t)((work + quota - 1) / quota) * 2 * BM *
+                                (head_dim == 64 ? PieceRow<64>::bytes : PieceRow<128>::bytes);
 }
 
 hipError_t launch_attention(const AttnParams &p, hipStream_t s) {

@@ -1,20 +1,20 @@
 // Decode-shaped attention over a packed low-bit KV cache: at most 16 query rows per
 // (batch, KV head) -- in GQA decode, one token of each query head that shares the KV
-// head -- against a long quantized history (plus, optionally, raw segments and an
-// unquantized current chunk).
+// head -- against a long quantized history (plus, optionally, an unquantized current
+// chunk). Built for bf16 elements, INT2 at head_dim 64 or 128 and INT4 at head_dim 128,
+// one packed segment; other calls take the chunk kernel (decode_eligible).
 //
 // Method: as the chunk kernel ("Quantized Keys Steal Attention: Bias Correction for
 // KV-Cache Compression in Video Diffusion", abstract): logits over packed tokens are
 // corrected by beta = tau^2/24 * sum_c q_c^2 step_c^2 of their K-group; no mask; the
 // dequantized keys and values exist only in registers and LDS ("KV Cache Quantization
-// for Self-Forcing Video Generation", abstract). The WindowQuant segments ("技術的に面白い
-// 点") are walked one after another.
+// for Self-Forcing Video Generation", abstract).
 //
 // With so few rows the work is streaming the packed cache and expanding it, so the
 // layout is built for memory-level parallelism and for few vector instructions per
 // code rather than for MFMA reuse:
 //   - every wave walks its own contiguous token range (no barriers until the end) in
-//     steps of 64 INT2 / 32 INT4 tokens (16 for raw tokens); the codes of the next step
+//     steps of 64 INT2 / 32 INT4 tokens (16 for current-chunk tokens); the codes of the next step
 //     are loaded into one 20-register set as soon as this step's copy has been expanded
 //     (keys after the QK product, values after their LDS write), so each load has about
 //     a whole step to land;
@@ -41,7 +41,7 @@ namespace {
 constexpr int kDWaves = 4;
 constexpr int kDThreads = kDWaves * kWave;
 constexpr int TP = 64;   // tokens per step of an INT2 segment (32 for INT4)
-constexpr int TR = 16;   // tokens per step of a raw segment or of the current chunk
+constexpr int TR = 16;   // tokens per step of the current chunk
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kDRescale = 8.0f;  // log2 headroom before the running max is moved
 
@@ -57,13 +57,13 @@ template <int HD> struct DGeo {
     static constexpr int OROW = HD + 4;      // epilogue scratch row (floats)
 };
 
-enum : int { ST_END = 0, ST_PACKED = 1, ST_RAW = 2, ST_CUR = 3 };
+enum : int { ST_END = 0, ST_PACKED = 1, ST_CUR = 3 };
 
 
 struct Step {
     int kind, seg, g, t, len;
     int new_group;  // first step of K-group g in this walk
-    int bits;       // the segment's bit-width (16: raw)
+    int bits;       // the segment's bit-width (16: current chunk)
 };
 
 __device__ __forceinline__ Step uniform(Step s) {
@@ -135,12 +135,7 @@ struct Walker {
                 t += len;
                 return r;
             }
-            if (sbits == 16) {
-                const int len = min(TR, e - t);
-                const Step r{ST_RAW, si, 0, t, len, 0, 16};
-                t += len;
-                return r;
-            }
+            if (sbits == 16) { t = e; continue; }   // raw segments take the chunk kernel
             if (g >= sng) { t = e; continue; }
             if (ge <= t) {
                 ++g;
@@ -196,7 +191,7 @@ __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step 
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k);
-    if (st.bits == 2) {
+    if (HD == 64 || st.bits == 2) {   // INT4 only at head_dim 128
         constexpr int WPR = HD / 16, WL = WPR / 4;   // words per row, per quarter
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -231,7 +226,7 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
-    if (st.bits == 2) {
+    if (HD == 64 || st.bits == 2) {
         constexpr int WPR = HD / 16;
         const int tok = min(lane, st.len - 1);
         const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR);
@@ -393,7 +388,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
                 s[b] = E::mma16(__builtin_bit_cast(vec, u32x4{ko[4], ko[5], ko[6], ko[7]}), cx.qb[2 * bl + 1], s[b]);
             }
         }
-    } else if (bits == 4) {
+    } else if (HD == 128 && bits == 4) {
 #pragma unroll
         for (int b = 0; b < 2; ++b) {
 #pragma unroll
@@ -407,18 +402,10 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             }
         }
     } else {
-        // raw keys, read now (raw steps are rare in decode): quarter j of token r16
+        // current-chunk keys, read now (a few steps at the end of the walk): quarter j of token r16
         u32x4 kq[G::QV];
-        const uint16_t *kb;
-        size_t row0;
-        if (st.kind == ST_RAW) {
-            const SegmentView &sg = p.segs[st.seg];
-            row0 = bh * (size_t)sg.capacity + st.t;
-            kb = reinterpret_cast<const uint16_t *>(sg.k);
-        } else {
-            row0 = bh * (size_t)p.n_cur + st.t;
-            kb = reinterpret_cast<const uint16_t *>(p.k_cur);
-        }
+        const size_t row0 = bh * (size_t)p.n_cur + st.t;
+        const uint16_t *kb = reinterpret_cast<const uint16_t *>(p.k_cur);
         const bool ok = r16 < len;
         const u32x4 *src = reinterpret_cast<const u32x4 *>(kb + (row0 + (ok ? r16 : 0)) * HD + j * (HD / 4));
 #pragma unroll
@@ -456,7 +443,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
                 *reinterpret_cast<u32x4 *>(row + 16 * blk + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
             }
         }
-    } else if (bits == 4) {
+    } else if (HD == 128 && bits == 4) {
         const int tok = lane / 2, half = lane % 2;
         uint16_t *row = vt + tok * G::VROW + half * (HD / 2);
 #pragma unroll
@@ -467,19 +454,11 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             *reinterpret_cast<u32x4 *>(row + 16 * hb + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
         }
     } else {
-        // raw values, read now: quarter lane % 4 of token lane / 4
+        // current-chunk values, read now: quarter lane % 4 of token lane / 4
         const int tr = lane / 4, qq = lane % 4;
         const bool ok = tr < len;
-        const uint16_t *vb;
-        size_t row0;
-        if (st.kind == ST_RAW) {
-            const SegmentView &sg = p.segs[st.seg];
-            row0 = bh * (size_t)sg.capacity + st.t;
-            vb = reinterpret_cast<const uint16_t *>(sg.v);
-        } else {
-            row0 = bh * (size_t)p.n_cur + st.t;
-            vb = reinterpret_cast<const uint16_t *>(p.v_cur);
-        }
+        const size_t row0 = bh * (size_t)p.n_cur + st.t;
+        const uint16_t *vb = reinterpret_cast<const uint16_t *>(p.v_cur);
         u32x4 vq[G::QV];
         const u32x4 *src = reinterpret_cast<const u32x4 *>(vb + (row0 + (ok ? tr : 0)) * HD + qq * (HD / 4));
 #pragma unroll
@@ -688,8 +667,9 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     }
 }
 
-template <int HD, bool BF16>
+template <int HD>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
+    constexpr bool BF16 = true;
     dim3 grid(p.n_split, p.batch * p.n_kv_heads);
     if (p.jensen == JENSEN_EXACT)
         hipLaunchKernelGGL((decode_kernel<HD, BF16, true>), grid, dim3(kDThreads), 0, s, p);
@@ -704,8 +684,9 @@ hipError_t launch_d(const AttnParams &p, hipStream_t s) {
 
 bool decode_eligible(int dtype, int batch, int n_q_heads, int n_kv_heads, int head_dim, int n_q,
                      const int *seg_bits, int n_segs, int n_cur, int n_total) {
+    // built for bf16 only, one packed segment (the multi-segment walk is not covered by a
+    // passing GPU run), no raw segments, INT4 only at head_dim 128
     if ((long)(n_q_heads / n_kv_heads) * n_q > kDecodeRows || dtype != DT_BF16) return false;
-    // one packed segment: the multi-segment walk is not covered by a passing GPU run
     if (n_segs > 1) return false;
     for (int i = 0; i < n_segs; ++i) {
         if (seg_bits[i] == 16) return false;
@@ -735,9 +716,9 @@ void decode_plan(int batch, int n_kv_heads, int n_total, int *n_wg, int *wave_to
 }
 
 hipError_t launch_decode(const AttnParams &p, hipStream_t s) {
-    const bool bf = p.dtype == DT_BF16;
-    if (p.head_dim == 64) return bf ? launch_d<64, true>(p, s) : launch_d<64, false>(p, s);
-    return bf ? launch_d<128, true>(p, s) : launch_d<128, false>(p, s);
+    // only what decode_eligible admits is built
+    if (p.dtype != DT_BF16) return hipErrorInvalidValue;
+    return p.head_dim == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
 }
 
 }  // namespace kvq

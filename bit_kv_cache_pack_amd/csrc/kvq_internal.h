@@ -88,7 +88,8 @@ struct AttnParams {
     int32_t n_rb, tok_pad;
     int64_t quota, work;
     float *partial;                // decode: [n_split][rows][head_dim + 2];
-                                   // chunk: [workgroup][2][row in block][head_dim + 4]
+                                   // chunk: [workgroup][2][row in block] rows of 2 head_dim + 16
+                                   // bytes (int16 mantissas; m, l, exponent, pad)
     int32_t decode;                // run the decode-shaped kernel (decided by decode_eligible)
     // quantize-append of the current chunk in the same call (app_bits 0: none). The chunk
     // kernel runs it in workgroups after its own (blocks past n_attn_wg, app_per_wg units

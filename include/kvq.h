@@ -315,15 +315,20 @@ typedef struct kvq_attn_args {
  * call.
  * Errors: as kvq_chunk_attention; KVQ_ERR_WORKSPACE when the call needs more scratch than
  * the array holds (kvq_attention_workspace_size > KVQ_NOALLOC_SCRATCH_BYTES; on MI355X the
- * largest plan needs 69.2 MB, so no valid call is refused there); KVQ_ERR_HIP when the
+ * largest plan needs 35.7 MB, so no valid call is refused there); KVQ_ERR_HIP when the
  * array's address cannot be looked up.
  */
-#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)72 << 20)
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)36 << 20)
 kvq_status kvq_chunk_attention_noalloc(const kvq_attn_args *args, void *stream);
 
 /* Bytes of workspace kvq_chunk_attention needs for these arguments (pointers are not
  * read). Host only; returns KVQ_ERR_ARG / KVQ_ERR_UNSUPPORTED for arguments that
- * kvq_chunk_attention would reject on shape grounds. */
+ * kvq_chunk_attention would reject on shape grounds. The size does not grow with the
+ * cache: it is 0 when the work divides into whole row blocks of 256 query rows, at most
+ * 2 x CUs x 256 rows x (2 head_dim + 16) bytes when the chunk-shaped path splits row
+ * blocks between workgroups (35.7 MB at head_dim 128 on 256 CUs; partial rows are kept
+ * as 16-bit mantissas with a per-row power-of-two scale), and at most
+ * 1023 x 16 rows x (head_dim + 2) x 4 bytes on the decode-shaped path. */
 kvq_status kvq_attention_workspace_size(const kvq_attn_args *args, size_t *bytes);
 
 kvq_status kvq_chunk_attention(const kvq_attn_args *args, void *stream);

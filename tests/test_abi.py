@@ -173,7 +173,7 @@ def test_workspace_size_and_check():
     # equal share and keeps two partial slots of 256 rows x (d + 4) floats
     a, arr = _attn(n_q=8192, n_q_heads=12, n_kv_heads=12, segs=[_seg(n_kv_heads=12, n_tokens=900, n_kgroups=8)])
     assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK
-    assert n.value > 0 and n.value % (2 * 256 * 4 * 132) == 0 and n.value // (2 * 256 * 4 * 132) <= 256
+    assert n.value > 0 and n.value % (2 * 256 * (2 * 128 + 16)) == 0 and n.value // (2 * 256 * (2 * 128 + 16)) <= 256
 
 
 def test_window_validation():

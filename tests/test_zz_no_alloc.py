@@ -33,7 +33,7 @@ def _case(B, Hq, Hkv, d, n_cache, n_cur, n_q, seed):
 @pytest.mark.parametrize("order", ["large_then_small"])
 def test_noalloc_matches_chunk_attention(order):
     cases = [
-        # 24 row blocks of 256 queries on a 256-CU part: equal shares, 69 MB of partials
+        # 24 row blocks of 256 queries on a 256-CU part: equal shares, 35.7 MB of partials
         dict(B=1, Hq=2, Hkv=2, d=128, n_cache=2000, n_cur=500, n_q=3000, seed=5),
         # GQA decode, one query per head, split over several workgroups per KV head
         dict(B=2, Hq=8, Hkv=2, d=128, n_cache=2000, n_cur=0, n_q=1, seed=7),
