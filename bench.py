@@ -475,10 +475,13 @@ def measure_chunk(args, w: workloads.Workload, copies: int = 0):
 EXTRA_WORKLOADS = ("video_chunk_int2_h12_d128", "decode_gqa32x8_int2_32k", "decode_gqa32x8_int4_32k")
 
 
-def trace_summary(path: str, skip: int) -> None:
+def trace_summary(path: str, keep: int) -> None:
     """Per-kernel durations from a rocprofv3 kernel-trace CSV (``--kernel-trace
-    --output-format csv``): dispatch count, mean, median, min and max in microseconds, the
-    first ``skip`` dispatches of each kernel (the warm-ups) left out. Prints a markdown table."""
+    --output-format csv``) of a ``--no-extra --no-probe-hbm --no-cpu-baseline`` run: dispatch
+    count, mean, median, min and max in microseconds over each kernel's last ``keep``
+    dispatches. The selected append mode is timed last, so for the step's kernels these are
+    the timed steps (warm-ups, cache building and the other mode's steps come before).
+    Prints a markdown table."""
     import csv
     durs = {}
     with open(path) as f:
@@ -488,10 +491,10 @@ def trace_summary(path: str, skip: int) -> None:
             if "<" in name.split("(")[0]:
                 short += "<" + name.split("(")[0].split("<", 1)[1]
             durs.setdefault(short, []).append((int(row["End_Timestamp"]) - int(row["Start_Timestamp"])) / 1e3)
-    print("| kernel | dispatches (after %d skipped) | mean us | median us | min us | max us |" % skip)
+    print("| kernel | dispatches (last %d kept) | mean us | median us | min us | max us |" % keep)
     print("|---|---|---|---|---|---|")
-    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1])):
-        v = v[skip:] if len(v) > skip else v
+    for k, v in sorted(durs.items(), key=lambda kv: -sum(kv[1][-keep:])):
+        v = v[-keep:]
         print("| `%s` | %d | %.1f | %.1f | %.1f | %.1f |" % (k, len(v), np.mean(v), np.median(v), min(v), max(v)))
 
 
@@ -520,7 +523,7 @@ def main():
                     help="print per-kernel durations of a rocprofv3 kernel-trace CSV and exit (no GPU)")
     args = ap.parse_args()
     if args.trace_summary:
-        trace_summary(args.trace_summary, args.warmup)
+        trace_summary(args.trace_summary, args.steps)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
