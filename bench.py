@@ -48,9 +48,12 @@ def log(*a):
 class ChunkStep:
     """Attention of the current chunk over the packed cache + the chunk's quantize-append."""
 
-    def __init__(self, w: workloads.Workload, n_copies: int = 1, fused: bool = True):
+    def __init__(self, w: workloads.Workload, n_copies: int = 1, fused: bool = True, k_group_channels: int = 0,
+                 comp_rank: int = 0):
         self.w = w
         self.fused = fused   # the append in the attention's own call (append_dst) or after it
+        self.kgc = k_group_channels   # per-token K groups of this many channels (0: per channel)
+        self.comp_rank = comp_rank    # low-rank logit compensation of this rank (0: none)
         t0 = time.time()
         data = workloads.generate(w)
         log("generated inputs in %.1fs" % (time.time() - t0))
@@ -60,10 +63,17 @@ class ChunkStep:
         self.bits = w.bits
         n_groups = w.n_appends * -(-w.append_tokens // w.k_group_tokens)
         extra = -(-w.n_cur // w.k_group_tokens) if w.n_cur else 0
+        self.basis = None
+        if comp_rank:
+            # the caller's estimate of each KV head's dominant query subspace: the top right
+            # singular vectors of the query rows that read it (setup, not timed)
+            qh = data["q"].float().reshape(B, Hkv, Hq // Hkv, w.n_q, d).permute(1, 0, 2, 3, 4).reshape(Hkv, -1, d)
+            vt = torch.linalg.svd(qh, full_matrices=False).Vh[:, :comp_rank, :]          # [Hkv][r][d]
+            self.basis = vt.transpose(1, 2).contiguous().cuda()                            # [Hkv][d][r]
         self.segs = []
         for c in range(n_copies):
             seg = kvq.Segment(w.bits, dt, B, Hkv, d, w.n_cache + w.n_cur, k_group_tokens=w.k_group_tokens,
-                              kgroup_capacity=n_groups + extra)
+                              kgroup_capacity=n_groups + extra, k_group_channels=self.kgc, comp_basis=self.basis)
             ck, cv = data["cache_k"], data["cache_v"]
             for a in range(w.n_appends):
                 sl = slice(a * w.append_tokens, (a + 1) * w.append_tokens)
@@ -88,7 +98,13 @@ class ChunkStep:
         """Packed codes + fp16 step/zero of the cache + raw current K/V, each read once."""
         w = self.w
         per_tok = 2 * w.head_dim * w.bits / 8 + 4 * (w.head_dim // w.v_group_channels)
-        kmeta = 4 * w.head_dim * w.n_appends * -(-w.append_tokens // w.k_group_tokens)
+        if self.kgc:
+            per_tok += 4 * (w.head_dim // self.kgc)   # K step/zero per (token, channel run)
+            kmeta = 0
+        else:
+            kmeta = 4 * w.head_dim * w.n_appends * -(-w.append_tokens // w.k_group_tokens)
+        if self.comp_rank:
+            per_tok += 16                              # the token's compensation row
         cache = w.batch * w.n_kv_heads * (w.n_cache * per_tok + kmeta)
         cur = 2 * w.batch * w.n_kv_heads * w.n_cur * w.head_dim * 2
         return cache + cur
@@ -104,8 +120,9 @@ class ChunkStep:
             return 0.0
         n = w.n_cur
         rd = 2 * w.batch * w.n_kv_heads * n * w.head_dim * 2
-        wr = w.batch * w.n_kv_heads * (2 * n * w.head_dim * w.bits / 8 + 4 * n * (w.head_dim // 32)
-                                       + 4 * w.head_dim * -(-n // w.k_group_tokens))
+        kmeta = 4 * n * (w.head_dim // self.kgc) if self.kgc else 4 * w.head_dim * -(-n // w.k_group_tokens)
+        wr = w.batch * w.n_kv_heads * (2 * n * w.head_dim * w.bits / 8 + 4 * n * (w.head_dim // 32) + kmeta
+                                       + (16 * n if self.comp_rank else 0))
         return rd + wr
 
     def run(self, events=None):
@@ -413,7 +430,8 @@ def measure_chunk(args, w: workloads.Workload, copies: int = 0):
     # decode caches can sit in the 256 MB last-level cache: rotate copies > 2x that size
     if copies == 0:
         copies = 1 if w.n_cur else 4
-    step = ChunkStep(w, n_copies=copies, fused=args.append == "fused")
+    step = ChunkStep(w, n_copies=copies, fused=args.append == "fused", k_group_channels=args.k_group_channels,
+                     comp_rank=args.comp_rank)
     log("%s: cache built, %d tokens, %d K-groups per head, %d copies" % (w.name, step.base[0], step.base[1], copies))
     separate = None
     if w.n_cur:
@@ -426,7 +444,9 @@ def measure_chunk(args, w: workloads.Workload, copies: int = 0):
     ms_step, attn_ms, app_ms = time_steps(step, args.steps, args.warmup)
     attn_avg = float(np.mean(attn_ms))
     app_avg = float(np.mean(app_ms))
-    default_mode = w.jensen == workloads.WORKLOADS[w.name].jensen   # stored counters: the workload's mode
+    # stored counters hold the workload's own mode: its Jensen form, the fused append, no extra K columns
+    default_mode = (w.jensen == workloads.WORKLOADS[w.name].jensen and args.append == "fused"
+                    and args.k_group_channels == 0 and args.comp_rank == 0)
     flops = step.flops()
     kvb = step.kv_bytes()
     attn_tflops = flops / (attn_avg * 1e-3) / 1e12
@@ -452,7 +472,8 @@ def measure_chunk(args, w: workloads.Workload, copies: int = 0):
         "config": {"workload": w.name, "batch": w.batch, "n_q_heads": w.n_q_heads, "n_kv_heads": w.n_kv_heads,
                    "head_dim": w.head_dim, "cache_tokens": w.n_cache, "cur_tokens": w.n_cur, "queries": w.n_q,
                    "bits": w.bits, "k_group_tokens": w.k_group_tokens, "v_group_channels": w.v_group_channels,
-                   "jensen": int(w.jensen), "cache_copies": copies},
+                   "jensen": int(w.jensen), "cache_copies": copies, "k_group_channels": args.k_group_channels,
+                   "comp_rank": args.comp_rank},
         "roofline": roof,
         "attention": {"ms": round(attn_avg, 4), "ms_median": round(float(np.median(attn_ms)), 4),
                       "ms_p10": round(float(np.percentile(attn_ms, 10)), 4),
@@ -516,6 +537,10 @@ def main():
     ap.add_argument("--jensen", type=int, choices=(0, 1, 2, 3), default=None,
                     help="Jensen correction (0 off, 1 channel-weighted, 2 isotropic, 3 all orders); "
                          "default: the workload's")
+    ap.add_argument("--k-group-channels", type=int, choices=(0, 32, 64, 128), default=0,
+                    help="per-token K groups of this many channels (0: per-channel K groups over tokens)")
+    ap.add_argument("--comp-rank", type=int, choices=range(0, 9), default=0, metavar="R",
+                    help="low-rank logit compensation of rank R (0: none)")
     ap.add_argument("--probe-copy-mib", type=int, default=0,
                     help="after timing, run one plain device copy of this many MiB (the reference dispatch "
                          "for scaling FETCH_SIZE / WRITE_SIZE counters to bytes)")
