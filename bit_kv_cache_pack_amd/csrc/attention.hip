@@ -40,6 +40,7 @@
 // other wave of the SIMD issues around it. A piece's output leaves through the wave's
 // table in LDS as 16-byte row segments: the final output for a whole row block, otherwise
 // unnormalized partials in the workspace, which a combine kernel merges by log-sum-exp.
+#include "decode_walk.cuh"
 #include "kvq_internal.h"
 #include "kvq_quant.cuh"
 #include "kvq_tile.cuh"
@@ -1273,7 +1274,7 @@ __global__ __launch_bounds__(HD) void combine_kernel(AttnParams p) {
                 l[k] = 0.f;
                 continue;
             }
-            const float *pp = p.partial + ((size_t)(s0 + k) * n_rows_total + row) * (HD + 2);
+            const float *pp = p.partial + dwalk::ws_row(s0 + k, n_rows_total, row) * (HD + 2);
             o[k] = pp[c];
             m[k] = pp[HD];
             l[k] = pp[HD + 1];

@@ -32,39 +32,23 @@
 //     and the split-combine kernel finishes them.
 // Channel order inside 16-channel blocks is the position order of kvq_tile.cuh for K
 // operands, Q and V rows; O is written back in channel order.
+#include "decode_walk.cuh"
 #include "kvq_internal.h"
 #include "kvq_tile.cuh"
 
 namespace kvq {
 namespace {
 
-constexpr int kDWaves = 4;
+using dwalk::DGeo;
+using dwalk::kDWaves;
+using dwalk::ST_CUR;
+using dwalk::ST_END;
+using dwalk::ST_PACKED;
+using dwalk::Step;
+using dwalk::TP;
 constexpr int kDThreads = kDWaves * kWave;
-constexpr int TP = 64;   // tokens per step of an INT2 segment (32 for INT4)
-constexpr int TR = 16;   // tokens per step of the current chunk
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr float kDRescale = 8.0f;  // log2 headroom before the running max is moved
-
-template <int HD> struct DGeo {
-    static constexpr int NBL = HD / 64;   // 16-channel blocks per quarter row
-    static constexpr int KS = HD / 32;    // k-steps of the QK product
-    static constexpr int DB = HD / 16;    // 16-position blocks of O^T
-    static constexpr int QV = HD / 32;    // 16-byte vectors per quarter row of 16-bit elements
-    // Value row stride (halves): 8 (HD 128) or 40 (HD 64) dwords mod 64 banks, so the
-    // eight 8-byte rows that half a wave reads per transposed load hit distinct banks.
-    static constexpr int VROW = HD + 16;
-    static constexpr int VTILE = TP * VROW;  // halves per wave
-    static constexpr int OROW = HD + 4;      // epilogue scratch row (floats)
-};
-
-enum : int { ST_END = 0, ST_PACKED = 1, ST_CUR = 3 };
-
-
-struct Step {
-    int kind, seg, g, t, len;
-    int new_group;  // first step of K-group g in this walk
-    int bits;       // the segment's bit-width (16: current chunk)
-};
 
 __device__ __forceinline__ Step uniform(Step s) {
     s.kind = __builtin_amdgcn_readfirstlane(s.kind);
@@ -77,85 +61,11 @@ __device__ __forceinline__ Step uniform(Step s) {
     return s;
 }
 
-// Walks the segments, then the current chunk, over the token range [tb, te), in steps
-// that never cross a K-group. Uniform across the wave. A segment's fields are read once,
-// when the walk enters it, and the end of the group after next is read a group ahead, so
-// a step inside a group costs a few scalar instructions.
-struct Walker {
-    int si, t, e, g, last_g, inited;
-    int sbits, sng, sn;   // the current segment's bit-width, K-groups, tokens
-    int ge, gen;          // end token of group g and of group g + 1
-    const int32_t *tab;   // its K-group table
-    __device__ __forceinline__ void init() {
-        si = 0; inited = 0; last_g = -1; t = e = g = 0;
-        sbits = 16; sng = sn = ge = gen = 0; tab = nullptr;
-    }
-    // end token of group gg, clamped: a corrupt table must not send reads outside the segment
-    __device__ __forceinline__ int group_end(int gg) const {
-        return gg < sng ? min(max(group_start(tab, gg + 1), 0), sn) : sn;
-    }
-    __device__ Step next(const AttnParams &p, int tb, int te) {
-        while (true) {
-            if (si > p.n_segs) return Step{ST_END, 0, 0, 0, 0, 0, 16};
-            if (!inited) {
-                int a;
-                if (si == p.n_segs) {
-                    const int cb = p.n_total - p.n_cur;
-                    a = max(tb, cb) - cb;
-                    e = min(te, p.n_total) - cb;
-                    sbits = 16;
-                } else {
-                    const SegmentView &sg = p.segs[si];
-                    a = max(tb, sg.token_begin) - sg.token_begin;
-                    e = min(te, sg.token_begin + sg.n_tokens) - sg.token_begin;
-                    sbits = sg.bits;
-                    sng = sg.n_kgroups;
-                    sn = sg.n_tokens;
-                    tab = sg.kgroup_start;
-                }
-                if (a >= e) { ++si; continue; }
-                t = a;
-                inited = 1;
-                if (si < p.n_segs && sbits != 16) {
-                    int lo = 0, hi = sng - 1;
-                    while (lo < hi) {
-                        const int mid = (lo + hi) >> 1;
-                        if (group_start(tab, mid + 1) <= a) lo = mid + 1; else hi = mid;
-                    }
-                    g = lo;
-                    last_g = -1;
-                    ge = group_end(g);
-                    gen = group_end(g + 1);
-                }
-            }
-            if (t >= e) { ++si; inited = 0; continue; }
-            if (si == p.n_segs) {
-                const int len = min(TR, e - t);
-                const Step r{ST_CUR, si, 0, t, len, 0, 16};
-                t += len;
-                return r;
-            }
-            if (sbits == 16) { t = e; continue; }   // raw segments take the chunk kernel
-            if (g >= sng) { t = e; continue; }
-            if (ge <= t) {
-                ++g;
-                ge = gen;
-                gen = group_end(g + 1);
-                continue;
-            }
-            const int len = min(sbits == 4 ? TP / 2 : TP, min(ge, e) - t);
-            const Step r{ST_PACKED, si, g, t, len, g != last_g, sbits};
-            last_g = g;
-            t += len;
-            if (t >= ge) {
-                ++g;
-                ge = gen;
-                gen = group_end(g + 1);
-            }
-            return r;
-        }
-    }
+// K-group tables read as uniform scalar loads (group_start)
+struct DevTab {
+    static __device__ __forceinline__ int start(const int32_t *tab, int g) { return group_start(tab, g); }
 };
+typedef dwalk::Walker<DevTab> Walker;
 
 // Registers of one packed step, loaded a step ahead (8 + 8 + 4 words per lane):
 //   INT2: k words 2 b .. (b = 0..3) = token 16 b + L%16, quarter L/16 (HD/64 words each);
@@ -187,16 +97,16 @@ __device__ __forceinline__ void set_word(u32x4 (&a)[N], int w, uint32_t v) {
 // with the old contents, which turns every prefetch into a wait for memory.
 template <int HD>
 __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step &st, size_t bh) {
-    const int r16 = threadIdx.x % 16, j = (threadIdx.x % kWave) / 16;
+    const int lane = threadIdx.x % kWave;
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k);
     if (HD == 64 || st.bits == 2) {   // INT4 only at head_dim 128
-        constexpr int WPR = HD / 16, WL = WPR / 4;   // words per row, per quarter
+        // dwalk::k_words: HD / 64 words per load
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
-            const uint32_t *src = kc + (row0 + min(16 * b + r16, st.len - 1)) * WPR + j * WL;
-            if (WL == 2) {
+            const uint32_t *src = kc + dwalk::k_word(HD, 2, row0, st.len, b, lane);
+            if (HD == 128) {
                 const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
                 set_word(d.k, 2 * b, w.x);
                 set_word(d.k, 2 * b + 1, w.y);
@@ -205,18 +115,9 @@ __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step 
             }
         }
     } else {
-        constexpr int WPR = HD / 8, WL = WPR / 4;
+        // INT4, head_dim 128: 4 words per load
 #pragma unroll
-        for (int b = 0; b < 2; ++b) {
-            const uint32_t *src = kc + (row0 + min(16 * b + r16, st.len - 1)) * WPR + j * WL;
-            if (WL == 4) {
-                d.k[b] = *reinterpret_cast<const u32x4 *>(src);
-            } else {
-                const u32x2 w = *reinterpret_cast<const u32x2 *>(src);
-                set_word(d.k, 2 * b, w.x);
-                set_word(d.k, 2 * b + 1, w.y);
-            }
-        }
+        for (int b = 0; b < 2; ++b) d.k[b] = *reinterpret_cast<const u32x4 *>(kc + dwalk::k_word(HD, 4, row0, st.len, b, lane));
     }
 }
 
@@ -226,13 +127,13 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
-    if (HD == 64 || st.bits == 2) {
-        constexpr int WPR = HD / 16;
-        const int tok = min(lane, st.len - 1);
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR);
+    const int bits = HD == 64 ? 2 : st.bits;
+    // dwalk::v_words = HD / 16 words (an INT2 row, an INT4 half row), in 16-byte loads
+    const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + dwalk::v_word(HD, bits, row0, st.len, lane));
 #pragma unroll
-        for (int i = 0; i < WPR / 4; ++i) d.v[i] = src[i];
-        const uint32_t *vm = sg.v_meta + (row0 + tok) * (HD / 32);
+    for (int i = 0; i < HD / 64; ++i) d.v[i] = src[i];
+    const uint32_t *vm = sg.v_meta + dwalk::vm_word(HD, bits, row0, st.len, lane);
+    if (bits == 2) {   // HD / 32 words
         if (HD == 128) {
             d.vm = *reinterpret_cast<const u32x4 *>(vm);
         } else {
@@ -240,20 +141,10 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
             d.vm.x = m.x;
             d.vm.y = m.y;
         }
-    } else {
-        constexpr int WPR = HD / 8, HW = WPR / 2;  // words per row, per half row
-        const int tok = min(lane / 2, st.len - 1), half = lane % 2;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + (row0 + tok) * WPR + half * HW);
-#pragma unroll
-        for (int i = 0; i < HW / 4; ++i) d.v[i] = src[i];
-        const uint32_t *vm = sg.v_meta + (row0 + tok) * (HD / 32) + half * (HD / 64);
-        if (HD == 128) {
-            const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
-            d.vm.x = m.x;
-            d.vm.y = m.y;
-        } else {
-            d.vm.x = *vm;
-        }
+    } else {           // INT4 at head_dim 128: 2 words
+        const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
+        d.vm.x = m.x;
+        d.vm.y = m.y;
     }
 }
 
@@ -269,10 +160,9 @@ template <int HD, bool BF16> struct DCtx {
 template <int HD>
 __device__ __forceinline__ void load_kmeta(u32x4 (&km)[4 * DGeo<HD>::NBL], const AttnParams &p, const Step &st,
                                            size_t bh) {
-    const int j = (threadIdx.x % kWave) / 16;
     const SegmentView &sg = p.segs[st.seg];
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(sg.k_meta + (bh * sg.kgroup_capacity + st.g) * HD +
-                                                       j * (HD / 4));
+    const u32x4 *src =
+        reinterpret_cast<const u32x4 *>(sg.k_meta + dwalk::km_word(HD, bh, sg.kgroup_capacity, st.g, threadIdx.x % kWave));
 #pragma unroll
     for (int i = 0; i < 4 * DGeo<HD>::NBL; ++i) km[i] = src[i];
 }
@@ -355,7 +245,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     typedef Elem<BF16> E;
     typedef typename DCtx<HD, BF16>::vec vec;
     typedef __attribute__((ext_vector_type(4))) short s16x4;
-    const int lane = threadIdx.x % kWave, r16 = lane % 16, j = lane / 16;
+    const int lane = threadIdx.x % kWave, j = lane / 16;
     const bool packed = st.kind == ST_PACKED;
     const int bits = st.bits;
     const int len = st.len;
@@ -406,8 +296,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
         u32x4 kq[G::QV];
         const size_t row0 = bh * (size_t)p.n_cur + st.t;
         const uint16_t *kb = reinterpret_cast<const uint16_t *>(p.k_cur);
-        const bool ok = r16 < len;
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(kb + (row0 + (ok ? r16 : 0)) * HD + j * (HD / 4));
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(kb + dwalk::ck_elem(HD, row0, len, lane));
 #pragma unroll
         for (int i = 0; i < G::QV; ++i) kq[i] = src[i];
 #pragma unroll
@@ -429,7 +318,6 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     // ---- values -> LDS (row = token, position order); rows past the step repeat its last
     // token (finite, and multiplied by p = 0)
     if (bits == 2) {
-        uint16_t *row = vt + lane * G::VROW;
 #pragma unroll
         for (int gv = 0; gv < HD / 32; ++gv) {
             uint32_t tlo, thi;
@@ -439,31 +327,27 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
                 const int blk = 2 * gv + bb;
                 uint32_t vo[8];
                 v_int2_block(word_of(d.v, blk), tlo, thi, vo);
-                *reinterpret_cast<u32x4 *>(row + 16 * blk) = u32x4{vo[0], vo[1], vo[2], vo[3]};
-                *reinterpret_cast<u32x4 *>(row + 16 * blk + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
+                *reinterpret_cast<u32x4 *>(vt + dwalk::vt_int2<HD>(lane, blk, 0)) = u32x4{vo[0], vo[1], vo[2], vo[3]};
+                *reinterpret_cast<u32x4 *>(vt + dwalk::vt_int2<HD>(lane, blk, 1)) = u32x4{vo[4], vo[5], vo[6], vo[7]};
             }
         }
     } else if (HD == 128 && bits == 4) {
-        const int tok = lane / 2, half = lane % 2;
-        uint16_t *row = vt + tok * G::VROW + half * (HD / 2);
 #pragma unroll
         for (int hb = 0; hb < HD / 32; ++hb) {
             uint32_t vo[8];
             v4_block<BF16>(word_of(d.v, 2 * hb), word_of(d.v, 2 * hb + 1), d.vm[hb / 2], vo);
-            *reinterpret_cast<u32x4 *>(row + 16 * hb) = u32x4{vo[0], vo[1], vo[2], vo[3]};
-            *reinterpret_cast<u32x4 *>(row + 16 * hb + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
+            *reinterpret_cast<u32x4 *>(vt + dwalk::vt_int4<HD>(lane, hb, 0)) = u32x4{vo[0], vo[1], vo[2], vo[3]};
+            *reinterpret_cast<u32x4 *>(vt + dwalk::vt_int4<HD>(lane, hb, 1)) = u32x4{vo[4], vo[5], vo[6], vo[7]};
         }
     } else {
         // current-chunk values, read now: quarter lane % 4 of token lane / 4
-        const int tr = lane / 4, qq = lane % 4;
-        const bool ok = tr < len;
+        const bool ok = lane / 4 < len;
         const size_t row0 = bh * (size_t)p.n_cur + st.t;
         const uint16_t *vb = reinterpret_cast<const uint16_t *>(p.v_cur);
         u32x4 vq[G::QV];
-        const u32x4 *src = reinterpret_cast<const u32x4 *>(vb + (row0 + (ok ? tr : 0)) * HD + qq * (HD / 4));
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vb + dwalk::cv_elem(HD, row0, len, lane));
 #pragma unroll
         for (int i = 0; i < G::QV; ++i) vq[i] = src[i];
-        uint16_t *row = vt + tr * G::VROW + 16 * G::NBL * qq;
 #pragma unroll
         for (int bl = 0; bl < G::NBL; ++bl) {
             uint32_t dd[8], vo[8];
@@ -472,8 +356,8 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
             to_positions(dd, vo);
 #pragma unroll
             for (int q = 0; q < 8; ++q) vo[q] = ok ? E::raw_to_f16(vo[q]) : 0u;
-            *reinterpret_cast<u32x4 *>(row + 16 * bl) = u32x4{vo[0], vo[1], vo[2], vo[3]};
-            *reinterpret_cast<u32x4 *>(row + 16 * bl + 8) = u32x4{vo[4], vo[5], vo[6], vo[7]};
+            *reinterpret_cast<u32x4 *>(vt + dwalk::vt_cur<HD>(lane, bl, 0)) = u32x4{vo[0], vo[1], vo[2], vo[3]};
+            *reinterpret_cast<u32x4 *>(vt + dwalk::vt_cur<HD>(lane, bl, 1)) = u32x4{vo[4], vo[5], vo[6], vo[7]};
         }
     }
     // this step's values are in LDS: fetch the next step's
@@ -528,13 +412,11 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     // 4 jj + aa addresses token T + jj at positions 16 db + 4 aa.
     // the wave's own LDS writes above are read below: one wave's LDS operations complete
     // in issue order, and the compiler keeps the reads after the stores they may alias
-    const int l16 = lane % 16;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-        const int tok0 = 32 * h + 4 * j + l16 / 4;
 #pragma unroll
         for (int db = 0; db < G::DB; ++db) {
-            const uint16_t *p0 = vt + tok0 * G::VROW + 16 * db + 4 * (l16 % 4);
+            const uint16_t *p0 = vt + dwalk::vt_read<HD>(lane, h, db);
             const s16x4 lo4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
                 (__attribute__((address_space(3))) s16x4 *)(p0));
             const s16x4 hi4 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -566,10 +448,9 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
         // Q^T operand: quarter j of row r16 in position order
         u32x4 qv[G::QV];
         if (r16 < rows) {
-            const int hq = h * gqa + r16 / p.n_q, qi = r16 % p.n_q;
-            const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
-            const u32x4 *src = reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(p.q) + qrow * HD +
-                                                               j * (HD / 4));
+            const size_t qrow = dwalk::out_row(b, h, r16, p.n_q_heads, p.n_kv_heads, p.n_q);
+            const u32x4 *src =
+                reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(p.q) + dwalk::q_elem(HD, qrow, j));
 #pragma unroll
             for (int i = 0; i < G::QV; ++i) qv[i] = src[i];
         } else {
@@ -625,10 +506,10 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
 #pragma unroll
     for (int db = 0; db < G::DB; ++db)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sc[r16 * G::OROW + swap_pos(16 * db + 4 * j + i)] = cx.o[db][i];
+        for (int i = 0; i < 4; ++i) sc[dwalk::epi_o<HD>(r16, swap_pos(16 * db + 4 * j + i))] = cx.o[db][i];
     if (j == 0) {
-        sc[16 * G::OROW + r16] = cx.m;
-        sc[16 * G::OROW + 16 + r16] = lt;
+        sc[dwalk::epi_m<HD>(r16)] = cx.m;
+        sc[dwalk::epi_l<HD>(r16)] = lt;
     }
     __syncthreads();
     const size_t n_rows_total = (size_t)p.batch * p.n_q_heads * p.n_q;
@@ -637,19 +518,18 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
         float M = -__builtin_inff();
 #pragma unroll
         for (int w = 0; w < kDWaves; ++w)
-            M = fmaxf(M, reinterpret_cast<const float *>(smem + w * G::VTILE)[16 * G::OROW + r]);
+            M = fmaxf(M, reinterpret_cast<const float *>(smem + w * G::VTILE)[dwalk::epi_m<HD>(r)]);
         float L = 0.f, acc = 0.f;
         if (M != -__builtin_inff()) {
 #pragma unroll
             for (int w = 0; w < kDWaves; ++w) {
                 const float *sw = reinterpret_cast<const float *>(smem + w * G::VTILE);
-                const float wt = exp2_fast(sw[16 * G::OROW + r] - M);
-                L = __builtin_fmaf(wt, sw[16 * G::OROW + 16 + r], L);
-                acc = __builtin_fmaf(wt, sw[r * G::OROW + c], acc);
+                const float wt = exp2_fast(sw[dwalk::epi_m<HD>(r)] - M);
+                L = __builtin_fmaf(wt, sw[dwalk::epi_l<HD>(r)], L);
+                acc = __builtin_fmaf(wt, sw[dwalk::epi_o<HD>(r, c)], acc);
             }
         }
-        const int hq = h * gqa + r / p.n_q, qi = r % p.n_q;
-        const size_t qrow = ((size_t)b * p.n_q_heads + hq) * p.n_q + qi;
+        const size_t qrow = dwalk::out_row(b, h, r, p.n_q_heads, p.n_kv_heads, p.n_q);
         if (gridDim.x == 1) {
             const float v = acc / L;
             if (p.out_dtype == DT_F32) reinterpret_cast<float *>(p.out)[qrow * HD + c] = v;
@@ -657,7 +537,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
             else reinterpret_cast<uint16_t *>(p.out)[qrow * HD + c] = f32_to_f16_bits(v);
             if (c == 0 && p.lse != nullptr) p.lse[qrow] = (M + __log2f(L)) * kLn2;
         } else {
-            float *pp = p.partial + ((size_t)blockIdx.x * n_rows_total + qrow) * (HD + 2);
+            float *pp = p.partial + dwalk::ws_row(blockIdx.x, n_rows_total, qrow) * (HD + 2);
             pp[c] = acc;
             if (c == 0) {
                 pp[HD] = M;

@@ -1,12 +1,13 @@
 """Host code under AddressSanitizer and UndefinedBehaviorSanitizer (no GPU needed).
 
-Two programs under tests/sanitize/ are built with the sanitizers and run:
+Three programs under tests/sanitize/ are built with the sanitizers and run:
 
 * oracle_driver.c with the C oracle: quantize-append in each layout, attention with each
   Jensen form, window scores, budget and gather lists;
 * host_driver.cpp against the library, with the C-ABI layer (argument checks, planners,
   workspace sizing, window budget) built with host-side sanitizers and linked with the
-  library's kernel objects. Every call it makes is answered or rejected before a launch.
+  library's kernel objects. Every call it makes is answered or rejected before a launch;
+* decode_checker.cpp: the decode kernel's own walk and indexing over exact-size buffers.
 
 A report from either sanitizer makes the program exit non-zero (halt_on_error), which
 fails the test with the report in the message.
@@ -62,3 +63,27 @@ def test_library_host_code_under_sanitizers(tmp_path):
          os.path.join(SAN, "host_driver.cpp"), "-x", "none", api_obj] + objs + ["-o", exe])
     r = _run([exe], env=ENV, timeout=300)
     assert "0 failures" in r.stdout
+
+
+def test_decode_kernel_accesses_in_bounds(tmp_path):
+    """The decode kernel's walk and index functions (csrc/decode_walk.cuh, which the kernel
+    itself calls) run on the host for every workgroup, wave, step and lane of real launch
+    plans, over exact-size host buffers under the sanitizers: every access inside its
+    buffer and inside its step's rows, every token walked once, and the configurations the
+    kernel is not built for refused."""
+    from bit_kv_cache_pack_amd import build as B
+    try:
+        hipcc = B.hipcc()
+    except RuntimeError:
+        pytest.skip("hipcc not found")
+    objs = [os.path.join(B.OBJ_DIR, os.path.splitext(s)[0] + ".o") for s in B.SOURCES]
+    if not all(os.path.exists(o) for o in objs):
+        B.build()
+    san = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+           "-Xarch_host", "-fno-sanitize-recover=undefined"]
+    exe = str(tmp_path / "decode_checker")
+    _run([hipcc, "--offload-arch=" + B.ARCH, "-g", "-O1", "-std=c++17"] + san +
+         ["-I", B.INCLUDE, "-I", B.CSRC, "-x", "hip", os.path.join(SAN, "decode_checker.cpp"), "-x", "none"] +
+         objs + ["-o", exe])
+    r = _run([exe], env=ENV, timeout=600)
+    assert " 0 failures" in r.stdout
