@@ -127,13 +127,12 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
-    const int bits = HD == 64 ? 2 : st.bits;
     // dwalk::v_words = HD / 16 words (an INT2 row, an INT4 half row), in 16-byte loads
-    const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + dwalk::v_word(HD, bits, row0, st.len, lane));
+    if (HD == 64 || st.bits == 2) {
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + dwalk::v_word(HD, 2, row0, st.len, lane));
 #pragma unroll
-    for (int i = 0; i < HD / 64; ++i) d.v[i] = src[i];
-    const uint32_t *vm = sg.v_meta + dwalk::vm_word(HD, bits, row0, st.len, lane);
-    if (bits == 2) {   // HD / 32 words
+        for (int i = 0; i < HD / 64; ++i) d.v[i] = src[i];
+        const uint32_t *vm = sg.v_meta + dwalk::vm_word(HD, 2, row0, st.len, lane);   // HD / 32 words
         if (HD == 128) {
             d.vm = *reinterpret_cast<const u32x4 *>(vm);
         } else {
@@ -141,8 +140,11 @@ __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step 
             d.vm.x = m.x;
             d.vm.y = m.y;
         }
-    } else {           // INT4 at head_dim 128: 2 words
-        const u32x2 m = *reinterpret_cast<const u32x2 *>(vm);
+    } else {   // INT4 at head_dim 128
+        const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + dwalk::v_word(HD, 4, row0, st.len, lane));
+#pragma unroll
+        for (int i = 0; i < HD / 64; ++i) d.v[i] = src[i];
+        const u32x2 m = *reinterpret_cast<const u32x2 *>(sg.v_meta + dwalk::vm_word(HD, 4, row0, st.len, lane));
         d.vm.x = m.x;
         d.vm.y = m.y;
     }
