@@ -94,6 +94,16 @@ def test_rollout_chunk_int2_h40_d128():
     _check_step("rollout_chunk_int2_h40_d128", stride=127)
 
 
+@pytest.mark.skip(reason="The WindowQuant decode query (fp16, head_dim 64, FP16 + INT4 + INT2 window segments) "
+                         "faulted the GPU once in an uncommitted working copy of decode_kernel, cause not found. "
+                         "decode_kernel now holds no code for raw segments, fp16, INT4 at head_dim 64 or several "
+                         "segments; decode_eligible sends this call to attention_kernel, which "
+                         "test_windowquant_fp16_gqa14x2_d64 checks against the oracle, and "
+                         "tests/sanitize/decode_checker.cpp checks that routing on the CPU.")
+def test_windowquant_decode_query_on_the_decode_kernel():
+    pass
+
+
 @pytest.mark.parametrize("jensen", [0, 1])
 def test_windowquant_fp16_gqa14x2_d64(jensen):
     """WindowQuant end to end: window scores, FP16/INT4/INT2 assignment and the grouped
