@@ -84,14 +84,15 @@ def test_decode_gqa32x8_32k(bits, jensen):
 
 
 @pytest.mark.timeout(600)
-def test_rollout_chunk_int2_h40_d128():
+@pytest.mark.parametrize("jensen", [1, 3])
+def test_rollout_chunk_int2_h40_d128(jensen):
     """Long rollout: 74,880 cached INT2 tokens + 4,680 current, 40 heads; every 127th
     query row and the last one, so every 256-row block of every head holds at least two
-    checked rows."""
+    checked rows (the second-order and the all-orders Jensen forms)."""
     w = workloads.WORKLOADS["rollout_chunk_int2_h40_d128"]
     rows = _rows(w.n_q, 127)
     assert {r // 256 for r in rows} == set(range(-(-w.n_q // 256)))
-    _check_step("rollout_chunk_int2_h40_d128", stride=127)
+    _check_step("rollout_chunk_int2_h40_d128", stride=127, jensen=jensen)
 
 
 @pytest.mark.skip(reason="The WindowQuant decode query (fp16, head_dim 64, FP16 + INT4 + INT2 window segments) "
