@@ -572,36 +572,178 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
 }
 
 // The all-orders Jensen terms of K-groups g0 .. g0+31 for the wave's 32 queries, log2
-// domain: sum over channels of log2(sinh(a) / a), a = (tau / 2) |q_c| step_c. Lane (r32, hh)
-// sums its query's channels of half hh (the positions it holds q at) for one group at a
-// time; the two halves meet through the lane L ^ 32 exchange.
+// domain: beta = sum over channels of G(a), G(a) = log2(sinh(a) / a), a = (tau / 2) |q_c|
+// step_c. With qm_c = (tau / 2) max over the wave's rows of |q_c| (the wave's table, see
+// exact_qmax), a^2 = u_q u_d with u_q = (q_c / max|q_c|)^2 <= 1 and u_d = (qm_c step_c)^2.
+// Where u_d <= 1, so a <= 1 for every row, G is its Taylor series in a^2 to the fifth
+// term (the sixth is below 2.7e-7), and the sum over channels of each term is a matrix
+// product over channels of u_q^k and u_d^k, as beta_block's (bf16 high and low parts for the
+// first two terms, high parts for the rest, each below 5.1e-4). The (group, channel)
+// pairs with u_d > 1, few (channels with outlying steps), are left out of the products and
+// evaluated directly for every row afterwards (exact_fallback).
+constexpr float kExactC[5] = {0.24044917f, -8.0149723e-3f, 5.0888713e-4f, -3.8166535e-5f, 3.0841773e-6f};
+// log2(e) times 1/6, -1/180, 1/2835, -1/37800, 1/467775
+
+// x = qm_c step_c beyond the series' range: the one test both beta_block_poly and
+// exact_fallback take.
+__device__ __forceinline__ bool outside_series(float x) { return x > 1.0f; }
+
 template <int HD, bool BF16>
-__device__ __forceinline__ void beta_block_exact(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0,
-                                                 float half_scale) {
+__device__ __forceinline__ void beta_block_poly(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0,
+                                                const float *qmt, uint32_t (&bigmask)[2]) {
     typedef Ctx<HD, BF16> C;
     const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
-    const int n = min(32, sg.n_kgroups - g0);
-    for (int gi = 0; gi < n; ++gi) {
-        const uint32_t *km = sg.k_meta + (bh * sg.kgroup_capacity + g0 + gi) * HD + 2 * hh;
-        float sum = 0.f;
+    const int g = g0 + r32;
+    const bool ok = g < sg.n_kgroups;
+    // this lane's channels in block ks: 4k + 2hh (elements i = k) and 4k + 2hh + 1 (i = 4 + k)
+    const uint32_t *km = sg.k_meta + (bh * sg.kgroup_capacity + (ok ? g : 0)) * HD + 2 * hh;
+    f32x16 acc = {};
+    uint32_t big[2] = {0u, 0u};   // this lane's group: bit 8 ks + i of its positions
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks) {
-            // opaque: the query values are taken apart here, per group, not hoisted out of the
-            // group loop (64 more live registers)
+    for (int ks = 0; ks < C::KS; ++ks) {
+        float ud[8], uq[8];
+        {
+            uint32_t m[8];
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) {
+                const u32x2 v = ok ? *reinterpret_cast<const u32x2 *>(km + 16 * ks + 4 * kk) : u32x2{0u, 0u};
+                m[kk] = v.x;
+                m[4 + kk] = v.y;
+            }
+            // opaque: the query side is derived here, not hoisted out of the tile loop
             u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
             asm volatile("" : "+v"(qw));
+            const f32x4 *qv4 = reinterpret_cast<const f32x4 *>(qmt + 16 * ks + 8 * hh);
+            const f32x4 *rv4 = reinterpret_cast<const f32x4 *>(qmt + HD + 16 * ks + 8 * hh);
+            const f32x4 qa = qv4[0], qb = qv4[1], ra = rv4[0], rb = rv4[1];
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-                // channels 4k + 2hh (element k) and 4k + 2hh + 1 (element 4 + k) of block ks
-                const u32x2 v = *reinterpret_cast<const u32x2 *>(km + 16 * ks + 4 * k);
-                const float q0 = C::E::val((qw[k / 2] >> (16 * (k % 2))) & 0xffffu);
-                const float q1 = C::E::val((qw[(4 + k) / 2] >> (16 * (k % 2))) & 0xffffu);
-                sum += log2_sinhc(half_scale * __builtin_fabsf(q0) * f16_bits_to_f32(v.x & 0xffffu));
-                sum += log2_sinhc(half_scale * __builtin_fabsf(q1) * f16_bits_to_f32(v.y & 0xffffu));
+            for (int i = 0; i < 8; ++i) {
+                const float qmi = i < 4 ? qa[i] : qb[i - 4], rqi = i < 4 ? ra[i] : rb[i - 4];
+                const float x = f16_bits_to_f32(m[i] & 0xffffu) * qmi;
+                const bool bg = outside_series(x);
+                big[(8 * ks + i) / 32] |= (bg ? 1u : 0u) << ((8 * ks + i) % 32);
+                ud[i] = bg ? 0.f : x * x;
+                const float t = C::E::val((qw[i / 2] >> (16 * (i % 2))) & 0xffffu) * rqi;
+                uq[i] = t * t;
             }
         }
-        sum += other_half(sum);
-        if (hh == 0) cx.btab[gi * 32 + r32] = sum;
+        // terms in increasing order, each power from the previous one
+        float pd[8], pq[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            pd[i] = ud[i];
+            pq[i] = uq[i];
+        }
+#pragma unroll
+        for (int k = 0; k < 5; ++k) {
+            bf16x8 ah, bh8, al, bl8;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float qv = kExactC[k] * pq[i];
+                const __bf16 dh = (__bf16)pd[i], qh = (__bf16)qv;
+                ah[i] = dh;
+                bh8[i] = qh;
+                if (k < 2) {
+                    al[i] = (__bf16)(pd[i] - (float)dh);
+                    bl8[i] = (__bf16)(qv - (float)qh);
+                }
+                if (k < 4) {
+                    pd[i] *= ud[i];
+                    pq[i] *= uq[i];
+                }
+            }
+            acc = mfma32_bf16(ah, bh8, acc);
+            if (k < 2) {
+                acc = mfma32_bf16(ah, bl8, acc);
+                acc = mfma32_bf16(al, bh8, acc);
+            }
+        }
+    }
+    // C layout: acc[j] is group 8 (j / 4) + 4 hh + j % 4 of the block, for query r32. The
+    // wave alone writes and reads its table, and one wave's LDS operations complete in order.
+#pragma unroll
+    for (int j = 0; j < 16; ++j) cx.btab[(8 * (j / 4) + 4 * hh + (j % 4)) * 32 + r32] = acc[j];
+    // the positions outlying in any group of the block, for the whole wave
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+        uint32_t v = big[w];
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) v |= __shfl_xor(v, o);
+        bigmask[w] = v;   // lanes of half hh: the positions 16 ks + 8 hh + i, bit 8 ks + i
+    }
+}
+
+// The (group, channel) pairs beta_block_poly left out: G(a) of every row of the wave, added
+// to its table. Positions with a bit in either half's mask are walked one at a time (uniform);
+// each lane takes its row's query element at the position (from the half holding it), and
+// each group's step is read once per position.
+template <int HD, bool BF16>
+__device__ __forceinline__ void exact_fallback(Ctx<HD, BF16> &cx, const SegmentView &sg, size_t bh, int g0,
+                                               const float *qmt, const uint32_t (&bigmask)[2], float half_scale) {
+    typedef Ctx<HD, BF16> C;
+    const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
+    const int ng = min(32, sg.n_kgroups - g0);
+    for (int h2 = 0; h2 < 2; ++h2) {
+        for (int w = 0; w < 2; ++w) {
+            // the mask of half h2 (lanes 32 h2 .. 32 h2 + 31 hold it)
+            uint32_t mask = __builtin_amdgcn_readlane(bigmask[w], 32 * h2);
+            while (mask != 0u) {
+                const int bit = __builtin_ctz(mask);
+                mask &= mask - 1u;
+                const int pidx = 32 * w + bit;          // 8 ks + i
+                const int ks = pidx / 8, i = pidx % 8;
+                const int pos = 16 * ks + 8 * h2 + i;   // position in the row
+                const int ch = 16 * ks + 4 * (i % 4) + 2 * h2 + i / 4;
+                // this lane's query element at (ks, i) of its own half; the row's value at the
+                // position comes from the half h2 lane of the same row
+                // static walk over the lane's elements: no register array indexed at run time
+                uint32_t h16 = 0u;
+#pragma unroll
+                for (int k = 0; k < C::KS; ++k) {
+                    const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[k]);
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        if (8 * k + e == pidx) h16 = (qw[e / 2] >> (16 * (e % 2))) & 0xffffu;
+                }
+                const float mine = C::E::val(h16);
+                const float there = other_half(mine);
+                const float qv = hh == h2 ? mine : there;
+                const float qmi = qmt[pos];
+                const float aq = half_scale * __builtin_fabsf(qv);
+                for (int gi = 0; gi < ng; ++gi) {
+                    const uint32_t mt = group_start(reinterpret_cast<const int32_t *>(sg.k_meta) +
+                                                        (bh * sg.kgroup_capacity + g0 + gi) * HD, ch);
+                    const float st = f16_bits_to_f32(mt & 0xffffu);
+                    if (outside_series(st * qmi)) {   // the pair beta_block_poly left out
+                        const float v = log2_sinhc(aq * st);
+                        if (hh == 0) cx.btab[gi * 32 + r32] += v;
+                    }
+                }
+            }
+        }
+    }
+}
+
+// qm of the wave's table: (tau / 2) max over the wave's 32 rows of |q| per position, then
+// its reciprocal (0 for a zero column), [HD] each.
+template <int HD, bool BF16>
+__device__ __forceinline__ void exact_qmax(const Ctx<HD, BF16> &cx, float half_scale, float *qmt) {
+    typedef Ctx<HD, BF16> C;
+    const int lane = threadIdx.x % kWave, r32 = lane % 32, hh = lane / 32;
+#pragma unroll
+    for (int ks = 0; ks < C::KS; ++ks) {
+        const u32x4 qw = __builtin_bit_cast(u32x4, cx.q[ks]);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float v = __builtin_fabsf(C::E::val((qw[i / 2] >> (16 * (i % 2))) & 0xffffu));
+#pragma unroll
+            for (int o = 1; o < 32; o <<= 1) v = fmaxf(v, __shfl_xor(v, o));
+            if (r32 == 0) {
+                const float qm = half_scale * v;
+                qmt[16 * ks + 8 * hh + i] = qm;
+                qmt[HD + 16 * ks + 8 * hh + i] = qm > 0.f ? 1.0f / v : 0.f;
+            }
+        }
     }
 }
 
@@ -960,6 +1102,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     __shared__ __attribute__((aligned(16))) uint16_t smem[2 * G::BUF];
     __shared__ __attribute__((aligned(16))) uint16_t augs[AUG ? 2 * TT * AROW : 8];
     __shared__ float btab_all[kWaves][32 * 32];
+    // EXACT: per wave, (tau / 2) max |q| per position and its reciprocal (exact_qmax)
+    __shared__ float qmt_all[EXACT ? kWaves * 2 * HD : 1];
     const int tid = threadIdx.x, lane = tid % kWave;
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);  // uniform: wave_ok branches on scalars
     const int r32 = lane % 32, hh = lane / 32;
@@ -1017,6 +1161,8 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             }
         }
         if constexpr (AUG) aug_operand<HD, BF16>(cx, p, h);
+        float *qmt_w = qmt_all + (EXACT ? wave * 2 * HD : 0);
+        if constexpr (EXACT) exact_qmax<HD, BF16>(cx, p.half_scale, qmt_w);
 #pragma unroll
         for (int db = 0; db < C::DB; ++db) cx.o[db] = f32x16{};
         cx.btab = btab_all[wave];
@@ -1064,9 +1210,11 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
             if (wave_ok) {
                 if (cur.kind() == TILE_PACKED) {
                     if (cur.batch()) {
-                        if constexpr (EXACT)
-                            beta_block_exact<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, p.half_scale);
-                        else
+                        if constexpr (EXACT) {
+                            uint32_t bigm[2];
+                            beta_block_poly<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, qmt_w, bigm);
+                            exact_fallback<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, qmt_w, bigm, p.half_scale);
+                        } else
                             beta_block<HD, BF16>(cx, p.segs[cur.seg()], bh, cur.g, p.jensen == JENSEN_ISO);
                     }
                     if (cur.new_group()) cx.beta = p.beta_log2 * beta_of<HD, BF16>(cx, cur.jrow());

@@ -110,3 +110,27 @@ def test_noalloc_matches_oracle(case):
     assert torch.equal(out, ref)
     assert np.abs(out.cpu().numpy() - oo).max() <= TOL
     assert np.abs(lse.cpu().numpy() - ol).max() <= TOL
+
+
+@pytest.mark.parametrize("dtype,d", [("bf16", 128), ("f16", 64)])
+def test_exact_jensen_outlying_key_channels(dtype, d):
+    """The all-orders form where some K-groups hold channels with large steps (outlier
+    channels scaled up to 60x, some in every group, some in two groups only), so that the
+    kernel's direct evaluation of the pairs outside its series' range runs beside the series."""
+    B, Hq, Hkv, n_q, n_cache, n_cur = 1, 4, 2, 600, 1000, 100
+    Gk = 128
+    k = _rand((B, Hkv, n_cache, d), "bf16", 241).float()
+    k[..., 5] *= 30.0
+    k[:, :, 256:512, 3] *= 60.0
+    k[:, 1, 640:768, d - 7] *= 45.0
+    gseg, oseg = make_pair(2, dtype, B, Hkv, d, capacity=n_cache, Gk=Gk, kgroup_capacity=-(-n_cache // Gk))
+    append_both(gseg, oseg, k.to(TORCH_DT[dtype]), _rand((B, Hkv, n_cache, d), dtype, 242))
+    q = _rand((B, Hq, n_q, d), dtype, 243, 1.5)
+    kc = _rand((B, Hkv, n_cur, d), dtype, 244)
+    vc = _rand((B, Hkv, n_cur, d), dtype, 245)
+    oo, ol = oracle_attention(q, [oseg], kc, vc, n_kv_heads=Hkv, jensen=3)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device="cuda")
+    out = kvq.chunk_attention(q.cuda(), [gseg], kc.cuda(), vc.cuda(), n_kv_heads=Hkv, jensen=3, lse=lse)
+    torch.cuda.synchronize()
+    assert np.abs(out.cpu().numpy() - oo).max() <= TOL
+    assert np.abs(lse.cpu().numpy() - ol).max() <= TOL
