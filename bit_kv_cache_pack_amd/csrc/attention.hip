@@ -581,7 +581,7 @@ __device__ __forceinline__ void beta_block(Ctx<HD, BF16> &cx, const SegmentView 
 // first two terms, high parts for the rest, each below 5.1e-4). The (group, channel)
 // pairs with u_d > 1, few (channels with outlying steps), are left out of the products and
 // evaluated directly for every row afterwards (exact_fallback).
-constexpr float kExactC[5] = {0.24044917f, -8.0149723e-3f, 5.0888713e-4f, -3.8166535e-5f, 3.0841773e-6f};
+constexpr float kExactC[5] = {0.24044917f, -8.0149723e-3f, 5.0888713e-4f, -3.8166535e-5f, 3.0841645e-6f};
 // log2(e) times 1/6, -1/180, 1/2835, -1/37800, 1/467775
 
 // x = qm_c step_c beyond the series' range: the one test both beta_block_poly and
