@@ -261,7 +261,56 @@ static void check_walk_multi() {
     printf("%-34s ok so far: %s\n", "walk over two window segments", fails ? "no" : "yes");
 }
 
+// The value tile's layout: an INT2 step's writes (64 lanes x HD / 16 blocks x 2 parts of 8
+// halves) cover each of the tile's 64 token rows at every channel position exactly once and
+// never the row padding; an INT4 step's cover rows 0..31 once, a current-chunk step's rows
+// 0..15; the PV reads stay inside the rows and the channel positions.
+template <int HD>
+static void check_tile_layout() {
+    typedef DGeo<HD> G;
+    static int cnt[G::VTILE];
+    auto expect = [&](int n_rows, const char *what) {
+        for (int i = 0; i < G::VTILE; ++i)
+            CHECK(cnt[i] == (i < n_rows * G::VROW && i % G::VROW < HD ? 1 : 0),
+                  "d%d: %s: tile half %d (row %d, position %d) written %d times", HD, what, i, i / G::VROW,
+                  i % G::VROW, cnt[i]);
+        memset(cnt, 0, sizeof(cnt));
+    };
+    auto write = [&](int i, const char *what) {
+        for (int k = 0; k < 8; ++k) {
+            CHECK(i + k >= 0 && i + k < G::VTILE, "d%d: %s write %d outside the tile", HD, what, i + k);
+            if (i + k >= 0 && i + k < G::VTILE) ++cnt[i + k];
+        }
+    };
+    memset(cnt, 0, sizeof(cnt));
+    for (int lane = 0; lane < kLanes; ++lane)
+        for (int blk = 0; blk < HD / 16; ++blk)
+            for (int part = 0; part < 2; ++part) write(vt_int2<HD>(lane, blk, part), "INT2");
+    expect(TP, "INT2");
+    if (HD == 128) {
+        for (int lane = 0; lane < kLanes; ++lane)
+            for (int hb = 0; hb < HD / 32; ++hb)
+                for (int part = 0; part < 2; ++part) write(vt_int4<HD>(lane, hb, part), "INT4");
+        expect(TP / 2, "INT4");
+    }
+    for (int lane = 0; lane < kLanes; ++lane)
+        for (int bl = 0; bl < G::NBL; ++bl)
+            for (int part = 0; part < 2; ++part) write(vt_cur<HD>(lane, bl, part), "current chunk");
+    expect(TR, "current chunk");
+    for (int lane = 0; lane < kLanes; ++lane)
+        for (int h = 0; h < 2; ++h)
+            for (int db = 0; db < G::DB; ++db)
+                for (int off = 0; off <= 16 * G::VROW; off += 16 * G::VROW) {
+                    const int i = vt_read<HD>(lane, h, db) + off;
+                    CHECK(i >= 0 && i + 4 <= TP * G::VROW && i % G::VROW + 4 <= HD, "d%d: PV read %d", HD, i);
+                }
+    printf("%-34s ok so far: %s\n", HD == 64 ? "value tile layout, head_dim 64" : "value tile layout, head_dim 128",
+           fails ? "no" : "yes");
+}
+
 int main() {
+    check_tile_layout<64>();
+    check_tile_layout<128>();
     const Config cases[] = {
         // name, B, Hq, Hkv, HD, n_q, bits, n_tokens, capacity, Gk, n_cur
         {"GQA decode INT2 32k", 8, 32, 8, 128, 1, 2, 32768, 32768, 128, 0},

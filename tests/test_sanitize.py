@@ -7,7 +7,8 @@ Three programs under tests/sanitize/ are built with the sanitizers and run:
 * host_driver.cpp against the library, with the C-ABI layer (argument checks, planners,
   workspace sizing, window budget) built with host-side sanitizers and linked with the
   library's kernel objects. Every call it makes is answered or rejected before a launch;
-* decode_checker.cpp: the decode kernel's own walk and indexing over exact-size buffers.
+* decode_checker.cpp: the decode kernel's own walk and indexing over exact-size buffers,
+  and its value tile's layout (each row and channel position written once per step).
 
 A report from either sanitizer makes the program exit non-zero (halt_on_error), which
 fails the test with the report in the message.
