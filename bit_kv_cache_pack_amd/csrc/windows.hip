@@ -9,7 +9,7 @@
 // Score of a window: for each KV head the window's mean key, cosine with the text vector,
 // averaged over heads. Everything in double, summed in index order (this file is built
 // with -ffp-contract=off), so the scores and therefore the ranking are reproducible.
-// Several independent caches (layers) are scored and assigned by the same two launches:
+// Several independent caches (layers) are scored and assigned by the same three launches:
 // blockIdx.y is the layer. The selection also writes the grouped layout's gather lists
 // ({first token, length} of every window, FP16 windows first, then INT4, then INT2, each
 // ascending) and each class's token count, so that the appends can take them as they are.
@@ -78,80 +78,74 @@ __global__ __launch_bounds__(kScoreThreads) void window_score_kernel(WindowParam
     if (tid == 0) p.score[(size_t)layer * p.n_windows + w] = acc / (double)H;
 }
 
-constexpr int kSortMax = 8192;   // windows ranked by a sort in LDS; more are ranked by counting
-
 // window a comes before window b: higher score, ties to the lower index
 __device__ __forceinline__ bool before(double sa, int ia, double sb, int ib) {
     return sa > sb || (sa == sb && ia < ib);
 }
+__device__ __forceinline__ int8_t class_of(int rank, int n16, int n4) {
+    return rank < n16 - 1 ? 16 : (rank < n16 - 1 + n4 ? 4 : 2);
+}
 
-// One workgroup: rank windows 1..W-1 (score descending, ties to the lower index), cut
-// into FP16 / INT4 / INT2 by the budget (window 0 is FP16), then list each class in
-// ascending window order. The ranking is a bitonic sort of (score, index) in LDS; the
-// lists come from a block prefix sum, over the windows in index order, of three class
-// counters packed in one 64-bit word.
+constexpr int kRankWaves = 4;
+
+// Rank of windows 1..W-1 among themselves (score descending, ties to the lower index),
+// counted: the rank of a window is the number of windows before it. Lane L of workgroup x
+// ranks window 1 + 64 x + L; wave q counts over the q-th quarter of the windows, and the
+// quarters' counts are summed through LDS. "before" is a strict total order on (score,
+// index), so the counts are exactly the positions a sort by it gives. The class follows
+// from the rank and the budget (the first n16 - 1 FP16, the next n4 INT4, the rest INT2);
+// window 0 is FP16 whatever its score.
+__global__ __launch_bounds__(kRankWaves * kWave) void window_rank_kernel(WindowParams p) {
+    __shared__ int part[kRankWaves][kWave];
+    const int W = p.n_windows, lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+    const size_t lw = (size_t)blockIdx.y * W;
+    const double *score = p.score + lw;
+    const int w = 1 + blockIdx.x * kWave + lane;
+    const double s = w < W ? score[w] : 0.0;
+    const int per = (W - 1 + kRankWaves - 1) / kRankWaves;
+    const int v0 = 1 + wave * per, v1 = min(W, v0 + per);
+    int rank = 0;
+    int v = v0;
+    // every lane reads the same score: one request per wave; eight in flight at a time
+    for (; v + 8 <= v1; v += 8) {
+        double t[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) t[k] = score[v + k];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) rank += before(t[k], v + k, s, w) ? 1 : 0;
+    }
+    for (; v < v1; ++v) rank += before(score[v], v, s, w) ? 1 : 0;
+    part[wave][lane] = rank;
+    __syncthreads();
+    if (wave == 0 && w < W) {
+        int r = 0;
+#pragma unroll
+        for (int q = 0; q < kRankWaves; ++q) r += part[q][lane];
+        p.bits_out[lw + w] = class_of(r, p.n_fp16, p.n_int4);
+    }
+    if (blockIdx.x == 0 && threadIdx.x == 0) p.bits_out[lw] = 16;
+}
+
+// One workgroup per layer, after window_rank_kernel: each class listed in ascending window
+// order (FP16 at 0, INT4 at n16, INT2 at n16 + n4) through a block prefix sum, over the
+// windows in index order, of three class counters packed in one 64-bit word; the gather
+// lists and each class's token count alongside.
 __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowParams p) {
     __shared__ int8_t cls[kMaxWindowsPerLayer];
-    __shared__ double key[kSortMax];
-    __shared__ int idx[kSortMax];
     __shared__ unsigned long long wsum[kSelectThreads / kWave];
     const int W = p.n_windows, tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
     const int n16 = p.n_fp16, n4 = p.n_int4;
-    const int M = W - 1;
     const size_t lw = (size_t)blockIdx.y * W;   // this layer's windows
-    const double *score = p.score + lw;
-    int8_t *bits_out = p.bits_out + lw;
+    const int8_t *bits_in = p.bits_out + lw;
     int32_t *order_out = p.order_out + lw;
     int32_t *groups_out = p.groups_out != nullptr ? p.groups_out + 2 * lw : nullptr;
-    auto class_of = [&](int rank) -> int8_t { return rank < n16 - 1 ? 16 : (rank < n16 - 1 + n4 ? 4 : 2); };
-    if (M <= kSortMax) {
-        int N = 1;
-        while (N < M) N <<= 1;
-        for (int i = tid; i < N; i += kSelectThreads) {
-            key[i] = i < M ? score[i + 1] : -__builtin_inf();
-            idx[i] = i < M ? i + 1 : 0x7fffffff;   // pads sort last
-        }
-        __syncthreads();
-        for (int k = 2; k <= N; k <<= 1) {
-            for (int j = k >> 1; j > 0; j >>= 1) {
-                for (int i = tid; i < N; i += kSelectThreads) {
-                    const int l = i ^ j;
-                    if (l > i) {
-                        const double si = key[i], sl = key[l];
-                        const int ii = idx[i], il = idx[l];
-                        // blocks with bit k clear end in "before" order, the others in reverse
-                        const bool swap = (i & k) == 0 ? before(sl, il, si, ii) : before(si, ii, sl, il);
-                        if (swap) {
-                            key[i] = sl; key[l] = si;
-                            idx[i] = il; idx[l] = ii;
-                        }
-                    }
-                }
-                __syncthreads();
-            }
-        }
-        // position r holds the window of rank r
-        for (int r = tid; r < M; r += kSelectThreads) cls[idx[r]] = class_of(r);
-    } else {
-        for (int w = threadIdx.x; w < W; w += kSelectThreads) {
-            if (w == 0) continue;
-            const double s = score[w];
-            int rank = 0;
-            for (int v = 1; v < W; ++v) {
-                const double t = score[v];
-                rank += before(t, v, s, w) ? 1 : 0;
-            }
-            cls[w] = class_of(rank);
-        }
-    }
-    if (tid == 0) cls[0] = 16;
+    for (int w = tid; w < W; w += kSelectThreads) cls[w] = bits_in[w];
     __syncthreads();
     // class lists, each in ascending window order: FP16 at 0, INT4 at n16, INT2 at n16 + n4
     unsigned long long carry = 0;   // counts of the windows before this chunk, 21 bits per class
     for (int w0 = 0; w0 < W; w0 += kSelectThreads) {
         const int w = w0 + tid;
         const int8_t b = w < W ? cls[w] : 0;
-        if (w < W) bits_out[w] = b;
         const int sh = b == 16 ? 0 : (b == 4 ? 21 : 42);
         const unsigned long long v = w < W ? 1ull << sh : 0ull;
         unsigned long long x = v;
@@ -200,6 +194,10 @@ __global__ __launch_bounds__(kSelectThreads) void window_select_kernel(WindowPar
 hipError_t launch_windows(const WindowParams &p, hipStream_t s) {
     hipLaunchKernelGGL(window_score_kernel, dim3(p.n_windows, p.n_layers), dim3(kScoreThreads), 0, s, p);
     hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int rank_wg = p.n_windows > 1 ? (p.n_windows - 1 + kWave - 1) / kWave : 1;
+    hipLaunchKernelGGL(window_rank_kernel, dim3(rank_wg, p.n_layers), dim3(kRankWaves * kWave), 0, s, p);
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(window_select_kernel, dim3(1, p.n_layers), dim3(kSelectThreads), 0, s, p);
     return hipGetLastError();
