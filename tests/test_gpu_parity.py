@@ -212,6 +212,21 @@ def test_windows_scores_and_assignment():
     _check_windows(asg, k, t, 1000)
 
 
+@pytest.mark.parametrize("N", [20, 32, 64, 2080, 2081, 4129])
+def test_windows_rank_boundaries(N):
+    """Window counts at the ranking's edges: one window (20, 32: nothing to rank), two, 65
+    (one more than a workgroup ranks), 66 and 130 windows (several workgroups, ranges not
+    split evenly over the four waves); bits, order, lists and counts against the oracle,
+    with tied scores (repeated windows) in the larger cases."""
+    k, t = _window_case(2, 2, N, 64, 31 + N % 7)
+    if N > 2000:
+        k[:, :, 32 * 7:32 * 8] = k[:, :, 32 * 3:32 * 4]     # windows 3 and 7 score the same
+        k[:, :, 32 * 40:32 * 41] = k[:, :, 32 * 3:32 * 4]
+    asg = kvq.assign_windows(k.cuda(), t.cuda(), 10, 30)
+    torch.cuda.synchronize()
+    _check_windows(asg, k, t, N)
+
+
 @pytest.mark.parametrize("N", [6272, 6256])
 def test_windows_many_layers_one_launch(N):
     """Prefill scale: 12 independent caches (layers) scored and assigned by one pair of
