@@ -95,13 +95,13 @@ __device__ __forceinline__ void set_word(u32x4 (&a)[N], int w, uint32_t v) {
 // it repeats the last one: its keys' scores are masked and its values are zeroed in LDS):
 // a load under a per-lane condition would have to land before its registers are merged
 // with the old contents, which turns every prefetch into a wait for memory.
-template <int HD>
+template <int HD, int PB>
 __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step &st, size_t bh) {
     const int lane = threadIdx.x % kWave;
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *kc = reinterpret_cast<const uint32_t *>(sg.k);
-    if (HD == 64 || st.bits == 2) {   // INT4 only at head_dim 128
+    if (HD == 64 || PB == 2) {   // INT4 only at head_dim 128
         // dwalk::k_words: HD / 64 words per load
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
@@ -121,14 +121,14 @@ __device__ __forceinline__ void load_k(DSet &d, const AttnParams &p, const Step 
     }
 }
 
-template <int HD>
+template <int HD, int PB>
 __device__ __forceinline__ void load_v(DSet &d, const AttnParams &p, const Step &st, size_t bh) {
     const int lane = threadIdx.x % kWave;
     const SegmentView &sg = p.segs[st.seg];
     const size_t row0 = bh * (size_t)sg.capacity + st.t;
     const uint32_t *vc = reinterpret_cast<const uint32_t *>(sg.v);
     // dwalk::v_words = HD / 16 words (an INT2 row, an INT4 half row), in 16-byte loads
-    if (HD == 64 || st.bits == 2) {
+    if (HD == 64 || PB == 2) {
         const u32x4 *src = reinterpret_cast<const u32x4 *>(vc + dwalk::v_word(HD, 2, row0, st.len, lane));
 #pragma unroll
         for (int i = 0; i < HD / 64; ++i) d.v[i] = src[i];
@@ -240,7 +240,7 @@ __device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx, bool iso) 
     return acc;
 }
 
-template <int HD, bool BF16, bool EXACT>
+template <int HD, bool BF16, bool EXACT, int PB>
 __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const Step &st, const Step &nx,
                                              uint16_t *vt, const AttnParams &p, size_t bh) {
     typedef DGeo<HD> G;
@@ -249,7 +249,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     typedef __attribute__((ext_vector_type(4))) short s16x4;
     const int lane = threadIdx.x % kWave, j = lane / 16;
     const bool packed = st.kind == ST_PACKED;
-    const int bits = st.bits;
+    const int bits = packed ? PB : 16;   // the launch's one packed segment has PB bits
     const int len = st.len;
     const bool nx_packed = nx.kind == ST_PACKED;
 
@@ -314,7 +314,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     // this step's keys are expanded: fetch the next step's keys and K-group {step, zero}
     if (nx_packed) {
         if (nx.new_group) load_kmeta<HD>(cx.km, p, nx, bh);
-        load_k<HD>(d, p, nx, bh);
+        load_k<HD, PB>(d, p, nx, bh);
     }
 
     // ---- values -> LDS (row = token, position order); rows past the step repeat its last
@@ -363,7 +363,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
         }
     }
     // this step's values are in LDS: fetch the next step's
-    if (nx_packed) load_v<HD>(d, p, nx, bh);
+    if (nx_packed) load_v<HD, PB>(d, p, nx, bh);
 
     // ---- online softmax (log2 domain); tokens past the step do not exist
     if (len < TP) {
@@ -430,8 +430,9 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     }
 }
 
-// EXACT: the all-orders Jensen form, in its own instance (as in the chunk kernel).
-template <int HD, bool BF16, bool EXACT>
+// EXACT: the all-orders Jensen form, in its own instance (as in the chunk kernel). PB: the
+// bit-width of the launch's packed segment, one instance each.
+template <int HD, bool BF16, bool EXACT, int PB>
 __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     typedef DGeo<HD> G;
     typedef typename DCtx<HD, BF16>::vec vec;
@@ -492,11 +493,11 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     Step s1 = uniform(wk.next(p, tb, te));
     if (s0.kind == ST_PACKED) {
         load_kmeta<HD>(cx.km, p, s0, bh);
-        load_k<HD>(d, p, s0, bh);
-        load_v<HD>(d, p, s0, bh);
+        load_k<HD, PB>(d, p, s0, bh);
+        load_v<HD, PB>(d, p, s0, bh);
     }
     while (s0.kind != ST_END) {
-        process_step<HD, BF16, EXACT>(cx, d, s0, s1, vt, p, bh);
+        process_step<HD, BF16, EXACT, PB>(cx, d, s0, s1, vt, p, bh);
         s0 = s1;
         s1 = uniform(wk.next(p, tb, te));
     }
@@ -549,14 +550,14 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     }
 }
 
-template <int HD>
+template <int HD, int PB>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
     constexpr bool BF16 = true;
     dim3 grid(p.n_split, p.batch * p.n_kv_heads);
     if (p.jensen == JENSEN_EXACT)
-        hipLaunchKernelGGL((decode_kernel<HD, BF16, true>), grid, dim3(kDThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<HD, BF16, true, PB>), grid, dim3(kDThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_kernel<HD, BF16, false>), grid, dim3(kDThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<HD, BF16, false, PB>), grid, dim3(kDThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
     return launch_combine(p, s);
@@ -600,7 +601,10 @@ void decode_plan(int batch, int n_kv_heads, int n_total, int *n_wg, int *wave_to
 hipError_t launch_decode(const AttnParams &p, hipStream_t s) {
     // only what decode_eligible admits is built
     if (p.dtype != DT_BF16) return hipErrorInvalidValue;
-    return p.head_dim == 64 ? launch_d<64>(p, s) : launch_d<128>(p, s);
+    // one packed segment at most (none: only current-chunk steps, which any instance walks)
+    const int pb = p.n_segs > 0 ? p.segs[0].bits : 2;
+    if (p.head_dim == 64) return pb == 2 ? launch_d<64, 2>(p, s) : hipErrorInvalidValue;
+    return pb == 4 ? launch_d<128, 4>(p, s) : launch_d<128, 2>(p, s);
 }
 
 }  // namespace kvq
