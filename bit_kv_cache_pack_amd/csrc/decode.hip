@@ -240,7 +240,7 @@ __device__ __forceinline__ float jensen_sum(const DCtx<HD, BF16> &cx, bool iso) 
     return acc;
 }
 
-template <int HD, bool BF16, bool EXACT, int PB>
+template <int HD, bool BF16, bool EXACT, int PB, bool CUR>
 __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const Step &st, const Step &nx,
                                              uint16_t *vt, const AttnParams &p, size_t bh) {
     typedef DGeo<HD> G;
@@ -248,7 +248,7 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
     typedef typename DCtx<HD, BF16>::vec vec;
     typedef __attribute__((ext_vector_type(4))) short s16x4;
     const int lane = threadIdx.x % kWave, j = lane / 16;
-    const bool packed = st.kind == ST_PACKED;
+    const bool packed = !CUR || st.kind == ST_PACKED;   // without CUR every step is packed
     const int bits = packed ? PB : 16;   // the launch's one packed segment has PB bits
     const int len = st.len;
     const bool nx_packed = nx.kind == ST_PACKED;
@@ -431,8 +431,9 @@ __device__ __forceinline__ void process_step(DCtx<HD, BF16> &cx, DSet &d, const 
 }
 
 // EXACT: the all-orders Jensen form, in its own instance (as in the chunk kernel). PB: the
-// bit-width of the launch's packed segment, one instance each.
-template <int HD, bool BF16, bool EXACT, int PB>
+// bit-width of the launch's packed segment, one instance each. CUR: the launch has a
+// current chunk (without it, INT2 instances hold no code for its steps).
+template <int HD, bool BF16, bool EXACT, int PB, bool CUR>
 __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     typedef DGeo<HD> G;
     typedef typename DCtx<HD, BF16>::vec vec;
@@ -497,7 +498,7 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
         load_v<HD, PB>(d, p, s0, bh);
     }
     while (s0.kind != ST_END) {
-        process_step<HD, BF16, EXACT, PB>(cx, d, s0, s1, vt, p, bh);
+        process_step<HD, BF16, EXACT, PB, CUR>(cx, d, s0, s1, vt, p, bh);
         s0 = s1;
         s1 = uniform(wk.next(p, tb, te));
     }
@@ -550,14 +551,14 @@ __global__ __launch_bounds__(kDThreads, 2) void decode_kernel(AttnParams p) {
     }
 }
 
-template <int HD, int PB>
+template <int HD, int PB, bool CUR>
 hipError_t launch_d(const AttnParams &p, hipStream_t s) {
     constexpr bool BF16 = true;
     dim3 grid(p.n_split, p.batch * p.n_kv_heads);
     if (p.jensen == JENSEN_EXACT)
-        hipLaunchKernelGGL((decode_kernel<HD, BF16, true, PB>), grid, dim3(kDThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<HD, BF16, true, PB, CUR>), grid, dim3(kDThreads), 0, s, p);
     else
-        hipLaunchKernelGGL((decode_kernel<HD, BF16, false, PB>), grid, dim3(kDThreads), 0, s, p);
+        hipLaunchKernelGGL((decode_kernel<HD, BF16, false, PB, CUR>), grid, dim3(kDThreads), 0, s, p);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || p.n_split == 1) return e;
     return launch_combine(p, s);
@@ -603,8 +604,14 @@ hipError_t launch_decode(const AttnParams &p, hipStream_t s) {
     if (p.dtype != DT_BF16) return hipErrorInvalidValue;
     // one packed segment at most (none: only current-chunk steps, which any instance walks)
     const int pb = p.n_segs > 0 ? p.segs[0].bits : 2;
-    if (p.head_dim == 64) return pb == 2 ? launch_d<64, 2>(p, s) : hipErrorInvalidValue;
-    return pb == 4 ? launch_d<128, 4>(p, s) : launch_d<128, 2>(p, s);
+    // INT2 without a current chunk in instances of their own (measured faster); INT4 keeps
+    // one instance (its specialized one measured slower)
+    if (p.head_dim == 64) {
+        if (pb != 2) return hipErrorInvalidValue;
+        return p.n_cur > 0 ? launch_d<64, 2, true>(p, s) : launch_d<64, 2, false>(p, s);
+    }
+    if (pb == 4) return launch_d<128, 4, true>(p, s);
+    return p.n_cur > 0 ? launch_d<128, 2, true>(p, s) : launch_d<128, 2, false>(p, s);
 }
 
 }  // namespace kvq
