@@ -281,7 +281,9 @@ kvq_status kvq_assign_windows(const kvq_window_args *args, void *stream);
  *            kvq_quantize_append, reported before anything is enqueued.
  * Errors: KVQ_ERR_ARG (nulls, shape mismatch, no tokens at all, n_q_heads not a
  * multiple of n_kv_heads), KVQ_ERR_UNSUPPORTED (dtypes, head_dim, bits, too many
- * segments, jensen not a kvq_jensen value), KVQ_ERR_WORKSPACE.
+ * segments, jensen not a kvq_jensen value, KVQ_JENSEN_EXACT with a segment that holds
+ * per-token K groups or a compensation basis, segments whose per-token K groups or
+ * compensation differ in kind, width or basis), KVQ_ERR_WORKSPACE.
  */
 typedef struct kvq_attn_args {
     const void *q;

@@ -148,6 +148,16 @@ def test_attention_segment_checks():
     assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_ARG
     a, arr = _attn(segs=[], n_cur=0)               # no tokens at all
     assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_ARG
+    # per-token K columns: the all-orders form is refused, and so are two segments whose
+    # extra columns differ in kind; the same segments pass the checks with the default form
+    tok = _seg(n_tokens=300, n_kgroups=3, k_group_channels=32)
+    a, arr = _attn(segs=[tok], jensen=3)
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_UNSUPPORTED
+    n = ctypes.c_size_t()
+    a, arr = _attn(segs=[tok], jensen=1)
+    assert kvq.lib().kvq_attention_workspace_size(ctypes.byref(a), ctypes.byref(n)) == kvq.OK
+    a, arr = _attn(segs=[tok, _seg(n_tokens=300, n_kgroups=3, k_group_channels=64)], jensen=1)
+    assert kvq.lib().kvq_chunk_attention(ctypes.byref(a), None) == kvq.ERR_UNSUPPORTED
 
 
 def test_workspace_size_and_check():
