@@ -15,13 +15,21 @@ def f32(t: torch.Tensor) -> np.ndarray:
 
 
 def make_pair(bits, elem, B, H, d, capacity, Gk, kgroup_capacity, k_group_channels=0, comp_basis=None):
-    """comp_basis: numpy float32 [H][d][r] (the low-rank compensation's basis)."""
-    gb = None if comp_basis is None else torch.from_numpy(np.ascontiguousarray(comp_basis, np.float32)).cuda()
+    """comp_basis: the low-rank compensation's basis [H][d][r], float32: numpy (copied to the
+    device for this segment), or a CUDA tensor (the device copy itself, which segments read in
+    one attention call share)."""
+    if comp_basis is None:
+        gb = ob = None
+    elif isinstance(comp_basis, torch.Tensor):
+        gb, ob = comp_basis, comp_basis.cpu().numpy()
+    else:
+        ob = np.ascontiguousarray(comp_basis, np.float32)
+        gb = torch.from_numpy(ob).cuda()
     g = kvq.Segment(bits, TORCH_DT[elem], B, H, d, capacity, k_group_tokens=Gk, kgroup_capacity=kgroup_capacity,
                     k_group_channels=k_group_channels, comp_basis=gb)
     o = oracle.new_segment(bits, elem, B, H, d, capacity=capacity, k_group_tokens=Gk,
                            kgroup_capacity=kgroup_capacity, k_group_channels=k_group_channels,
-                           comp_basis=comp_basis)
+                           comp_basis=ob)
     return g, o
 
 
