@@ -118,3 +118,31 @@ def bf16_half_ulp(x: np.ndarray) -> np.ndarray:
     """Half a bf16 ulp at |x| (the rounding error of writing x as bf16)."""
     ax = np.maximum(np.abs(x), 2.0 ** -126)
     return np.exp2(np.floor(np.log2(ax)) - 8)
+
+
+def window_case(nl, H, N, d, seed, dtype=torch.float16):
+    """Seeded keys [nl][H][N][d] and text queries [nl][d] for window scoring."""
+    rng = np.random.default_rng(seed)
+    k = torch.from_numpy(rng.standard_normal((nl, H, N, d)).astype(np.float32)).to(dtype)
+    t = torch.from_numpy(rng.standard_normal((nl, d)).astype(np.float32))
+    return k, t
+
+
+def check_windows(asg, k, t, N, window=32, pct=(10, 30)):
+    """Every layer's scores (4 ulp), bits, order, gather lists and class token counts
+    (bit-exact) against the oracle run on that layer alone; k [layers][H][N][d], t
+    [layers][d] on the CPU."""
+    W = -(-N // window)
+    n16, n4 = oracle.window_budget(W, *pct)
+    assert (asg.n_fp16, asg.n_int4) == (n16, n4)
+    score, bits, order = asg.score.cpu().numpy(), asg.bits.cpu().numpy(), asg.order.cpu().numpy()
+    groups, ct = asg.groups.cpu().numpy(), asg.class_tokens.cpu().numpy()
+    for layer in range(k.shape[0]):
+        osc = oracle.window_scores(f32(k[layer]), t[layer].numpy(), window)
+        ob, oo = oracle.assign_windows(osc, n16, n4)
+        og, oct_ = oracle.window_groups(ob, oo, N, window)
+        np.testing.assert_array_max_ulp(score[layer], osc, maxulp=4)
+        assert np.array_equal(bits[layer], ob), layer
+        assert np.array_equal(order[layer], oo), layer
+        assert np.array_equal(groups[layer], og), layer
+        assert np.array_equal(ct[layer], oct_), layer

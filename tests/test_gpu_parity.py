@@ -12,6 +12,7 @@ import torch
 import bit_kv_cache_pack_amd as kvq
 import oracle
 import workloads
+from parity_util import check_windows as _check_windows, window_case as _window_case
 from parity_util import (TORCH_DT, append_both, assert_segments_equal, bf16_half_ulp, f32, gpu_attention,
                          make_pair, oracle_attention)
 
@@ -177,32 +178,6 @@ def test_tiny_workload(jensen):
     oo, ol = oracle_attention(data["q"], [oseg], data["cur_k"], data["cur_v"], jensen=jensen)
     assert np.abs(go - oo).max() <= TOL
     assert np.abs(gl - ol).max() <= TOL
-
-
-def _window_case(nl, H, N, d, seed, dtype=torch.float16):
-    rng = np.random.default_rng(seed)
-    k = torch.from_numpy(rng.standard_normal((nl, H, N, d)).astype(np.float32)).to(dtype)
-    t = torch.from_numpy(rng.standard_normal((nl, d)).astype(np.float32))
-    return k, t
-
-
-def _check_windows(asg, k, t, N, window=32, pct=(10, 30)):
-    """Every layer's scores (4 ulp), bits, order, gather lists and class token counts
-    (bit-exact) against the oracle run on that layer alone."""
-    W = -(-N // window)
-    n16, n4 = oracle.window_budget(W, *pct)
-    assert (asg.n_fp16, asg.n_int4) == (n16, n4)
-    score, bits, order = asg.score.cpu().numpy(), asg.bits.cpu().numpy(), asg.order.cpu().numpy()
-    groups, ct = asg.groups.cpu().numpy(), asg.class_tokens.cpu().numpy()
-    for layer in range(k.shape[0]):
-        osc = oracle.window_scores(f32(k[layer]), t[layer].numpy(), window)
-        ob, oo = oracle.assign_windows(osc, n16, n4)
-        og, oct_ = oracle.window_groups(ob, oo, N, window)
-        np.testing.assert_array_max_ulp(score[layer], osc, maxulp=4)
-        assert np.array_equal(bits[layer], ob), layer
-        assert np.array_equal(order[layer], oo), layer
-        assert np.array_equal(groups[layer], og), layer
-        assert np.array_equal(ct[layer], oct_), layer
 
 
 def test_windows_scores_and_assignment():

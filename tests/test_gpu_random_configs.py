@@ -121,3 +121,53 @@ def test_random_configuration_extras(case):
         assert_segments_equal(gsegs[fused], osegs[fused])
     err, lerr = np.abs(go - oo).max(), np.abs(gl - ol).max()
     assert err <= TOL and lerr <= TOL, (c, aug, kgc, fused, err, lerr)
+
+
+@pytest.mark.parametrize("case", range(32))
+def test_random_appends(case):
+    """Quantize-appends of random shape against the oracle, bit for bit: INT2 or INT4, head
+    dim 64 or 128, fp32/bf16/fp16 sources into bf16/fp16 caches, K-groups of 32 to 256
+    tokens, two or three appends of ragged lengths (1 to 700 tokens), contiguous or gathered
+    from random windows (any order, ragged window lengths, a repeated window)."""
+    rng = np.random.default_rng(9000 + case)
+    bits, d = int(rng.choice([2, 4])), int(rng.choice([64, 128]))
+    elem = str(rng.choice(["bf16", "f16"]))
+    src = str(rng.choice(["f32", elem]))
+    B, H, Gk = int(rng.choice([1, 2])), int(rng.choice([1, 2, 3])), int(rng.choice([32, 64, 128, 256]))
+    plans = []
+    for _ in range(int(rng.integers(2, 4))):
+        n = int(rng.integers(1, 701))
+        if rng.random() < 0.4:
+            wl = int(rng.choice([16, 32, Gk]))
+            starts = rng.permutation(np.arange(0, max(n - 1, 1), wl))[: int(rng.integers(1, 12))]
+            groups = [(int(s0), int(min(wl, n - s0))) for s0 in starts]
+            if len(groups) > 1:
+                groups.append(groups[0])        # a window taken twice
+            plans.append((n, [(s0, min(ln, Gk)) for s0, ln in groups]))
+        else:
+            plans.append((n, None))
+    cap = sum(n if g is None else sum(ln for _, ln in g) for n, g in plans)
+    kcap = sum(-(-n // Gk) if g is None else len(g) for n, g in plans)
+    gseg, oseg = make_pair(bits, elem, B, H, d, capacity=cap, Gk=Gk, kgroup_capacity=kcap)
+    for n, groups in plans:
+        k = _rand(rng, (B, H, n, d), src, 3.0)
+        v = _rand(rng, (B, H, n, d), src)
+        append_both(gseg, oseg, k, v, groups=groups)
+        assert_segments_equal(gseg, oseg)
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_window_assignments(case):
+    """Window scores, bit-widths, order, gather lists and class token counts for random
+    token counts (1 to 9,000), KV heads, head dims, layers and budget percentages (the class
+    boundaries move with them), against the oracle."""
+    from parity_util import check_windows, window_case
+    rng = np.random.default_rng(9500 + case)
+    nl, H, d = int(rng.integers(1, 4)), int(rng.integers(1, 4)), int(rng.choice([64, 128]))
+    N = int(rng.integers(1, 9001))
+    p16 = int(rng.integers(0, 31))
+    p4 = int(rng.integers(0, 101 - p16))
+    k, t = window_case(nl, H, N, d, 9500 + case, dtype=TORCH_DT[str(rng.choice(["f16", "bf16"]))])
+    asg = kvq.assign_windows(k.cuda(), t.cuda(), p16, p4)
+    torch.cuda.synchronize()
+    check_windows(asg, k, t, N, pct=(p16, p4))
