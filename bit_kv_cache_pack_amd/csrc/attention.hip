@@ -1324,24 +1324,36 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
 // the attention launch) takes the row block holding position y quota if share y is the
 // first to start in it; the row block's pieces are in shares w0..w1. One pass over the
 // pieces with a running maximum; a thread merges 8 channels of one row (one 16-byte load
-// of mantissas per piece, and the piece row's m, l and exponent).
+// of mantissas per piece, and the piece row's m, l and exponent). When the block's live
+// rows leave threads over (few rows, e.g. decode-shaped queries cut into many pieces), NG
+// groups of threads take every NG-th piece each, and their partial merges are combined
+// through LDS, the same log-sum-exp way.
 template <int HD>
 __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     constexpr int CPT = 8;          // channels per thread
     constexpr int TPR = HD / CPT;   // threads per row
     constexpr int RPB = 256 / TPR;  // rows per block
+    constexpr int MAXG = 8;         // piece groups at most
+    __shared__ float part[256][CPT + 2];   // a group's acc, then its M and L
     const int64_t U = p.quota, Np = p.tok_pad;
     const int64_t y = blockIdx.x;
     const int64_t rb = y * U / Np;
     if ((rb * Np + U - 1) / U != y) return;
     const int64_t w0 = rb * Np / U, w1 = ((rb + 1) * Np - 1) / U;
     if (w1 == w0) return;
-    const int r = blockIdx.y * RPB + threadIdx.x / TPR, c = (threadIdx.x % TPR) * CPT;
     const int gqa = p.n_q_heads / p.n_kv_heads;
     const int rows = gqa * p.n_q;
     const int bhi = (int)(rb / p.n_rb), rbi = (int)(rb - (int64_t)bhi * p.n_rb);
+    const int row_base = rbi * BM + blockIdx.y * RPB;
+    const int live = min(RPB, rows - row_base);   // live rows of this block (uniform)
+    if (live <= 0) return;
+    const int need = live * TPR;                  // threads one pass over the pieces needs
+    int NG = 1;
+    while (NG < MAXG && 2 * NG * need <= 256) NG *= 2;
+    const int gi = threadIdx.x / need, li = threadIdx.x % need;
+    const bool active = gi < NG;
+    const int r = blockIdx.y * RPB + li / TPR, c = (li % TPR) * CPT;
     const int row = rbi * BM + r;
-    if (row >= rows) return;
     const int b = bhi / p.n_kv_heads, h = bhi % p.n_kv_heads;
     const size_t qrow = ((size_t)b * p.n_q_heads + h * gqa + row / p.n_q) * p.n_q + row % p.n_q;
     const uint8_t *base = reinterpret_cast<const uint8_t *>(p.partial);
@@ -1349,41 +1361,70 @@ __global__ __launch_bounds__(256) void piece_combine_kernel(AttnParams p) {
     float acc[CPT];
 #pragma unroll
     for (int i = 0; i < CPT; ++i) acc[i] = 0.f;
-    // pieces in groups of 8 whose loads are in flight together (a row block of a few rows can
-    // be cut into many pieces)
+    // pieces in batches of 8 whose loads are in flight together: group gi takes pieces
+    // w0 + gi, w0 + gi + NG, ...
     constexpr int NP = 8;
-    for (int64_t w = w0; w <= w1; w += NP) {
-        u32x4 o[NP];
-        f32x4 t[NP];   // m, l, exponent bits, pad
+    if (active) {
+        for (int64_t w = w0 + gi; w <= w1; w += (int64_t)NP * NG) {
+            u32x4 o[NP];
+            f32x4 t[NP];   // m, l, exponent bits, pad
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const int64_t ww = w + k;
-            if (ww > w1) {   // past the last piece (uniform over the workgroup): no load
-                o[k] = u32x4{0u, 0u, 0u, 0u};
-                t[k] = f32x4{-__builtin_inff(), 0.f, 0.f, 0.f};
-                continue;
+            for (int k = 0; k < NP; ++k) {
+                const int64_t ww = w + (int64_t)k * NG;
+                if (ww > w1) {   // past the last piece (uniform over the group): no load
+                    o[k] = u32x4{0u, 0u, 0u, 0u};
+                    t[k] = f32x4{-__builtin_inff(), 0.f, 0.f, 0.f};
+                    continue;
+                }
+                // the row block's piece in share ww is that share's first piece iff the share starts in it
+                const uint8_t *pp =
+                    base + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * PieceRow<HD>::bytes;
+                o[k] = *reinterpret_cast<const u32x4 *>(pp + 2 * c);
+                t[k] = *reinterpret_cast<const f32x4 *>(pp + 2 * HD);
             }
-            // the row block's piece in share ww is that share's first piece iff the share starts in it
-            const uint8_t *pp = base + (((size_t)ww * 2 + (ww * U >= rb * Np ? 0 : 1)) * BM + r) * PieceRow<HD>::bytes;
-            o[k] = *reinterpret_cast<const u32x4 *>(pp + 2 * c);
-            t[k] = *reinterpret_cast<const f32x4 *>(pp + 2 * HD);
-        }
 #pragma unroll
-        for (int k = 0; k < NP; ++k) {
-            const float mk = t[k][0];
-            if (mk == -__builtin_inff()) continue;   // past the last piece, or a piece past the last token
-            const float mn = fmaxf(M, mk);
-            const float sa = exp2f(M - mn), sb = exp2f(mk - mn);
-            const float so = ldexpf(sb, __float_as_int(t[k][2]) - 15);   // mantissa weight
+            for (int k = 0; k < NP; ++k) {
+                const float mk = t[k][0];
+                if (mk == -__builtin_inff()) continue;   // past the last piece, or a piece past the last token
+                const float mn = fmaxf(M, mk);
+                const float sa = exp2f(M - mn), sb = exp2f(mk - mn);
+                const float so = ldexpf(sb, __float_as_int(t[k][2]) - 15);   // mantissa weight
 #pragma unroll
-            for (int i = 0; i < CPT; ++i) {
-                const uint32_t wd = o[k][i / 2];
-                const float mv = (float)(int16_t)(i % 2 ? wd >> 16 : wd & 0xffffu);
-                acc[i] = acc[i] * sa + mv * so;
+                for (int i = 0; i < CPT; ++i) {
+                    const uint32_t wd = o[k][i / 2];
+                    const float mv = (float)(int16_t)(i % 2 ? wd >> 16 : wd & 0xffffu);
+                    acc[i] = acc[i] * sa + mv * so;
+                }
+                L = L * sa + t[k][1] * sb;
+                M = mn;
             }
-            L = L * sa + t[k][1] * sb;
-            M = mn;
         }
+    }
+    if (NG > 1) {   // uniform: the groups' partial merges meet in LDS
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) part[threadIdx.x][i] = acc[i];
+            part[threadIdx.x][CPT] = M;
+            part[threadIdx.x][CPT + 1] = L;
+        }
+        __syncthreads();
+        if (gi != 0) return;
+        float Mt = M;
+        for (int g = 1; g < NG; ++g) Mt = fmaxf(Mt, part[g * need + li][CPT]);
+        const float s0 = exp2f(M - Mt);   // a group without pieces has M = -inf: weight 0
+        L *= s0;
+#pragma unroll
+        for (int i = 0; i < CPT; ++i) acc[i] *= s0;
+        for (int g = 1; g < NG; ++g) {
+            const float *pg = part[g * need + li];
+            const float sg = exp2f(pg[CPT] - Mt);
+            L += pg[CPT + 1] * sg;
+#pragma unroll
+            for (int i = 0; i < CPT; ++i) acc[i] += pg[i] * sg;
+        }
+        M = Mt;
+    } else if (!active) {
+        return;   // threads past the live rows (one group: no barrier to reach)
     }
     const float inv = 1.0f / L;
 #pragma unroll
