@@ -187,6 +187,40 @@ def test_windows_scores_and_assignment():
     _check_windows(asg, k, t, 1000)
 
 
+def test_windows_at_the_window_limit():
+    """16,384 windows in one layer, the most kvq_assign_windows takes: the ranking's widest
+    grid (256 workgroups, every wave counting over 4,096 windows) and the list pass over 16
+    chunks, against the oracle (its O(W^2) ranking included)."""
+    N = 16384 * 32 - 5
+    k, t = _window_case(1, 1, N, 64, 77)
+    asg = kvq.assign_windows(k.cuda(), t.cuda(), 10, 30)
+    torch.cuda.synchronize()
+    _check_windows(asg, k, t, N)
+
+
+def test_attention_eight_segments():
+    """The most segments one attention call takes (8): INT2, INT4 and raw segments of ragged
+    sizes and K-group sizes, with a current chunk, chunk-shaped (several row blocks) and
+    decode-shaped (one query per head), every Jensen form, against the oracle."""
+    B, Hq, Hkv, d = 1, 4, 2, 128
+    specs = [(2, 128, 700), (4, 64, 333), (16, 32, 95), (2, 32, 1), (4, 128, 1200), (2, 64, 257), (16, 32, 40),
+             (2, 128, 129)]
+    gsegs, osegs = [], []
+    for i, (bits, Gk, n) in enumerate(specs):
+        gseg, oseg = make_pair(bits, "bf16", B, Hkv, d, capacity=n, Gk=Gk, kgroup_capacity=-(-n // Gk))
+        append_both(gseg, oseg, _rand((B, Hkv, n, d), "bf16", 400 + i, 2.0), _rand((B, Hkv, n, d), "bf16", 420 + i))
+        gsegs.append(gseg)
+        osegs.append(oseg)
+    kc = _rand((B, Hkv, 77, d), "bf16", 440, 2.0)
+    vc = _rand((B, Hkv, 77, d), "bf16", 441)
+    for n_q, jensen in ((300, 1), (1, 2), (300, 3), (1, 0)):
+        q = _rand((B, Hq, n_q, d), "bf16", 442 + n_q + jensen)
+        go, gl = gpu_attention(q, gsegs, kc, vc, n_kv_heads=Hkv, jensen=jensen)
+        oo, ol = oracle_attention(q, osegs, kc, vc, n_kv_heads=Hkv, jensen=jensen)
+        assert np.abs(go - oo).max() <= TOL, (n_q, jensen)
+        assert np.abs(gl - ol).max() <= TOL, (n_q, jensen)
+
+
 @pytest.mark.parametrize("N", [20, 32, 64, 2080, 2081, 4129])
 def test_windows_rank_boundaries(N):
     """Window counts at the ranking's edges: one window (20, 32: nothing to rank), two, 65
