@@ -221,6 +221,25 @@ def test_attention_eight_segments():
         assert np.abs(gl - ol).max() <= TOL, (n_q, jensen)
 
 
+@pytest.mark.parametrize("n_q", [1, 260])
+def test_attention_with_empty_segments(n_q):
+    """Empty segments in the list, as a WindowQuant budget with an empty class leaves them
+    (here the INT4 one, and an empty raw one): they hold no token and change nothing."""
+    B, Hq, Hkv, d = 1, 4, 2, 64
+    gsegs, osegs = [], []
+    for i, (bits, n) in enumerate(((16, 0), (4, 0), (2, 333), (16, 45))):
+        gseg, oseg = make_pair(bits, "f16", B, Hkv, d, capacity=max(n, 32), Gk=32, kgroup_capacity=max(-(-n // 32), 1))
+        if n:
+            append_both(gseg, oseg, _rand((B, Hkv, n, d), "f16", 460 + i, 2.0), _rand((B, Hkv, n, d), "f16", 470 + i))
+        gsegs.append(gseg)
+        osegs.append(oseg)
+    q = _rand((B, Hq, n_q, d), "f16", 480 + n_q)
+    go, gl = gpu_attention(q, gsegs, n_kv_heads=Hkv, jensen=1)
+    oo, ol = oracle_attention(q, osegs, n_kv_heads=Hkv, jensen=1)
+    assert np.abs(go - oo).max() <= TOL
+    assert np.abs(gl - ol).max() <= TOL
+
+
 @pytest.mark.parametrize("N", [20, 32, 64, 2080, 2081, 4129])
 def test_windows_rank_boundaries(N):
     """Window counts at the ranking's edges: one window (20, 32: nothing to rank), two, 65
