@@ -118,9 +118,12 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _stream(stream) -> Optional[int]:
+def _stream(stream, t: torch.Tensor):
+    """The stream to launch on: ``stream`` (a torch stream or a raw handle), or torch's
+    current stream on t's device, read as the raw handle (building a torch stream object
+    costs more host time than the launch itself)."""
     if stream is None:
-        stream = torch.cuda.current_stream()
+        return ctypes.c_void_p(torch._C._cuda_getCurrentRawStream(t.device.index))
     return ctypes.c_void_p(stream.cuda_stream) if hasattr(stream, "cuda_stream") else stream
 
 
@@ -209,7 +212,7 @@ def quantize_append(segment: Segment, k_src: torch.Tensor, v_src: torch.Tensor, 
             n_new = k_src.shape[2]
     args = KvqAppendArgs(ctypes.pointer(segment.desc), _ptr(k_src), _ptr(v_src), _TORCH_DT[k_src.dtype],
                          k_src.shape[2], int(n_new), _ptr(src_groups), n_groups)
-    _check(lib().kvq_quantize_append(ctypes.byref(args), _stream(stream)), "kvq_quantize_append")
+    _check(lib().kvq_quantize_append(ctypes.byref(args), _stream(stream, k_src)), "kvq_quantize_append")
 
 
 def window_budget(n_windows: int, pct_fp16: int, pct_int4: int):
@@ -268,7 +271,7 @@ def assign_windows(k: torch.Tensor, text_query: torch.Tensor, pct_fp16: int, pct
     args = KvqWindowArgs(_ptr(k), _TORCH_DT[k.dtype], nl, H, d, N, window, _ptr(text_query), int(pct_fp16),
                          int(pct_int4), _ptr(out.bits), _ptr(out.order), _ptr(out.score), _ptr(out.groups),
                          _ptr(out.class_tokens))
-    _check(lib().kvq_assign_windows(ctypes.byref(args), _stream(stream)), "kvq_assign_windows")
+    _check(lib().kvq_assign_windows(ctypes.byref(args), _stream(stream, k)), "kvq_assign_windows")
     return out
 
 
@@ -325,7 +328,7 @@ def chunk_attention(q: torch.Tensor, segments: Sequence[Segment], k_cur: Optiona
             workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     a, arr = _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out,
                         _TORCH_DT[out.dtype], lse, workspace, append_to)
-    _check(lib().kvq_chunk_attention(ctypes.byref(a), _stream(stream)), "kvq_chunk_attention")
+    _check(lib().kvq_chunk_attention(ctypes.byref(a), _stream(stream, q)), "kvq_chunk_attention")
     return out
 
 
@@ -346,7 +349,7 @@ def chunk_attention_noalloc(q: torch.Tensor, segments: Sequence[Segment], out: t
         n_kv_heads = k_cur.shape[1]
     a, arr = _attn_args(q, segments, k_cur, v_cur, n_kv_heads, softmax_scale, jensen, out,
                         _TORCH_DT[out.dtype], lse, None)
-    _check(lib().kvq_chunk_attention_noalloc(ctypes.byref(a), _stream(stream)), "kvq_chunk_attention_noalloc")
+    _check(lib().kvq_chunk_attention_noalloc(ctypes.byref(a), _stream(stream, q)), "kvq_chunk_attention_noalloc")
     return out
 
 
@@ -354,4 +357,4 @@ def probe_hbm_read(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
     """Enqueue one streaming read of ``buf`` (a measurement aid: kvq_probe_hbm_read)."""
     _dev(buf, "buf"); _dev(sink, "sink")
     nbytes = buf.numel() * buf.element_size()
-    _check(lib().kvq_probe_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream)), "kvq_probe_hbm_read")
+    _check(lib().kvq_probe_hbm_read(_ptr(buf), nbytes, _ptr(sink), _stream(stream, buf)), "kvq_probe_hbm_read")
