@@ -16,7 +16,8 @@
 //
 // A workgroup quantizes one K-group (<= k_group_tokens tokens) of one (batch, head):
 // the K statistics run down the group's tokens per channel, the V statistics across
-// each token's 32-channel runs.
+// each token's 32-channel runs (quant_group); the append kernel gives the keys and the
+// values of a K-group to two workgroups (quant_group_part).
 #pragma once
 
 #include <type_traits>
@@ -305,6 +306,54 @@ __device__ __forceinline__ uint32_t k_row(const float (&x)[8], int r, int len, i
     return kbits;
 }
 
+// The K-group's per-channel step/zero from each thread's running extremes (mn, mx over
+// its rows of the thread's 8 channels): the extremes are combined across the lanes and
+// waves that hold the same channels, the meta is stored by the first row pass, and the
+// reciprocals of the steps are returned for fast_code. Called by every thread of the
+// workgroup in uniform control flow; holds a barrier.
+template <int HD, int BITS, int NT>
+__device__ __forceinline__ void k_group_quant(const QuantAppendParams &p, float (&mn)[8], float (&mx)[8], int g,
+                                              size_t bh, Quant (&kq)[8], float (&kinv)[8]) {
+    constexpr int L = (1 << BITS) - 1;
+    constexpr int CC = HD / 8;
+    const int tid = threadIdx.x;
+    const int cc = tid % CC, rp = tid / CC;
+    const int lane = tid % kWave, wave = tid / kWave;
+    // lanes holding the same channels differ in the bits above log2(CC)
+#pragma unroll
+    for (int o = CC; o < kWave; o <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            mn[i] = fminf(mn[i], __shfl_xor(mn[i], o));
+            mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o));
+        }
+    }
+    __shared__ float s_mn[NT / kWave][HD], s_mx[NT / kWave][HD];
+    if (lane < CC) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { s_mn[wave][cc * 8 + i] = mn[i]; s_mx[wave][cc * 8 + i] = mx[i]; }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        float a = s_mn[0][cc * 8 + i], z = s_mx[0][cc * 8 + i];
+#pragma unroll
+        for (int w = 1; w < NT / kWave; ++w) {
+            a = fminf(a, s_mn[w][cc * 8 + i]);
+            z = fmaxf(z, s_mx[w][cc * 8 + i]);
+        }
+        kq[i].set(a, z, L);
+    }
+    if (rp == 0) {
+        uint32_t *km = reinterpret_cast<uint32_t *>(p.k_meta) +
+                       (bh * p.kgroup_capacity + p.n_kgroups + g) * HD + cc * 8;
+        *reinterpret_cast<u32x4 *>(km) = u32x4{kq[0].meta, kq[1].meta, kq[2].meta, kq[3].meta};
+        *reinterpret_cast<u32x4 *>(km + 4) = u32x4{kq[4].meta, kq[5].meta, kq[6].meta, kq[7].meta};
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) kinv[i] = kq[i].inv();
+}
+
 // Per-token K groups: no K-group statistics; rows are coded one after another, keys as
 // values are, with the group width of the segment.
 template <typename T, int HD, int BITS, int NT, int GW>
@@ -342,7 +391,6 @@ __device__ __forceinline__ void token_group_rows(const T *ks, const T *vs, int l
 // can occur, so that those paths take no code or registers there).
 template <typename T, int HD, int BITS, int NT, bool EXT = true>
 __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, int h, int b, int n_groups) {
-    constexpr int L = (1 << BITS) - 1;
     constexpr int CC = HD / 8;            // 8-channel chunks per token row
     constexpr int RP = NT / CC;           // rows processed per pass
     constexpr int WPR = HD * BITS / 32;   // packed words per token row
@@ -350,7 +398,6 @@ __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, i
     typedef typename Src<T>::Raw Raw;
     const int tid = threadIdx.x;
     const int cc = tid % CC, rp = tid / CC;
-    const int lane = tid % kWave, wave = tid / kWave;
 
     // ---- which source tokens, and where they land ----
     int src0, len, dst0;
@@ -442,43 +489,9 @@ __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, i
             }
         }
     }
-    // lanes holding the same channels differ in the bits above log2(CC)
-#pragma unroll
-    for (int o = CC; o < kWave; o <<= 1) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            mn[i] = fminf(mn[i], __shfl_xor(mn[i], o));
-            mx[i] = fmaxf(mx[i], __shfl_xor(mx[i], o));
-        }
-    }
-    __shared__ float s_mn[NT / kWave][HD], s_mx[NT / kWave][HD];
-    if (lane < CC) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) { s_mn[wave][cc * 8 + i] = mn[i]; s_mx[wave][cc * 8 + i] = mx[i]; }
-    }
-    __syncthreads();
     Quant kq[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-        float a = s_mn[0][cc * 8 + i], z = s_mx[0][cc * 8 + i];
-#pragma unroll
-        for (int w = 1; w < NT / kWave; ++w) {
-            a = fminf(a, s_mn[w][cc * 8 + i]);
-            z = fmaxf(z, s_mx[w][cc * 8 + i]);
-        }
-        kq[i].set(a, z, L);
-    }
-    if (rp == 0) {
-        uint32_t *km = reinterpret_cast<uint32_t *>(p.k_meta) +
-                       (bh * p.kgroup_capacity + p.n_kgroups + g) * HD + cc * 8;
-        u32x4 m0 = {kq[0].meta, kq[1].meta, kq[2].meta, kq[3].meta};
-        u32x4 m1 = {kq[4].meta, kq[5].meta, kq[6].meta, kq[7].meta};
-        *reinterpret_cast<u32x4 *>(km) = m0;
-        *reinterpret_cast<u32x4 *>(km + 4) = m1;
-    }
     float kinv[8];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) kinv[i] = kq[i].inv();
+    k_group_quant<HD, BITS, NT>(p, mn, mx, g, bh, kq, kinv);
 
     // ---- codes: the remaining V rows, then K ----
     // Batches of rows as above. The four lanes of a quad hold one row (CC is a multiple of
@@ -522,6 +535,127 @@ __device__ __forceinline__ void quant_group(const QuantAppendParams &p, int g, i
                 const uint32_t kb = k_row<HD, BITS>(x, b0 + u * RP + rp, len, cc, kq, kinv, kcodes);
                 if (rank > 0)
                     comp_row<HD, BITS, kBf16Elem>(x, kb, b0 + u * RP + rp, len, cc, kq, u_lds, rank, comp);
+            }
+        }
+    }
+}
+
+
+// The same K-group's work in two halves for two workgroups, so that the append launch has
+// twice as many, half as long: PART 1 takes the keys (statistics, step/zero, codes, the
+// group-table entries and the compensation), PART 2 the values (a group per token and 32
+// channels). The arithmetic is quant_group's, element for element; only the split differs.
+// Plain per-channel K groups only (per-token K groups take quant_group). Every thread of
+// the workgroup calls it, in uniform control flow.
+template <typename T, int HD, int BITS, int NT, int PART>
+__device__ __forceinline__ void quant_group_part(const QuantAppendParams &p, int g, int h, int b, int n_groups) {
+    constexpr int CC = HD / 8;
+    constexpr int RP = NT / CC;
+    constexpr int WPR = HD * BITS / 32;
+    constexpr int VG = 32;
+    typedef typename Src<T>::Raw Raw;
+    const int tid = threadIdx.x;
+    const int cc = tid % CC, rp = tid / CC;
+    int src0, len, dst0;
+    group_span<NT>(p, g, src0, len, dst0);
+    if (PART == 1 && b == 0 && h == 0 && tid == 0) {
+        p.kgroup_start[p.n_kgroups + g] = p.n_tokens + min(dst0, p.n_new);
+        if (g == n_groups - 1) p.kgroup_start[p.n_kgroups + g + 1] = p.n_tokens + p.n_new;
+    }
+    if (len <= 0) return;  // only reachable with a malformed gather list
+    const size_t bh = (size_t)b * p.n_kv_heads + h;
+
+    if constexpr (PART == 2) {
+        // values: rows in batches whose loads are all in flight together (rows past the
+        // group end repeat its last row and are not stored)
+        const T *vs = reinterpret_cast<const T *>(p.v_src) + (bh * p.src_tokens + src0) * HD + cc * 8;
+        uint32_t *vcodes = reinterpret_cast<uint32_t *>(p.v_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
+        uint32_t *vm_base =
+            reinterpret_cast<uint32_t *>(p.v_meta) + (bh * p.capacity + p.n_tokens + dst0) * (HD / VG);
+        for (int b0 = 0; b0 < len; b0 += kBatch1 * RP) {
+            Raw vraw[kBatch1];
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u) vraw[u] = Src<T>::load(vs + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u) {
+                float y[8];
+                Src<T>::unpack(vraw[u], y);
+                v_row<HD, BITS>(y, b0 + u * RP + rp, len, cc, vcodes, vm_base);
+            }
+        }
+    } else {
+        // keys: extremes, step/zero, codes, as quant_group without its value rows
+        const T *ks = reinterpret_cast<const T *>(p.k_src) + (bh * p.src_tokens + src0) * HD + cc * 8;
+        uint32_t *kcodes = reinterpret_cast<uint32_t *>(p.k_dst) + (bh * p.capacity + p.n_tokens + dst0) * WPR;
+        __shared__ float u_lds[8 * HD];
+        const int rank = p.comp_rank;
+        if (rank > 0) {
+            const float *U = p.comp_basis + (size_t)h * HD * rank;
+            for (int i = tid; i < HD * rank; i += NT) u_lds[(i % rank) * HD + i / rank] = U[i];
+        }
+        uint16_t *comp = rank > 0 ? reinterpret_cast<uint16_t *>(p.k_comp) + (bh * p.capacity + p.n_tokens + dst0) * 8
+                                  : nullptr;
+        constexpr bool kBf16Elem = std::is_same<T, __bf16>::value;
+        const bool resident = sizeof(Raw) == 16 && len <= kBatch1 * RP;
+        float mn[8], mx[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) { mn[i] = __builtin_inff(); mx[i] = -__builtin_inff(); }
+        Raw kres[kBatch1];
+        if (resident) {
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u)
+                if (u * RP < len) kres[u] = Src<T>::load(ks + (size_t)min(u * RP + rp, len - 1) * HD);
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u) {
+                if (u * RP < len) {
+                    float x[8];
+                    Src<T>::unpack(kres[u], x);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+                }
+            }
+        } else {
+            for (int b0 = 0; b0 < len; b0 += kBatch1 * RP) {
+                Raw raw[kBatch1];
+#pragma unroll
+                for (int u = 0; u < kBatch1; ++u)
+                    raw[u] = Src<T>::load(ks + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+#pragma unroll
+                for (int u = 0; u < kBatch1; ++u) {
+                    float x[8];
+                    Src<T>::unpack(raw[u], x);
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) { mn[i] = fminf(mn[i], x[i]); mx[i] = fmaxf(mx[i], x[i]); }
+                }
+            }
+        }
+        Quant kq[8];
+        float kinv[8];
+        k_group_quant<HD, BITS, NT>(p, mn, mx, g, bh, kq, kinv);
+        if (resident) {
+#pragma unroll
+            for (int u = 0; u < kBatch1; ++u) {
+                if (u * RP < len) {
+                    float x[8];
+                    Src<T>::unpack(kres[u], x);
+                    const uint32_t kb = k_row<HD, BITS>(x, u * RP + rp, len, cc, kq, kinv, kcodes);
+                    if (rank > 0) comp_row<HD, BITS, kBf16Elem>(x, kb, u * RP + rp, len, cc, kq, u_lds, rank, comp);
+                }
+            }
+        } else {
+            for (int b0 = 0; b0 < len; b0 += kBatch2 * RP) {
+                Raw kraw[kBatch2];
+#pragma unroll
+                for (int u = 0; u < kBatch2; ++u)
+                    kraw[u] = Src<T>::load(ks + (size_t)min(b0 + u * RP + rp, len - 1) * HD);
+#pragma unroll
+                for (int u = 0; u < kBatch2; ++u) {
+                    float x[8];
+                    Src<T>::unpack(kraw[u], x);
+                    const uint32_t kb = k_row<HD, BITS>(x, b0 + u * RP + rp, len, cc, kq, kinv, kcodes);
+                    if (rank > 0)
+                        comp_row<HD, BITS, kBf16Elem>(x, kb, b0 + u * RP + rp, len, cc, kq, u_lds, rank, comp);
+                }
             }
         }
     }
