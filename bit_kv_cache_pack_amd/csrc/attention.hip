@@ -1116,14 +1116,15 @@ __global__ __launch_bounds__(kThreads, 1) void attention_kernel(AttnParams p) {
     // cut into pieces at row-block ends; a piece that is a whole row block writes the
     // output, any other one of the two partial slots of its workgroup (0: the share's
     // first piece, 1: its last).
-    // With one row block per workgroup, the row blocks of a head go to one XCD: workgroups
-    // are dispatched to the 8 XCDs in turn (workgroup i on XCD i % 8), so workgroup i takes
-    // share (i % 8) q + i / 8 (q = shares / 8). The row blocks of a head, which read the same
-    // K/V stream in the same order at about the same time, then share that XCD's L2
-    // (long rollout: 5.8x -> 1.65x the algorithmic HBM bytes, same time). Equal shares cut
-    // row blocks at different tokens and keep the plain order.
+    // Consecutive shares (the row blocks of a head, in order) go to one XCD: workgroups are
+    // dispatched to the 8 XCDs in turn (workgroup i on XCD i % 8), so workgroup i takes
+    // share (i % 8) q + i / 8 (q = shares / 8; the last shares map to themselves). The row
+    // blocks of a head read the same K/V stream at about the same time and then share that
+    // XCD's L2 (HBM bytes per launch: long rollout 5.8x -> 1.66x the algorithmic bytes,
+    // video chunk 11.2x -> 7.0x; the same time). Partial slots and the piece merge count
+    // in shares.
     int share = blockIdx.x;
-    if (p.quota == p.tok_pad) {
+    {
         const int q8 = p.n_attn_wg / 8;
         if (share < 8 * q8) share = (share % 8) * q8 + share / 8;
     }
