@@ -12,16 +12,19 @@ using namespace qz;
 
 constexpr int kThreads = 256;
 
-// Per-token K groups: one workgroup per (K-group, KV head, batch) takes keys and values.
+// Per-token K groups, and K-groups of fewer than 64 tokens: one workgroup per (K-group,
+// KV head, batch) takes keys and values.
 template <typename T, int HD, int BITS>
 __global__ __launch_bounds__(kThreads) void quant_append_kernel(QuantAppendParams p) {
     quant_group<T, HD, BITS, kThreads>(p, blockIdx.x, blockIdx.y, blockIdx.z, gridDim.x);
 }
 
-// Per-channel K groups: blockIdx.x < n_groups takes the keys of K-group blockIdx.x, the
-// rest the values of K-group blockIdx.x - n_groups. Twice the workgroups of half the work
-// each: measured on the long-rollout chunk (40 heads x 4,680 tokens) 30.4 against 36.5 us,
-// on the video chunk (12 heads) 12.5 against 16.1 us.
+// Per-channel K groups of 64 tokens or more: blockIdx.x < n_groups takes the keys of
+// K-group blockIdx.x, the rest the values of K-group blockIdx.x - n_groups. Twice the
+// workgroups of half the work each: measured on the long-rollout chunk (40 heads x 4,680
+// tokens) 30.4 against 36.5 us, on the video chunk (12 heads) 12.5 against 16.1 us. For
+// 32-token groups (WindowQuant windows, gathered) the halves are too small to pay for
+// the extra workgroups: 40.8 against 34.4 us for the three gathered appends of a step.
 template <typename T, int HD, int BITS>
 __global__ __launch_bounds__(kThreads) void quant_split_kernel(QuantAppendParams p) {
     const int ng = gridDim.x / 2;
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void raw_append_kernel(QuantAppendParams 
 template <typename T, int HD>
 hipError_t launch_t(const QuantAppendParams &p, int bits, int n_groups, hipStream_t s) {
     dim3 grid(n_groups, p.n_kv_heads, p.batch);
-    if (bits != 16 && p.k_group_channels == 0) {
+    if (bits != 16 && p.k_group_channels == 0 && p.k_group_tokens >= 64) {
         const dim3 split(2 * n_groups, p.n_kv_heads, p.batch);
         if (bits == 2)
             hipLaunchKernelGGL((quant_split_kernel<T, HD, 2>), split, dim3(kThreads), 0, s, p);
