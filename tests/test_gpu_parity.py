@@ -166,6 +166,17 @@ def test_attention_whole_row_blocks_half_outputs(out_dtype):
     assert np.abs(gl - ol).max() <= TOL
 
 
+def test_attention_whole_row_blocks_share_order_tail():
+    """250 row blocks over a short history: on a 256-CU part each workgroup takes one whole
+    row block, and the XCD-aware share order maps workgroups 0..247 to shares
+    (i % 8) * 31 + i / 8 and the last two to themselves. Every row of every block must come
+    out once and right (a share taken twice or never shows as a wrong or zero row)."""
+    go, gl, oo, ol = _attention_case(2, "bf16", 1, 1, 1, 64, appends=(64,), n_cur=16, n_q=250 * 256, jensen=1,
+                                     seed=29)
+    assert np.abs(go - oo).max() <= TOL
+    assert np.abs(gl - ol).max() <= TOL
+
+
 @pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_tiny_workload(jensen):
     w = workloads.WORKLOADS["tiny_int2_h1_d64"]
