@@ -68,18 +68,18 @@ def _check_step(name, stride, jensen=None):
         assert_segments_equal(gseg, oseg)
 
 
-@pytest.mark.parametrize("jensen", [1, 3])
+@pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_video_chunk_int2_h12_d128(jensen):
     """Video chunk step: 18,720 cached INT2 tokens + 4,680 current, 4,680 queries x 12 heads
-    (the second-order and the all-orders Jensen forms)."""
+    (every Jensen form: off, channel-weighted, isotropic, all orders)."""
     _check_step("video_chunk_int2_h12_d128", stride=37, jensen=jensen)
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("jensen", [0, 1, 3])
+@pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_decode_gqa32x8_32k(bits, jensen):
     """Decode, GQA 32/8, 8 sequences x 32,768 cached tokens: every query row, with the
-    Jensen correction off and on."""
+    Jensen correction off and in each of its three forms."""
     _check_step("decode_gqa32x8_int%d_32k" % bits, stride=1, jensen=jensen)
 
 
@@ -105,7 +105,7 @@ def test_windowquant_decode_query_on_the_decode_kernel():
     pass
 
 
-@pytest.mark.parametrize("jensen", [0, 1])
+@pytest.mark.parametrize("jensen", [0, 1, 2, 3])
 def test_windowquant_fp16_gqa14x2_d64(jensen):
     """WindowQuant end to end: window scores, FP16/INT4/INT2 assignment and the grouped
     layout's gather lists (bit-exact), the three grouped segments built by gathered appends
