@@ -130,6 +130,18 @@ def test_attention_gqa_decode_splits(d, jensen):
     assert np.abs(gl - ol).max() <= TOL
 
 
+@pytest.mark.parametrize("bits,d", [(2, 64), (2, 128), (4, 128)])
+@pytest.mark.parametrize("jensen", [0, 1, 3])
+def test_attention_decode_with_current_chunk(bits, d, jensen):
+    """Decode-shaped (4 query rows per KV head) over one packed segment and a 40-token
+    current chunk, 340 tokens in all: one workgroup walks each (batch, KV head), so the
+    decode kernel's current-chunk instances take the call."""
+    go, gl, oo, ol = _attention_case(bits, "bf16", 2, 8, 2, d, appends=(300,), n_cur=40, n_q=1, jensen=jensen,
+                                     seed=31 + bits + d)
+    assert np.abs(go - oo).max() <= TOL
+    assert np.abs(gl - ol).max() <= TOL
+
+
 def test_attention_shares_span_row_blocks():
     """600 row blocks (the last one ragged) over 130 tokens: more than two rounds of
     workgroups, so every workgroup takes an equal share of about 2.3 row blocks -- a cut
