@@ -393,16 +393,24 @@ def probe_hbm(mib=2048, reps=5):
 
 
 def host_cpu():
-    """The host CPU as /proc/cpuinfo names it, and the thread settings the oracle runs under."""
-    model = "unknown"
+    """The host CPU as /proc/cpuinfo names it (model name, and the family and model numbers
+    that identify the generation where a virtual machine shows only a generic name), and the
+    thread settings the oracle runs under."""
+    info = {}
     try:
         for line in open("/proc/cpuinfo"):
-            if line.startswith("model name"):
-                model = line.split(":", 1)[1].strip()
-                break
+            if ":" not in line:
+                if info:
+                    break   # the first processor's block is enough
+                continue
+            k, v = (x.strip() for x in line.split(":", 1))
+            if k in ("model name", "vendor_id", "cpu family", "model") and k not in info:
+                info[k] = v
     except OSError:
         pass
-    return {"cpu_model": model, "nproc": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
+    return {"cpu_model": info.get("model name", "unknown"), "cpu_vendor": info.get("vendor_id"),
+            "cpu_family": info.get("cpu family"), "cpu_model_number": info.get("model"),
+            "nproc": os.cpu_count(), "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS")}
 
 
 def time_steps(step: ChunkStep, steps: int, warmup: int):

@@ -94,3 +94,10 @@ def test_trace_summary_keeps_each_kernels_last_dispatches(tmp_path, capsys):
     assert (float(cells[4]), float(cells[5])) == (10.0, 40.0)
     q = [l for l in out if "quant_split_kernel" in l]
     assert len(q) == 1 and "| 4 | 5.0 | 5.0 | 5.0 | 5.0 |" in q[0]
+
+
+def test_host_cpu_names_the_generation():
+    h = bench.host_cpu()
+    for k in ("cpu_model", "cpu_vendor", "cpu_family", "cpu_model_number", "nproc", "OMP_NUM_THREADS"):
+        assert k in h
+    assert h["nproc"] == os.cpu_count()
