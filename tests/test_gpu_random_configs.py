@@ -25,7 +25,7 @@ from parity_util import (TORCH_DT, append_both, assert_segments_equal, f32, gpu_
 
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
-N_CASES = 48
+N_CASES = 160
 
 
 def _rand(rng, shape, dtype, scale=1.0):
@@ -79,7 +79,7 @@ def _basis(rng, H, d, r):
     return U
 
 
-@pytest.mark.parametrize("case", range(24))
+@pytest.mark.parametrize("case", range(64))
 def test_random_configuration_extras(case):
     c, rng = _draw(100 + case)
     dtype, d, B, Hkv = c["dtype"], c["d"], c["B"], c["Hkv"]
@@ -123,7 +123,7 @@ def test_random_configuration_extras(case):
     assert err <= TOL and lerr <= TOL, (c, aug, kgc, fused, err, lerr)
 
 
-@pytest.mark.parametrize("case", range(32))
+@pytest.mark.parametrize("case", range(96))
 def test_random_appends(case):
     """Quantize-appends of random shape against the oracle, bit for bit: INT2 or INT4, head
     dim 64 or 128, fp32/bf16/fp16 sources into bf16/fp16 caches, K-groups of 32 to 256
@@ -156,7 +156,7 @@ def test_random_appends(case):
         assert_segments_equal(gseg, oseg)
 
 
-@pytest.mark.parametrize("case", range(16))
+@pytest.mark.parametrize("case", range(40))
 def test_random_window_assignments(case):
     """Window scores, bit-widths, order, gather lists and class token counts for random
     token counts (1 to 9,000), KV heads, head dims, layers and budget percentages (the class
