@@ -14,6 +14,8 @@ and the current chunk appended by the attention call itself. Appended segments a
 bit for bit, attention within 2e-3 (fp32 output) and the log-sum-exp within 2e-3, as in
 test_gpu_parity.py.
 """
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -26,6 +28,14 @@ from parity_util import (TORCH_DT, append_both, assert_segments_equal, f32, gpu_
 pytestmark = pytest.mark.gpu
 TOL = 2e-3
 N_CASES = 160
+# Wider sweeps on demand: KVQ_SWEEP_SCALE multiplies every case count and KVQ_SWEEP_OFFSET
+# moves every seed (defaults 1 and 0: the committed cases).
+SCALE = int(os.environ.get("KVQ_SWEEP_SCALE", "1"))
+OFFSET = int(os.environ.get("KVQ_SWEEP_OFFSET", "0"))
+
+
+def _cases(n):
+    return range(OFFSET, OFFSET + n * SCALE)
 
 
 def _rand(rng, shape, dtype, scale=1.0):
@@ -48,7 +58,7 @@ def _draw(case):
     return c, rng
 
 
-@pytest.mark.parametrize("case", range(N_CASES))
+@pytest.mark.parametrize("case", _cases(N_CASES))
 def test_random_configuration(case):
     c, rng = _draw(case)
     dtype, d, B, Hkv = c["dtype"], c["d"], c["B"], c["Hkv"]
@@ -79,7 +89,7 @@ def _basis(rng, H, d, r):
     return U
 
 
-@pytest.mark.parametrize("case", range(64))
+@pytest.mark.parametrize("case", _cases(64))
 def test_random_configuration_extras(case):
     c, rng = _draw(100 + case)
     dtype, d, B, Hkv = c["dtype"], c["d"], c["B"], c["Hkv"]
@@ -123,7 +133,7 @@ def test_random_configuration_extras(case):
     assert err <= TOL and lerr <= TOL, (c, aug, kgc, fused, err, lerr)
 
 
-@pytest.mark.parametrize("case", range(96))
+@pytest.mark.parametrize("case", _cases(96))
 def test_random_appends(case):
     """Quantize-appends of random shape against the oracle, bit for bit: INT2 or INT4, head
     dim 64 or 128, fp32/bf16/fp16 sources into bf16/fp16 caches, K-groups of 32 to 256
@@ -156,7 +166,7 @@ def test_random_appends(case):
         assert_segments_equal(gseg, oseg)
 
 
-@pytest.mark.parametrize("case", range(40))
+@pytest.mark.parametrize("case", _cases(40))
 def test_random_window_assignments(case):
     """Window scores, bit-widths, order, gather lists and class token counts for random
     token counts (1 to 9,000), KV heads, head dims, layers and budget percentages (the class
